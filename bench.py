@@ -1,0 +1,325 @@
+"""Benchmark of one int4 routed-expert MoE layer on one MI355X.
+
+A step is one full pass of the layer (route -> union -> expert FFNs ->
+combine) over one batch of synthetic tokens, through the C ABI.  The headline
+workload is single-token decode: H=6144, I=2048, 256 routed experts (top-8)
+plus one shared expert, int4 weights with fp16 group-32 scales, all experts in
+VRAM.  To keep the 256 MB last-level cache from serving weights, steps rotate
+over several layer instances (distinct copies of the experts), so every step
+streams its experts from HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% peak) at decode B=1/64; prefill MFMA %"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(spec, n_union, n_tok):
+    """Bytes one layer call must move at minimum: each union expert's blob
+    once, the shared expert's blob, the router weight, activations in, output
+    out."""
+    from int4_routed_expert_layer_amd import configs
+    blob = configs.blob_bytes(spec.hidden, spec.inter)
+    experts = n_union + (1 if spec.has_shared else 0)
+    h, i = spec.hidden, spec.inter
+    gateup = experts * (2 * i * h // 2 + 2 * i * (h // 32) * 2)
+    down = experts * (h * i // 2 + h * (i // 32) * 2)
+    router = h * spec.n_experts * 4
+    act = n_tok * h * spec.act_bytes + n_tok * h * 4
+    return dict(total=experts * blob + router + act, gateup=gateup, down=down, router=router)
+
+
+def expert_flops(spec, n_tok):
+    rows = n_tok * spec.top_k + (n_tok if spec.has_shared else 0)
+    return 2.0 * rows * 3 * spec.hidden * spec.inter
+
+
+class Workload:
+    def __init__(self, name, spec, layers, steps, warmup, graph_steps):
+        self.name, self.spec, self.layers = name, spec, layers
+        self.steps, self.warmup, self.graph_steps = steps, warmup, graph_steps
+
+
+def make_layers(B, spec, blobs, shared, n_inst, max_tokens, w, b):
+    layers = []
+    for r in range(n_inst):
+        L = B.MoELayer.from_spec(spec, max_tokens=max_tokens)
+        L.set_router(w, b)
+        for e in range(spec.n_experts):
+            L.place(e, blobs[e])
+        if shared is not None:
+            L.place(B.SHARED, shared)
+        layers.append(L)
+        log(f"  layer instance {r + 1}/{n_inst} placed")
+    return layers
+
+
+def run_workload(B, torch, wl, x_all, use_graph=True):
+    """Time `steps` steps; returns timing, union sizes and per-kernel times."""
+    spec, layers = wl.spec, wl.layers
+    n_tok = spec.n_tok
+    R = len(layers)
+    n_slices = x_all.shape[0] // n_tok
+    dev = "cuda:0"
+    k, E, H = spec.top_k, spec.n_experts, spec.hidden
+
+    # Static buffers, one set per (instance) so graph replays reuse addresses.
+    bufs = []
+    for r in range(R):
+        bufs.append(dict(
+            idx=torch.empty((n_tok, k), dtype=torch.int32, device=dev),
+            w=torch.empty((n_tok, k), dtype=torch.float32, device=dev),
+            n_union=torch.empty(1, dtype=torch.int32, device=dev),
+            union_ids=torch.empty(E, dtype=torch.int32, device=dev),
+            counts=torch.empty(E, dtype=torch.int32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            gather=torch.empty(n_tok * k, dtype=torch.int32, device=dev),
+            y=torch.empty((n_tok, H), dtype=torch.float32, device=dev)))
+
+    C = B.C
+    lib = B.lib
+
+    def step(s):
+        r = s % R
+        L, bf = layers[r], bufs[r]
+        x = x_all[(s % n_slices) * n_tok:(s % n_slices + 1) * n_tok]
+        st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        p = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
+        B._check(lib.coli_moe_route(L.handle, p(x), n_tok, p(bf["idx"]), p(bf["w"]), st), L.handle)
+        B._check(lib.coli_moe_union(L.handle, p(bf["idx"]), n_tok, p(bf["n_union"]), p(bf["union_ids"]),
+                                    p(bf["counts"]), p(bf["offsets"]), p(bf["gather"]), st), L.handle)
+        B._check(lib.coli_moe_forward(L.handle, p(x), n_tok, p(bf["idx"]), p(bf["w"]), p(bf["n_union"]),
+                                      p(bf["union_ids"]), p(bf["counts"]), p(bf["offsets"]),
+                                      p(bf["gather"]), p(bf["y"]), st), L.handle)
+        return bf
+
+    # 1) eager pass with per-kernel events (roofline of the dominant kernel)
+    for s in range(wl.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    for L in layers:
+        L.kernel_times()
+        L.set_timing(True)
+    unions = []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for s in range(wl.steps):
+        bf = step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    eager_ms = ev0.elapsed_time(ev1) / wl.steps
+    kt = {}
+    for L in layers:
+        L.set_timing(False)
+        for kind, (ms, n) in L.kernel_times().items():
+            a = kt.setdefault(kind, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+    # union sizes over one rotation of inputs
+    for s in range(min(wl.steps, n_slices)):
+        bf = step(s)
+        unions.append(int(bf["n_union"].cpu()[0]))
+    torch.cuda.synchronize()
+
+    res = dict(eager_ms_per_step=eager_ms, kernel_ms={k_: v[0] / max(v[1], 1) for k_, v in kt.items() if v[1]},
+               kernel_launches={k_: v[1] for k_, v in kt.items() if v[1]},
+               union_mean=float(np.mean(unions)), union_min=int(np.min(unions)),
+               union_max=int(np.max(unions)))
+
+    # 2) graph pass: capture graph_steps steps once, replay to cover `steps`
+    if use_graph:
+        G = wl.graph_steps
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step(0)   # warm the capture stream
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for s in range(G):
+                step(s)
+        reps = max(1, wl.steps // G)
+        for _ in range(max(1, wl.warmup // G)):
+            g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = ev0.elapsed_time(ev1) / (reps * G)
+        res["graph_steps_timed"] = reps * G
+    return res
+
+
+def cpu_baseline(spec, x, w, b, blobs, shared, seconds):
+    from oracle import oracle as orc
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        xt = x[n:n + 1]
+        logits = orc.router_logits(xt, w, b)
+        idx, wt = orc.topk(logits, spec.top_k)
+        orc.union(idx, spec.n_experts)
+        need = {int(e): blobs[int(e)] for e in idx[0]}
+        orc.layer_tokens(xt, spec.hidden, spec.inter, idx, wt, need, shared, [0])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= x.shape[0]:
+            break
+    return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n} single-token decode calls of the same layer (route + union + 8 routed "
+                       f"+ 1 shared int4 SwiGLU experts, fp64), {el:.1f} s on 1 host core")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--instances", type=int, default=8, help="layer copies rotated per step")
+    ap.add_argument("--workloads", default="decode_b1,decode_b64,prefill_b4096")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one MoE layer on one GPU; runs on more than one GPU are "
+              "not part of this build (see DESIGN.md for how the layer would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_routed_expert_layer_amd import binding as B
+    from int4_routed_expert_layer_amd import configs, inputs
+
+    torch.cuda.init()
+    wanted = args.workloads.split(",")
+    spec1 = configs.DECODE_B1
+    log(f"generating experts of {spec1.name}")
+    blobs = inputs.expert_blobs(spec1, 0, range(spec1.n_experts), threads=8)
+    shared = inputs.expert_blob(spec1, 0, inputs.SHARED)
+    w1, b1 = inputs.router_weight(spec1), inputs.router_bias(spec1)
+
+    results = {}
+    decode_layers = []
+    if "decode_b1" in wanted or "decode_b64" in wanted:
+        log(f"placing {args.instances} decode layer instances")
+        decode_layers = make_layers(B, spec1, blobs, shared, args.instances, 64, w1, b1)
+
+    if "decode_b1" in wanted:
+        n_x = 256
+        x = B.activations_to_device(inputs.activations(spec1, 0, n_x))
+        wl = Workload("decode_b1", spec1, decode_layers, args.steps, args.warmup, graph_steps=64)
+        log("timing decode_b1")
+        results["decode_b1"] = run_workload(B, torch, wl, x, use_graph=not args.no_graph)
+
+    if "decode_b64" in wanted:
+        spec2 = configs.DECODE_B64
+        for L in decode_layers:
+            L.set_router(inputs.router_weight(spec2), inputs.router_bias(spec2))
+        x = B.activations_to_device(inputs.activations(spec2, 0, 64 * 16))
+        wl = Workload("decode_b64", spec2, decode_layers, max(16, args.steps // 8),
+                      max(4, args.warmup // 8), graph_steps=16)
+        log("timing decode_b64")
+        results["decode_b64"] = run_workload(B, torch, wl, x, use_graph=not args.no_graph)
+    for L in decode_layers:
+        L.close()
+    decode_layers = []
+    torch.cuda.empty_cache()
+
+    if "prefill_b4096" in wanted:
+        spec3 = configs.PREFILL_B4096
+        log("placing the prefill layer")
+        (L3,) = make_layers(B, spec3, blobs, shared, 1, spec3.n_tok, inputs.router_weight(spec3),
+                            inputs.router_bias(spec3))
+        x = B.activations_to_device(inputs.activations(spec3, 0))
+        wl = Workload("prefill_b4096", spec3, [L3], max(4, args.steps // 32), 2, graph_steps=1)
+        log("timing prefill_b4096")
+        results["prefill_b4096"] = run_workload(B, torch, wl, x, use_graph=False)
+        L3.close()
+
+    # ---- report
+    out_also = {}
+    for name, r in results.items():
+        spec = {"decode_b1": spec1, "decode_b64": configs.DECODE_B64,
+                "prefill_b4096": configs.PREFILL_B4096}[name]
+        ms = r.get("graph_ms_per_step", r["eager_ms_per_step"])
+        nb = algorithmic_bytes(spec, r["union_mean"], spec.n_tok)
+        entry = dict(tokens_per_s=spec.n_tok / (ms / 1e3), ms_per_step=ms,
+                     eager_ms_per_step=r["eager_ms_per_step"],
+                     union_mean=r["union_mean"], union_min=r["union_min"], union_max=r["union_max"],
+                     step_GBs=nb["total"] / (ms / 1e3) / 1e9,
+                     step_frac_hbm=nb["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     kernel_us={k: v * 1e3 for k, v in r["kernel_ms"].items()})
+        kg, kd = r["kernel_ms"].get("gateup"), r["kernel_ms"].get("down")
+        if kg:
+            entry["gateup_GBs"] = nb["gateup"] / (kg / 1e3) / 1e9
+        if kd:
+            entry["down_GBs"] = nb["down"] / (kd / 1e3) / 1e9
+        if name == "prefill_b4096" and kg and kd:
+            fl = expert_flops(spec, spec.n_tok)
+            entry["expert_gemm_TFLOPs"] = fl / ((kg + kd) / 1e3) / 1e12
+            entry["expert_gemm_frac_mfma"] = entry["expert_gemm_TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+        out_also[name] = entry
+
+    head = out_also.get("decode_b1") or next(iter(out_also.values()))
+    head_name = "decode_b1" if "decode_b1" in out_also else next(iter(out_also))
+    head_spec = {"decode_b1": spec1, "decode_b64": configs.DECODE_B64,
+                 "prefill_b4096": configs.PREFILL_B4096}[head_name]
+    r = results[head_name]
+    nb = algorithmic_bytes(head_spec, r["union_mean"], head_spec.n_tok)
+    kg = r["kernel_ms"]["gateup"]
+    achieved = nb["gateup"] / (kg / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "w4a16-f32acc",
+        "data": "synthetic",
+        "config": {"workload": head_spec.name + "+shared", "tokens_per_step": head_spec.n_tok,
+                   "layer_instances_rotated": args.instances, "hip_graph": not args.no_graph,
+                   "all_experts_vram": True},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemv_gateup (gate+up+SwiGLU)",
+                     "bytes_per_launch": nb["gateup"], "avg_launch_us": kg * 1e3},
+        "also": out_also,
+    }
+    if not args.no_cpu_baseline and head_name == "decode_b1":
+        log("timing the CPU oracle")
+        xs = inputs.activations(spec1, 0, 64)
+        line["cpu_baseline"] = cpu_baseline(spec1, xs, w1, b1, blobs, shared, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+/*
+ * coli_moe.h -- C ABI of the int4 routed-expert MoE layer for AMD MI355X
+ * (gfx950).  ABI version 1.
+ *
+ * One call sequence runs one Mixture-of-Experts layer over a batch of tokens,
+ * following the per-token path of the Colibri pages (getting-started page,
+ * "動作原理 / トークンごとの処理経路"; README "Come funziona / Il percorso di
+ * ogni token"):
+ *
+ *   coli_moe_route    Route: router logits, top-k experts per token and their
+ *                     weights.
+ *   coli_moe_union    Union: deduplicate the selected experts across the
+ *                     batch ("batch-union", README "Mai aspettare il disco due
+ *                     volte"), so each unique expert is read once.
+ *   coli_moe_forward  the int4 SwiGLU expert FFNs over the union, plus the
+ *                     always-on shared expert, and the routing-weighted
+ *                     combine.
+ *   coli_expert_place Place: keep an expert in VRAM or in pinned host memory
+ *                     (streamed over PCIe on a side stream when used).  The
+ *                     README states that placement changes speed only, never
+ *                     router decisions or weight precision: results are
+ *                     bit-identical across placements.
+ *
+ * The pages give no formula for any step.  The definitions implemented here:
+ *
+ *   logit[t][e]  = fp32 dot(x_t, W_r[:, e]) + b[e], summed in one fixed order:
+ *                  64 interleaved fmaf chains (chain l takes reduction indices
+ *                  l, l+64, l+128, ... ascending) folded by the tree
+ *                  s = 32,16,8,4,2,1 (p[i] = p[i] + p[i+s]), then + b[e].
+ *   top-k        = the k largest logits under (logit desc, expert id asc);
+ *                  slot order is rank order.
+ *   weight       = sigmoid(logit_j) / sum over the k selected of sigmoid.
+ *   expert e     = y = Wd (silu(Wg x) * (Wu x)), silu(z) = z sigmoid(z).
+ *   output y_t   = sum_j weight_j * expert_{e_j}(x_t) + shared(x_t).
+ *
+ * Expert weights are int4 (two's complement, element 2j in the low nibble of
+ * byte j, 2j+1 in the high nibble) with one fp16 scale per 32 consecutive
+ * reduction elements (w = q * s).  The int4 container and its group scales
+ * follow the README "Scarica il modello" (group-scaled int4); the group size
+ * is 32 here.
+ *
+ * Conventions for every entry point:
+ *  - Return codes only; nothing aborts or throws across the ABI.  On error
+ *    the layer stays usable and coli_last_error() holds a message.
+ *  - Arguments are validated on the host before any device work; a call that
+ *    fails validation has no effect.
+ *  - "device pointer" arguments are HIP device memory owned by the caller
+ *    (e.g. torch tensors); "host pointer" arguments are ordinary host memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *    enqueued on it asynchronously, except where a call says it synchronises.
+ *  - One host thread at a time per layer handle.  Distinct handles are
+ *    independent.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COLI_ABI_VERSION 1
+
+typedef enum {
+    COLI_OK = 0,
+    COLI_E_INVALID = 1,      /* bad argument; nothing was done */
+    COLI_E_NOMEM = 2,        /* device or pinned-host allocation failed */
+    COLI_E_DEVICE = 3,       /* a HIP call failed (text in coli_last_error) */
+    COLI_E_STATE = 4,        /* layer not ready: router or an expert unplaced */
+    COLI_E_UNSUPPORTED = 5   /* shape outside what the kernels support */
+} coli_status;
+
+typedef enum { COLI_ACT_F32 = 0, COLI_ACT_BF16 = 1 } coli_act;
+typedef enum { COLI_TIER_VRAM = 0, COLI_TIER_HOST = 1 } coli_tier;
+
+/* Forward strategy.  AUTO picks the VALU GEMV path for n_tok <= 2 and the
+ * grouped MFMA path otherwise.  Both give results within tolerance of the
+ * definition; for a given strategy results are deterministic. */
+typedef enum {
+    COLI_PATH_AUTO = 0,
+    COLI_PATH_GEMV = 1,      /* wave-per-row int4 GEMV on the vector ALUs */
+    COLI_PATH_GROUPED = 2    /* grouped int4->fp16 GEMM on MFMA */
+} coli_path;
+
+/* Expert id of the shared expert in coli_expert_place. */
+#define COLI_SHARED (-1)
+
+typedef struct {
+    int32_t hidden;      /* H: multiple of 128 */
+    int32_t inter;       /* I: multiple of 128 */
+    int32_t n_experts;   /* E: 1..1024 routed experts */
+    int32_t top_k;       /* k: 1..min(E, 32) */
+    int32_t has_shared;  /* 0 or 1: one always-on shared expert */
+    int32_t max_tokens;  /* largest n_tok any call will pass (>= 1) */
+    int32_t act;         /* coli_act: dtype of x */
+} coli_moe_dims;
+
+typedef struct coli_layer coli_layer;   /* opaque, library-owned */
+
+/* Bytes of one expert blob for H, I: gate_q, up_q ([I x H/2] bytes each),
+ * down_q ([H x I/2]), gate_s, up_s (fp16 [I x H/32]), down_s (fp16
+ * [H x I/32]), in that order, each section starting on a 256-byte boundary.
+ * The README stores an expert's three matrices contiguously so one read
+ * fetches all of them; this blob is that unit.  Returns 0 for invalid sizes. */
+size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter);
+
+/* Repack a blob (host pointer, layout above) into the library's device
+ * layout (host pointer `out`, same size): the bytes coli_expert_place keeps
+ * per expert.  Each int4 matrix is cut into 1 KB tiles of 16 rows x 128
+ * columns ordered so that lane L of a 64-lane wave loads bytes L*16..L*16+15
+ * of a tile: row L mod 16, columns 32s + 8(L div 16) + 0..7 in dword s, each
+ * stored as q + 8 with columns 2j and 2j+1 in nibbles j and 4+j; each tile's
+ * 64 fp16 scales are stored row-major next to it in the scale section.
+ * Host-only, no device needed.  COLI_E_INVALID for NULL pointers or sizes
+ * that are not multiples of 128. */
+coli_status coli_expert_repack(const void *blob_host, void *out_host,
+                               int32_t hidden, int32_t inter);
+
+/* Create a layer on HIP device `device`.  Allocates the router copy, the
+ * expert pointer table and scratch sized from dims->max_tokens.
+ * COLI_E_INVALID for bad dims, COLI_E_UNSUPPORTED for sizes the kernels do
+ * not handle, COLI_E_DEVICE if the device cannot be used, COLI_E_NOMEM on
+ * allocation failure.  *out is set only on success. */
+coli_status coli_layer_create(const coli_moe_dims *dims, int device,
+                              coli_layer **out);
+
+/* Free everything the layer owns (device memory, pinned host copies,
+ * streams).  NULL is accepted.  Synchronises the device. */
+coli_status coli_layer_destroy(coli_layer *layer);
+
+/* Copy the router weight W_r (host pointer, fp32 [H x E], reduction index
+ * outer: w_host[k*E + e]) and optional bias (host pointer, fp32 [E], or NULL
+ * for zero) into the layer.  Synchronous. */
+coli_status coli_router_set(coli_layer *layer, const float *w_host,
+                            const float *bias_host);
+
+/* Place expert `expert` (0..E-1, or COLI_SHARED) from a host blob in the
+ * layout of coli_expert_blob_bytes.  The library repacks it once into its
+ * device layout and keeps it in VRAM (COLI_TIER_VRAM) or in pinned host
+ * memory (COLI_TIER_HOST, copied to a device staging slot when a forward
+ * call needs it).  Re-placing an expert replaces its data and tier.  The
+ * shared expert must be VRAM-resident.  blob_host may be freed on return.
+ * Synchronous. */
+coli_status coli_expert_place(coli_layer *layer, int32_t expert,
+                              const void *blob_host, size_t blob_bytes,
+                              coli_tier tier);
+
+/* Route: for n_tok tokens x (device pointer, [n_tok x H], fp32 or bf16 per
+ * dims.act), write topk_idx (device, int32 [n_tok x k], rank order) and
+ * topk_w (device, fp32 [n_tok x k]).  0 <= n_tok <= max_tokens; n_tok == 0
+ * does nothing.  COLI_E_STATE if the router was never set. */
+coli_status coli_moe_route(coli_layer *layer, const void *x, int32_t n_tok,
+                           int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Router logits only (device, fp32 [n_tok x E]), in the fixed summation
+ * order above; coli_moe_route selects from exactly these values. */
+coli_status coli_moe_router_logits(coli_layer *layer, const void *x,
+                                   int32_t n_tok, float *logits, void *stream);
+
+/* Union over the batch of topk_idx (device, int32 [n_tok x k], ids in
+ * 0..E-1, distinct within a token, as coli_moe_route writes them).  Writes
+ * (all device): n_union [1]; union_ids [E] (ascending, first n_union valid);
+ * counts [E] (tokens per expert); offsets [E+1] (exclusive prefix sum of
+ * counts); gather [n_tok*k] (entries t*k+j ordered by expert id, then token).
+ * Out-of-range ids are skipped and raise the layer's device error flag
+ * (coli_layer_device_errors). */
+coli_status coli_moe_union(coli_layer *layer, const int32_t *topk_idx,
+                           int32_t n_tok, int32_t *n_union, int32_t *union_ids,
+                           int32_t *counts, int32_t *offsets, int32_t *gather,
+                           void *stream);
+
+/* Forward: y (device, fp32 [n_tok x H]) = routing-weighted sum of the expert
+ * FFNs over the union, plus the shared expert, for the tokens x (device),
+ * given the outputs of coli_moe_route and coli_moe_union for the same batch.
+ * Requires the router to have been set and the shared expert (if any) to be
+ * VRAM-resident.  If every routed expert is VRAM-resident the call is fully
+ * asynchronous.  Otherwise it reads back the union (synchronising `stream`),
+ * returns COLI_E_STATE if a routed expert in the union was never placed, and
+ * streams pinned-host experts into staging slots on a side stream while the
+ * resident ones compute; it returns after the stream has drained.  Results
+ * are bit-identical whichever tier an expert sits in. */
+coli_status coli_moe_forward(coli_layer *layer, const void *x, int32_t n_tok,
+                             const int32_t *topk_idx, const float *topk_w,
+                             const int32_t *n_union, const int32_t *union_ids,
+                             const int32_t *counts, const int32_t *offsets,
+                             const int32_t *gather, float *y, void *stream);
+
+/* Choose the forward strategy (coli_path).  Default COLI_PATH_AUTO. */
+coli_status coli_layer_set_path(coli_layer *layer, int32_t path);
+
+/* Statistics of the last tiered forward call (host pointers, may be NULL):
+ * experts streamed over PCIe and bytes copied. */
+coli_status coli_layer_stream_stats(const coli_layer *layer,
+                                    int32_t *n_streamed, int64_t *bytes);
+
+/* Read and clear the device error flags (synchronises the device):
+ * bit 0 = an out-of-range expert id reached coli_moe_union. */
+coli_status coli_layer_device_errors(coli_layer *layer, int32_t *flags);
+
+/* Kernel timing, for tracing and benchmarks.  While enabled, every kernel
+ * the layer launches is bracketed by two HIP events on its launch stream and
+ * its elapsed time is added to the total of its kind.  coli_layer_kernel_times
+ * synchronises the device, writes per-kind totals (host arrays of
+ * COLI_KERNEL_KINDS entries, either may be NULL) and resets them. */
+typedef enum {
+    COLI_K_ROUTER = 0,   /* router logits */
+    COLI_K_TOPK = 1,     /* top-k and weights */
+    COLI_K_UNION = 2,    /* batch union */
+    COLI_K_PLAN = 3,     /* grouped work list */
+    COLI_K_GATEUP = 4,   /* gate/up + SwiGLU (GEMV or grouped) */
+    COLI_K_DOWN = 5,     /* down projection x routing weight */
+    COLI_K_COMBINE = 6,  /* per-token sum of expert rows */
+    COLI_KERNEL_KINDS = 7
+} coli_kernel_kind;
+coli_status coli_layer_set_timing(coli_layer *layer, int32_t enable);
+coli_status coli_layer_kernel_times(coli_layer *layer, double *ms_total,
+                                    int64_t *launches);
+
+const char *coli_status_str(coli_status status);
+const char *coli_last_error(const coli_layer *layer);
+int32_t coli_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COLI_MOE_H */

@@ -1,0 +1,755 @@
+// abi.hip -- host side of the C ABI declared in include/coli_moe.h:
+// argument validation, layer lifetime, placement (repack into the device
+// layout, VRAM or pinned-host tier), and the orchestration of the route,
+// union and forward kernels, including the tiered forward that streams
+// pinned-host experts over PCIe on a side stream while resident experts
+// compute (the README's Place and Overlap steps).
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "coli_moe.h"
+#include "internal.h"
+
+namespace coli {
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+BlobLayout blob_layout(int hidden, int inter) {
+    const size_t h = static_cast<size_t>(hidden), i = static_cast<size_t>(inter);
+    const size_t sz[6] = {i * h / 2, i * h / 2, h * i / 2,
+                          i * (h / kGroup) * 2, i * (h / kGroup) * 2, h * (i / kGroup) * 2};
+    size_t off[7];
+    size_t o = 0;
+    for (int k = 0; k < 6; ++k) {
+        off[k] = o;
+        o = align256(o + sz[k]);
+    }
+    off[6] = o;
+    return BlobLayout{off[0], off[1], off[2], off[3], off[4], off[5], off[6]};
+}
+
+namespace {
+
+// Nibble permutation of one packed dword (columns k0..k0+7, column i in bits
+// 4i..4i+3, two's complement) into the device order: u = q + 8 in slot
+// i/2 (even i) or 4 + i/2 (odd i).  Two 64K-entry tables, one per half.
+struct RepackTables {
+    uint32_t lo[65536];
+    uint32_t hi[65536];
+    RepackTables() {
+        for (uint32_t v = 0; v < 65536; ++v) {
+            uint32_t a = 0, b = 0;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ua = ((v >> (4 * i)) & 15u) ^ 8u;      // column i
+                const uint32_t ub = ua;                               // column 4+i
+                const int ia = i, ib = 4 + i;
+                const int sa = (ia & 1) ? 4 + (ia >> 1) : (ia >> 1);
+                const int sb = (ib & 1) ? 4 + (ib >> 1) : (ib >> 1);
+                a |= ua << (4 * sa);
+                b |= ub << (4 * sb);
+            }
+            lo[v] = a;
+            hi[v] = b;
+        }
+    }
+};
+
+const RepackTables &repack_tables() {
+    static const RepackTables *t = new RepackTables();
+    return *t;
+}
+
+// Repack rows [p_begin, p_end) panels of one [R x K] matrix.
+void repack_panels(const uint8_t *q_src, const uint16_t *s_src, int K, int p_begin,
+                   int p_end, uint8_t *q_dst, uint16_t *s_dst) {
+    const RepackTables &T = repack_tables();
+    const int C = K / kChunkK;
+    const size_t row_bytes = static_cast<size_t>(K) / 2;
+    const int groups = K / kGroup;
+    for (int p = p_begin; p < p_end; ++p) {
+        for (int c = 0; c < C; ++c) {
+            uint8_t *qc = q_dst + (static_cast<size_t>(p) * C + c) * kChunkBytes;
+            uint16_t *sc = s_dst + (static_cast<size_t>(p) * C + c) * (kScaleChunkBytes / 2);
+            for (int lane = 0; lane < 64; ++lane) {
+                const int r = p * kPanel + (lane & 15);
+                for (int s = 0; s < 4; ++s) {
+                    const int k0 = c * kChunkK + 32 * s + 8 * (lane >> 4);
+                    uint32_t in;
+                    std::memcpy(&in, q_src + static_cast<size_t>(r) * row_bytes + k0 / 2, 4);
+                    const uint32_t out = T.lo[in & 0xFFFFu] | T.hi[in >> 16];
+                    std::memcpy(qc + lane * 16 + s * 4, &out, 4);
+                }
+            }
+            for (int r = 0; r < kPanel; ++r)
+                for (int s = 0; s < 4; ++s)
+                    sc[r * 4 + s] = s_src[static_cast<size_t>(p * kPanel + r) * groups + 4 * c + s];
+        }
+    }
+}
+
+void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter) {
+    const BlobLayout L = blob_layout(hidden, inter);
+    std::memset(dst, 0, L.total);
+    struct Mat { size_t q, s; int rows, K; } mats[3] = {
+        {L.gate_q, L.gate_s, inter, hidden},
+        {L.up_q, L.up_s, inter, hidden},
+        {L.down_q, L.down_s, hidden, inter}};
+    const unsigned hw = std::max(1u, std::min(8u, std::thread::hardware_concurrency()));
+    const size_t work = L.total;
+    const int nthreads = work >= (4u << 20) ? static_cast<int>(hw) : 1;
+    for (const Mat &m : mats) {
+        const int P = m.rows / kPanel;
+        auto run = [&](int b, int e) {
+            repack_panels(src + m.q, reinterpret_cast<const uint16_t *>(src + m.s), m.K, b, e,
+                          dst + m.q, reinterpret_cast<uint16_t *>(dst + m.s));
+        };
+        if (nthreads <= 1 || P < 2 * nthreads) {
+            run(0, P);
+        } else {
+            std::vector<std::thread> th;
+            const int per = (P + nthreads - 1) / nthreads;
+            for (int t = 0; t < nthreads; ++t) {
+                const int b = t * per, e = std::min(P, b + per);
+                if (b < e) th.emplace_back(run, b, e);
+            }
+            for (auto &x : th) x.join();
+        }
+    }
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+thread_local std::string g_create_error;
+
+}  // namespace
+}  // namespace coli
+
+using namespace coli;
+
+struct ExpertSlot {
+    uint8_t *dev = nullptr;     // VRAM copy (device layout)
+    uint8_t *host = nullptr;    // pinned host copy (device layout)
+    int tier = -1;              // -1 unplaced, else coli_tier
+};
+
+struct coli_layer {
+    coli_moe_dims d{};
+    int device = 0;
+    int n_cu = 0;
+    size_t max_lds = 0;
+    BlobLayout lay{};
+    int path = COLI_PATH_AUTO;
+
+    float *wt = nullptr;        // router weight, transposed [E x H]
+    float *bias = nullptr;      // [E]
+    bool router_set = false;
+
+    std::vector<ExpertSlot> experts;          // E + 1 (index E = shared)
+    std::vector<const uint8_t *> table_host;  // mirrors table_dev
+    const uint8_t **table_dev = nullptr;      // [E + 1]; NULL for non-VRAM experts
+
+    float *logits = nullptr;    // [max_tokens x E]
+    _Float16 *h = nullptr;      // [(max_tokens*k + max_tokens) x I]
+    float *ys = nullptr;        // [(max_tokens*k + max_tokens) x H]
+    ChunkDesc *chunks = nullptr;
+    int32_t *n_chunks = nullptr;
+    int max_chunks = 0;
+    int32_t *err = nullptr;
+    uint8_t *pin_stage = nullptr;    // pinned staging for placement
+
+    // tiered forward
+    hipStream_t side = nullptr;
+    std::vector<uint8_t *> slots;
+    std::vector<hipEvent_t> slot_free;
+    std::vector<hipEvent_t> batch_ready;
+    std::vector<const uint8_t **> pin_tables;
+    std::vector<const uint8_t **> dev_tables;
+    int32_t *pin_union = nullptr;    // [1 + E]
+    int32_t last_streamed = 0;
+    int64_t last_bytes = 0;
+
+    // kernel timing
+    bool timing = false;
+    struct Mark { int kind; hipEvent_t a, b; };
+    std::vector<Mark> marks;          // recorded since the last read
+    std::vector<hipEvent_t> ev_pool;  // idle events
+
+    std::string msg;
+};
+
+namespace {
+
+constexpr int kSlotCount = 16;
+constexpr int kBatchExperts = 4;
+
+coli_status fail(coli_layer *L, coli_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (L) L->msg = buf;
+    else g_create_error = buf;
+    return st;
+}
+
+coli_status hip_fail(coli_layer *L, hipError_t e, const char *what) {
+    return fail(L, e == hipErrorOutOfMemory ? COLI_E_NOMEM : COLI_E_DEVICE, "%s: %s", what,
+                hipGetErrorString(e));
+}
+
+#define HIP_TRY(L, call, what)                          \
+    do {                                                \
+        hipError_t e_ = (call);                         \
+        if (e_ != hipSuccess) return hip_fail(L, e_, what); \
+    } while (0)
+
+hipEvent_t take_event(coli_layer *L) {
+    if (!L->ev_pool.empty()) {
+        hipEvent_t e = L->ev_pool.back();
+        L->ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one kernel launch with events when timing is enabled.
+struct KernelMark {
+    coli_layer *L;
+    int kind;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    KernelMark(coli_layer *L_, int kind_, hipStream_t s_) : L(L_), kind(kind_), s(s_) {
+        if (L->timing && (a = take_event(L)) != nullptr) (void)hipEventRecord(a, s);
+    }
+    ~KernelMark() {
+        if (!a) return;
+        hipEvent_t b = take_event(L);
+        if (b && hipEventRecord(b, s) == hipSuccess) {
+            L->marks.push_back({kind, a, b});
+        } else {
+            L->ev_pool.push_back(a);
+            if (b) L->ev_pool.push_back(b);
+        }
+    }
+};
+
+bool dims_valid(const coli_moe_dims *d, std::string &why) {
+    char buf[256];
+    if (!d) { why = "dims is NULL"; return false; }
+    if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->max_tokens <= 0) {
+        why = "dims must be positive";
+        return false;
+    }
+    if (d->has_shared != 0 && d->has_shared != 1) { why = "has_shared must be 0 or 1"; return false; }
+    if (d->act != COLI_ACT_F32 && d->act != COLI_ACT_BF16) { why = "act must be COLI_ACT_F32 or COLI_ACT_BF16"; return false; }
+    if (d->top_k > d->n_experts || d->top_k > kMaxTopK) {
+        std::snprintf(buf, sizeof buf, "top_k %d must be <= min(n_experts, %d)", d->top_k, kMaxTopK);
+        why = buf;
+        return false;
+    }
+    return true;
+}
+
+bool dims_supported(const coli_moe_dims *d, std::string &why) {
+    char buf[256];
+    if (d->hidden % kChunkK || d->inter % kChunkK) {
+        std::snprintf(buf, sizeof buf, "hidden (%d) and inter (%d) must be multiples of %d",
+                      d->hidden, d->inter, kChunkK);
+        why = buf;
+        return false;
+    }
+    if (d->n_experts + d->has_shared > kMaxExperts) {
+        std::snprintf(buf, sizeof buf, "n_experts + has_shared must be <= %d", kMaxExperts);
+        why = buf;
+        return false;
+    }
+    if (static_cast<int64_t>(d->max_tokens) * d->top_k > (1 << 26)) {
+        why = "max_tokens * top_k too large";
+        return false;
+    }
+    return true;
+}
+
+bool all_routed_resident(const coli_layer *L) {
+    for (int e = 0; e < L->d.n_experts; ++e)
+        if (L->experts[e].tier != COLI_TIER_VRAM) return false;
+    return true;
+}
+
+int choose_path(const coli_layer *L, int n_tok) {
+    if (L->path != COLI_PATH_AUTO) return L->path;
+    return n_tok <= 2 ? COLI_PATH_GEMV : COLI_PATH_GROUPED;
+}
+
+coli_status launch_experts(coli_layer *L, const FwdArgs &a, int path, hipStream_t s) {
+    hipError_t e;
+    if (path == COLI_PATH_GEMV) {
+        {
+            KernelMark m(L, COLI_K_GATEUP, s);
+            if ((e = launch_gemv_gateup(a, L->max_lds, s)) != hipSuccess) return hip_fail(L, e, "gemv gate/up launch");
+        }
+        KernelMark m(L, COLI_K_DOWN, s);
+        if ((e = launch_gemv_down(a, L->max_lds, s)) != hipSuccess) return hip_fail(L, e, "gemv down launch");
+    } else {
+        const int mc = max_work_chunks(a.n_tok, a.k, a.n_experts, a.has_shared);
+        {
+            KernelMark m(L, COLI_K_GATEUP, s);
+            if ((e = launch_grouped_gateup(a, mc, L->n_cu, s)) != hipSuccess) return hip_fail(L, e, "grouped gate/up launch");
+        }
+        KernelMark m(L, COLI_K_DOWN, s);
+        if ((e = launch_grouped_down(a, mc, L->n_cu, s)) != hipSuccess) return hip_fail(L, e, "grouped down launch");
+    }
+    return COLI_OK;
+}
+
+void free_layer(coli_layer *L) {
+    if (!L) return;
+    (void)hipDeviceSynchronize();
+    for (auto &x : L->experts) {
+        if (x.dev) (void)hipFree(x.dev);
+        if (x.host) (void)hipHostFree(x.host);
+    }
+    for (auto p : L->slots) (void)hipFree(p);
+    for (auto ev : L->slot_free) (void)hipEventDestroy(ev);
+    for (auto ev : L->batch_ready) (void)hipEventDestroy(ev);
+    for (auto &mk : L->marks) {
+        (void)hipEventDestroy(mk.a);
+        (void)hipEventDestroy(mk.b);
+    }
+    for (auto ev : L->ev_pool) (void)hipEventDestroy(ev);
+    for (auto p : L->pin_tables) (void)hipHostFree(const_cast<uint8_t **>(p));
+    for (auto p : L->dev_tables) (void)hipFree(const_cast<uint8_t **>(p));
+    if (L->side) (void)hipStreamDestroy(L->side);
+    void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->ys, L->chunks, L->n_chunks, L->err};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+    if (L->pin_stage) (void)hipHostFree(L->pin_stage);
+    if (L->pin_union) (void)hipHostFree(L->pin_union);
+    delete L;
+}
+
+coli_status ensure_stream_resources(coli_layer *L, int n_batches) {
+    const size_t bytes = L->lay.total;
+    if (!L->side) HIP_TRY(L, hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking), "side stream");
+    while (static_cast<int>(L->slots.size()) < kSlotCount) {
+        uint8_t *p = nullptr;
+        HIP_TRY(L, hipMalloc(&p, bytes), "staging slot");
+        L->slots.push_back(p);
+        hipEvent_t ev;
+        HIP_TRY(L, hipEventCreateWithFlags(&ev, hipEventDisableTiming), "slot event");
+        L->slot_free.push_back(ev);
+    }
+    const size_t tbytes = sizeof(uint8_t *) * (L->d.n_experts + 1);
+    while (static_cast<int>(L->dev_tables.size()) < n_batches) {
+        void *hp = nullptr, *dp = nullptr;
+        HIP_TRY(L, hipHostMalloc(&hp, tbytes, hipHostMallocDefault), "pinned table");
+        HIP_TRY(L, hipMalloc(&dp, tbytes), "device table");
+        L->pin_tables.push_back(static_cast<const uint8_t **>(hp));
+        L->dev_tables.push_back(static_cast<const uint8_t **>(dp));
+        hipEvent_t ev;
+        HIP_TRY(L, hipEventCreateWithFlags(&ev, hipEventDisableTiming), "batch event");
+        L->batch_ready.push_back(ev);
+    }
+    return COLI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t coli_abi_version(void) { return COLI_ABI_VERSION; }
+
+const char *coli_status_str(coli_status s) {
+    switch (s) {
+        case COLI_OK: return "COLI_OK";
+        case COLI_E_INVALID: return "COLI_E_INVALID";
+        case COLI_E_NOMEM: return "COLI_E_NOMEM";
+        case COLI_E_DEVICE: return "COLI_E_DEVICE";
+        case COLI_E_STATE: return "COLI_E_STATE";
+        case COLI_E_UNSUPPORTED: return "COLI_E_UNSUPPORTED";
+    }
+    return "unknown coli_status";
+}
+
+const char *coli_last_error(const coli_layer *L) {
+    return L ? L->msg.c_str() : g_create_error.c_str();
+}
+
+size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter) {
+    if (hidden <= 0 || inter <= 0 || hidden % kGroup || inter % kGroup) return 0;
+    return blob_layout(hidden, inter).total;
+}
+
+coli_status coli_expert_repack(const void *blob_host, void *out_host, int32_t hidden, int32_t inter) {
+    if (!blob_host || !out_host) return fail(nullptr, COLI_E_INVALID, "NULL host pointer");
+    if (hidden <= 0 || inter <= 0 || hidden % kChunkK || inter % kChunkK)
+        return fail(nullptr, COLI_E_INVALID, "hidden and inter must be positive multiples of %d", kChunkK);
+    repack_blob(static_cast<const uint8_t *>(blob_host), static_cast<uint8_t *>(out_host), hidden, inter);
+    return COLI_OK;
+}
+
+coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer **out) {
+    std::string why;
+    if (!out) return fail(nullptr, COLI_E_INVALID, "out is NULL");
+    if (!dims_valid(dims, why)) return fail(nullptr, COLI_E_INVALID, "%s", why.c_str());
+    if (!dims_supported(dims, why)) return fail(nullptr, COLI_E_UNSUPPORTED, "%s", why.c_str());
+    int ndev = 0;
+    hipError_t he = hipGetDeviceCount(&ndev);
+    if (he != hipSuccess || ndev <= 0)
+        return fail(nullptr, COLI_E_DEVICE, "no HIP device available (%s)", hipGetErrorString(he));
+    if (device < 0 || device >= ndev) return fail(nullptr, COLI_E_INVALID, "device %d out of range", device);
+    DeviceGuard guard(device);
+    if (!guard.ok) return fail(nullptr, COLI_E_DEVICE, "cannot select device %d", device);
+    hipDeviceProp_t prop;
+    if ((he = hipGetDeviceProperties(&prop, device)) != hipSuccess)
+        return fail(nullptr, COLI_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(he));
+
+    coli_layer *L = new coli_layer();
+    L->d = *dims;
+    L->device = device;
+    L->n_cu = prop.multiProcessorCount;
+    L->max_lds = prop.sharedMemPerBlock;
+    L->lay = blob_layout(dims->hidden, dims->inter);
+    const int E = dims->n_experts, H = dims->hidden, I = dims->inter;
+    const size_t T = static_cast<size_t>(dims->max_tokens);
+    const size_t rows = T * dims->top_k + T;
+    L->max_chunks = max_work_chunks(dims->max_tokens, dims->top_k, E, dims->has_shared);
+    L->experts.resize(E + 1);
+    L->table_host.assign(E + 1, nullptr);
+
+    struct A { void **p; size_t n; const char *what; } allocs[] = {
+        {reinterpret_cast<void **>(&L->wt), sizeof(float) * E * H, "router weight"},
+        {reinterpret_cast<void **>(&L->bias), sizeof(float) * E, "router bias"},
+        {reinterpret_cast<void **>(&L->table_dev), sizeof(void *) * (E + 1), "expert table"},
+        {reinterpret_cast<void **>(&L->logits), sizeof(float) * T * E, "logits scratch"},
+        {reinterpret_cast<void **>(&L->h), sizeof(_Float16) * rows * I, "hidden scratch"},
+        {reinterpret_cast<void **>(&L->ys), sizeof(float) * rows * H, "per-entry output scratch"},
+        {reinterpret_cast<void **>(&L->chunks), sizeof(ChunkDesc) * L->max_chunks, "work list"},
+        {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
+        {reinterpret_cast<void **>(&L->err), sizeof(int32_t), "error flags"},
+    };
+    for (auto &a : allocs) {
+        if ((he = hipMalloc(a.p, a.n)) != hipSuccess) {
+            coli_status st = he == hipErrorOutOfMemory ? COLI_E_NOMEM : COLI_E_DEVICE;
+            fail(nullptr, st, "hipMalloc %s (%zu bytes): %s", a.what, a.n, hipGetErrorString(he));
+            free_layer(L);
+            return st;
+        }
+    }
+    if ((he = hipMemset(L->table_dev, 0, sizeof(void *) * (E + 1))) != hipSuccess ||
+        (he = hipMemset(L->err, 0, sizeof(int32_t))) != hipSuccess ||
+        (he = hipMemset(L->bias, 0, sizeof(float) * E)) != hipSuccess ||
+        (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_stage), L->lay.total, hipHostMallocDefault)) != hipSuccess ||
+        (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_union), sizeof(int32_t) * (E + 1), hipHostMallocDefault)) != hipSuccess ||
+        (he = hipDeviceSynchronize()) != hipSuccess) {
+        coli_status st = he == hipErrorOutOfMemory ? COLI_E_NOMEM : COLI_E_DEVICE;
+        fail(nullptr, st, "layer setup: %s", hipGetErrorString(he));
+        free_layer(L);
+        return st;
+    }
+    *out = L;
+    return COLI_OK;
+}
+
+coli_status coli_layer_destroy(coli_layer *L) {
+    if (!L) return COLI_OK;
+    DeviceGuard guard(L->device);
+    free_layer(L);
+    return COLI_OK;
+}
+
+coli_status coli_layer_set_path(coli_layer *L, int32_t path) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (path < COLI_PATH_AUTO || path > COLI_PATH_GROUPED) return fail(L, COLI_E_INVALID, "bad path %d", path);
+    L->path = path;
+    return COLI_OK;
+}
+
+coli_status coli_router_set(coli_layer *L, const float *w_host, const float *bias_host) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (!w_host) return fail(L, COLI_E_INVALID, "w_host is NULL");
+    const int E = L->d.n_experts, H = L->d.hidden;
+    std::vector<float> wt(static_cast<size_t>(E) * H);
+    for (int k = 0; k < H; ++k)
+        for (int e = 0; e < E; ++e) wt[static_cast<size_t>(e) * H + k] = w_host[static_cast<size_t>(k) * E + e];
+    std::vector<float> b(E, 0.0f);
+    if (bias_host) std::memcpy(b.data(), bias_host, sizeof(float) * E);
+    DeviceGuard guard(L->device);
+    HIP_TRY(L, hipMemcpy(L->wt, wt.data(), sizeof(float) * wt.size(), hipMemcpyHostToDevice), "router upload");
+    HIP_TRY(L, hipMemcpy(L->bias, b.data(), sizeof(float) * E, hipMemcpyHostToDevice), "bias upload");
+    L->router_set = true;
+    return COLI_OK;
+}
+
+coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_host, size_t blob_bytes,
+                              coli_tier tier) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (!blob_host) return fail(L, COLI_E_INVALID, "blob_host is NULL");
+    if (expert != COLI_SHARED && (expert < 0 || expert >= L->d.n_experts))
+        return fail(L, COLI_E_INVALID, "expert %d out of range", expert);
+    if (expert == COLI_SHARED && !L->d.has_shared) return fail(L, COLI_E_INVALID, "layer has no shared expert");
+    if (blob_bytes != L->lay.total)
+        return fail(L, COLI_E_INVALID, "blob_bytes %zu != %zu", blob_bytes, L->lay.total);
+    if (tier != COLI_TIER_VRAM && tier != COLI_TIER_HOST) return fail(L, COLI_E_INVALID, "bad tier %d", tier);
+    if (expert == COLI_SHARED && tier != COLI_TIER_VRAM)
+        return fail(L, COLI_E_INVALID, "the shared expert must be VRAM-resident");
+    const int idx = expert == COLI_SHARED ? L->d.n_experts : expert;
+    ExpertSlot &x = L->experts[idx];
+    DeviceGuard guard(L->device);
+    const uint8_t *src = static_cast<const uint8_t *>(blob_host);
+    if (tier == COLI_TIER_VRAM) {
+        repack_blob(src, L->pin_stage, L->d.hidden, L->d.inter);
+        if (!x.dev) HIP_TRY(L, hipMalloc(&x.dev, L->lay.total), "expert VRAM");
+        HIP_TRY(L, hipMemcpy(x.dev, L->pin_stage, L->lay.total, hipMemcpyHostToDevice), "expert upload");
+        if (x.host) {
+            (void)hipHostFree(x.host);
+            x.host = nullptr;
+        }
+        L->table_host[idx] = x.dev;
+    } else {
+        if (!x.host) HIP_TRY(L, hipHostMalloc(reinterpret_cast<void **>(&x.host), L->lay.total, hipHostMallocDefault), "expert pinned host");
+        repack_blob(src, x.host, L->d.hidden, L->d.inter);
+        L->table_host[idx] = nullptr;
+    }
+    x.tier = tier;
+    HIP_TRY(L, hipMemcpy(L->table_dev + idx, &L->table_host[idx], sizeof(void *), hipMemcpyHostToDevice), "table update");
+    if (tier == COLI_TIER_HOST && x.dev) {
+        HIP_TRY(L, hipDeviceSynchronize(), "sync before free");
+        (void)hipFree(x.dev);
+        x.dev = nullptr;
+    }
+    return COLI_OK;
+}
+
+static coli_status check_tokens(coli_layer *L, int32_t n_tok) {
+    if (n_tok < 0 || n_tok > L->d.max_tokens)
+        return fail(L, COLI_E_INVALID, "n_tok %d outside [0, %d]", n_tok, L->d.max_tokens);
+    return COLI_OK;
+}
+
+coli_status coli_moe_router_logits(coli_layer *L, const void *x, int32_t n_tok, float *logits, void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !logits) return fail(L, COLI_E_INVALID, "NULL device pointer");
+    if (!L->router_set) return fail(L, COLI_E_STATE, "router weight not set");
+    DeviceGuard guard(L->device);
+    KernelMark m(L, COLI_K_ROUTER, static_cast<hipStream_t>(stream));
+    HIP_TRY(L, launch_router_logits(x, L->d.act == COLI_ACT_BF16, L->wt, L->bias, n_tok, L->d.hidden,
+                                    L->d.n_experts, logits, static_cast<hipStream_t>(stream)),
+            "router logits launch");
+    return COLI_OK;
+}
+
+coli_status coli_moe_route(coli_layer *L, const void *x, int32_t n_tok, int32_t *topk_idx, float *topk_w,
+                           void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !topk_idx || !topk_w) return fail(L, COLI_E_INVALID, "NULL device pointer");
+    if (!L->router_set) return fail(L, COLI_E_STATE, "router weight not set");
+    DeviceGuard guard(L->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        KernelMark m(L, COLI_K_ROUTER, s);
+        HIP_TRY(L, launch_router_logits(x, L->d.act == COLI_ACT_BF16, L->wt, L->bias, n_tok, L->d.hidden,
+                                        L->d.n_experts, L->logits, s),
+                "router logits launch");
+    }
+    KernelMark m(L, COLI_K_TOPK, s);
+    HIP_TRY(L, launch_topk(L->logits, n_tok, L->d.n_experts, L->d.top_k, topk_idx, topk_w, s), "top-k launch");
+    return COLI_OK;
+}
+
+coli_status coli_moe_union(coli_layer *L, const int32_t *topk_idx, int32_t n_tok, int32_t *n_union,
+                           int32_t *union_ids, int32_t *counts, int32_t *offsets, int32_t *gather,
+                           void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (!n_union || !union_ids || !counts || !offsets || (n_tok > 0 && (!topk_idx || !gather)))
+        return fail(L, COLI_E_INVALID, "NULL device pointer");
+    DeviceGuard guard(L->device);
+    KernelMark m(L, COLI_K_UNION, static_cast<hipStream_t>(stream));
+    HIP_TRY(L, launch_union(topk_idx, n_tok, L->d.top_k, L->d.n_experts, n_union, union_ids, counts, offsets,
+                            gather, L->err, static_cast<hipStream_t>(stream)),
+            "union launch");
+    return COLI_OK;
+}
+
+coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const int32_t *topk_idx,
+                             const float *topk_w, const int32_t *n_union, const int32_t *union_ids,
+                             const int32_t *counts, const int32_t *offsets, const int32_t *gather, float *y,
+                             void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
+        return fail(L, COLI_E_INVALID, "NULL device pointer");
+    if (L->d.has_shared && L->experts[L->d.n_experts].tier != COLI_TIER_VRAM)
+        return fail(L, COLI_E_STATE, "shared expert not placed");
+    DeviceGuard guard(L->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int path = choose_path(L, n_tok);
+
+    FwdArgs a{};
+    a.x = x;
+    a.act_bf16 = L->d.act == COLI_ACT_BF16;
+    a.table = L->table_dev;
+    a.n_union = n_union;
+    a.union_ids = union_ids;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.gather = gather;
+    a.topk_w = topk_w;
+    a.n_tok = n_tok;
+    a.k = L->d.top_k;
+    a.hidden = L->d.hidden;
+    a.inter = L->d.inter;
+    a.n_experts = L->d.n_experts;
+    a.has_shared = L->d.has_shared;
+    a.lay = L->lay;
+    a.h = L->h;
+    a.ys = L->ys;
+    a.y = y;
+    a.chunks = L->chunks;
+    a.n_chunks = L->n_chunks;
+
+    L->last_streamed = 0;
+    L->last_bytes = 0;
+    std::vector<int> streamed;
+    if (!all_routed_resident(L)) {
+        // Read the union back to find the experts that are not in VRAM.
+        const int E = L->d.n_experts;
+        HIP_TRY(L, hipMemcpyAsync(L->pin_union, n_union, sizeof(int32_t), hipMemcpyDeviceToHost, s), "union readback");
+        HIP_TRY(L, hipMemcpyAsync(L->pin_union + 1, union_ids, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s),
+                "union readback");
+        HIP_TRY(L, hipStreamSynchronize(s), "union readback sync");
+        const int nu = L->pin_union[0];
+        if (nu < 0 || nu > E) return fail(L, COLI_E_INVALID, "n_union %d out of range", nu);
+        for (int u = 0; u < nu; ++u) {
+            const int e = L->pin_union[1 + u];
+            if (e < 0 || e >= E) return fail(L, COLI_E_INVALID, "union id %d out of range", e);
+            if (L->experts[e].tier < 0) return fail(L, COLI_E_STATE, "expert %d is routed to but not placed", e);
+            if (L->experts[e].tier == COLI_TIER_HOST) streamed.push_back(e);
+        }
+    }
+
+    if (path == COLI_PATH_GROUPED) {
+        KernelMark m(L, COLI_K_PLAN, s);
+        HIP_TRY(L, launch_plan(a, L->chunks, L->n_chunks, s), "plan launch");
+    }
+    // Resident experts (the table holds NULL for pinned-host experts).
+    if ((st = launch_experts(L, a, path, s)) != COLI_OK) return st;
+
+    if (!streamed.empty()) {
+        const int n_batches = (static_cast<int>(streamed.size()) + kBatchExperts - 1) / kBatchExperts;
+        if ((st = ensure_stream_resources(L, n_batches)) != COLI_OK) return st;
+        const size_t bytes = L->lay.total;
+        const size_t tbytes = sizeof(uint8_t *) * (L->d.n_experts + 1);
+        std::vector<bool> slot_used(L->slots.size(), false);
+        for (int b = 0; b < n_batches; ++b) {
+            const uint8_t **pt = L->pin_tables[b];
+            std::memset(pt, 0, tbytes);
+            const int first = b * kBatchExperts;
+            const int last = std::min<int>(static_cast<int>(streamed.size()), first + kBatchExperts);
+            for (int i = first; i < last; ++i) {
+                const int slot = i % kSlotCount;
+                if (slot_used[slot]) HIP_TRY(L, hipStreamWaitEvent(L->side, L->slot_free[slot], 0), "slot wait");
+                const int e = streamed[i];
+                HIP_TRY(L, hipMemcpyAsync(L->slots[slot], L->experts[e].host, bytes, hipMemcpyHostToDevice, L->side),
+                        "expert H2D");
+                pt[e] = L->slots[slot];
+                L->last_bytes += static_cast<int64_t>(bytes);
+            }
+            HIP_TRY(L, hipEventRecord(L->batch_ready[b], L->side), "batch event");
+            HIP_TRY(L, hipStreamWaitEvent(s, L->batch_ready[b], 0), "batch wait");
+            HIP_TRY(L, hipMemcpyAsync(L->dev_tables[b], pt, tbytes, hipMemcpyHostToDevice, s), "batch table");
+            FwdArgs ab = a;
+            ab.table = L->dev_tables[b];
+            if ((st = launch_experts(L, ab, path, s)) != COLI_OK) return st;
+            for (int i = first; i < last; ++i) {
+                const int slot = i % kSlotCount;
+                HIP_TRY(L, hipEventRecord(L->slot_free[slot], s), "slot event");
+                slot_used[slot] = true;
+            }
+        }
+        L->last_streamed = static_cast<int32_t>(streamed.size());
+    }
+    {
+        KernelMark m(L, COLI_K_COMBINE, s);
+        HIP_TRY(L, launch_combine(a, s), "combine launch");
+    }
+    if (!streamed.empty() || !all_routed_resident(L)) HIP_TRY(L, hipStreamSynchronize(s), "tiered forward sync");
+    return COLI_OK;
+}
+
+coli_status coli_layer_set_timing(coli_layer *L, int32_t enable) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    L->timing = enable != 0;
+    return COLI_OK;
+}
+
+coli_status coli_layer_kernel_times(coli_layer *L, double *ms_total, int64_t *launches) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    DeviceGuard guard(L->device);
+    HIP_TRY(L, hipDeviceSynchronize(), "sync");
+    double t[COLI_KERNEL_KINDS] = {0};
+    int64_t n[COLI_KERNEL_KINDS] = {0};
+    for (auto &mk : L->marks) {
+        float ms = 0.0f;
+        HIP_TRY(L, hipEventElapsedTime(&ms, mk.a, mk.b), "event elapsed");
+        t[mk.kind] += ms;
+        n[mk.kind] += 1;
+        L->ev_pool.push_back(mk.a);
+        L->ev_pool.push_back(mk.b);
+    }
+    L->marks.clear();
+    for (int k = 0; k < COLI_KERNEL_KINDS; ++k) {
+        if (ms_total) ms_total[k] = t[k];
+        if (launches) launches[k] = n[k];
+    }
+    return COLI_OK;
+}
+
+coli_status coli_layer_stream_stats(const coli_layer *L, int32_t *n_streamed, int64_t *bytes) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (n_streamed) *n_streamed = L->last_streamed;
+    if (bytes) *bytes = L->last_bytes;
+    return COLI_OK;
+}
+
+coli_status coli_layer_device_errors(coli_layer *L, int32_t *flags) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (!flags) return fail(L, COLI_E_INVALID, "flags is NULL");
+    DeviceGuard guard(L->device);
+    HIP_TRY(L, hipDeviceSynchronize(), "sync");
+    HIP_TRY(L, hipMemcpy(flags, L->err, sizeof(int32_t), hipMemcpyDeviceToHost), "error flag readback");
+    HIP_TRY(L, hipMemset(L->err, 0, sizeof(int32_t)), "error flag clear");
+    HIP_TRY(L, hipDeviceSynchronize(), "sync");
+    return COLI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// internal.h -- shared declarations of the HIP library (not part of the ABI).
+//
+// Device layout of one expert (written once by coli_expert_place):
+//   The blob keeps the section offsets of the ABI blob (gate_q, up_q, down_q,
+//   gate_s, up_s, down_s), but each [R x K] int4 matrix is re-tiled so that
+//   one 16-byte load per lane of a 64-lane wave fetches a 16-row x 128-column
+//   block (1 KB, a "chunk"):
+//     chunk (p, c) of rows 16p..16p+15, columns 128c..128c+127 sits at byte
+//     (p * K/128 + c) * 1024; lane L owns bytes L*16 .. L*16+15; dword s
+//     (0..3) of that lane holds row 16p + (L & 15), columns
+//     k0 = 128c + 32s + 8(L >> 4) .. k0+7.
+//   That is exactly the B-operand fragment of v_mfma_f32_16x16x32_f16 for
+//   k-step (c, s), and each dword is one 32-element scale group's 8-wide slice.
+//   Inside a dword, column k0+i is stored as u = q + 8 (0..15) in nibble slot
+//   i/2 (i even) or 4 + i/2 (i odd), so ((w >> 4j) & 0x000F000F) puts columns
+//   k0+2j and k0+2j+1 in the low and high 16-bit halves: OR-ing an fp16
+//   (0x6400 -> 1024 + u) or bf16 (0x4300 -> 128 + u) exponent turns each
+//   half into an exact small integer.
+//   Scales: chunk (p, c) has 128 bytes at (p * K/128 + c) * 128 in the scale
+//   section: fp16 [16 rows][4 groups], groups 4c .. 4c+3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace coli {
+
+constexpr int kGroup = 32;          // reduction elements per fp16 scale
+constexpr int kChunkK = 128;        // reduction elements per 1 KB chunk
+constexpr int kPanel = 16;          // matrix rows per chunk
+constexpr int kChunkBytes = 1024;
+constexpr int kScaleChunkBytes = 128;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxFrags = 8;        // 16-row MFMA tiles per grouped work chunk
+constexpr int kChunkRows = kMaxFrags * 16;
+
+struct BlobLayout {
+    size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
+};
+BlobLayout blob_layout(int hidden, int inter);
+
+// One grouped-GEMM work chunk: up to kChunkRows rows of one expert.
+// expert == n_experts means the shared expert.  row0 indexes the rows of the
+// hidden-activation buffer (routed rows in gather order, then shared rows at
+// n_tok*k + t).
+struct ChunkDesc {
+    int32_t expert;
+    int32_t row0;
+    int32_t rows;
+    int32_t pad;
+};
+
+struct FwdArgs {
+    const void *x;                  // [n_tok x H] fp32 or bf16
+    int act_bf16;
+    const uint8_t *const *table;    // [E + 1] device blob pointers (NULL = skip)
+    const int32_t *n_union;
+    const int32_t *union_ids;
+    const int32_t *counts;
+    const int32_t *offsets;
+    const int32_t *gather;
+    const float *topk_w;
+    int n_tok, k, hidden, inter, n_experts, has_shared;
+    BlobLayout lay;
+    _Float16 *h;                    // [(n_tok*k + n_tok) x I]
+    float *ys;                      // [(n_tok*k + n_tok) x H]
+    float *y;                       // [n_tok x H]
+    const ChunkDesc *chunks;        // grouped path work list
+    const int32_t *n_chunks;
+};
+
+// route.hip
+hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
+                                const float *bias, int n_tok, int hidden,
+                                int n_experts, float *logits, hipStream_t s);
+hipError_t launch_topk(const float *logits, int n_tok, int n_experts, int k,
+                       int32_t *idx, float *w, hipStream_t s);
+// union.hip
+hipError_t launch_union(const int32_t *idx, int n_tok, int k, int n_experts,
+                        int32_t *n_union, int32_t *union_ids, int32_t *counts,
+                        int32_t *offsets, int32_t *gather, int32_t *err,
+                        hipStream_t s);
+hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
+                       hipStream_t s);
+// gemv.hip
+hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s);
+hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s);
+// grouped.hip
+hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu,
+                                 hipStream_t s);
+hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu,
+                               hipStream_t s);
+hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
+
+// Upper bound on grouped work chunks for n_tok tokens.
+int max_work_chunks(int n_tok, int k, int n_experts, int has_shared);
+
+}  // namespace coli

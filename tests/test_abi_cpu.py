@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function the header declares, validates arguments before touching a
+device, and its host repack writes the documented device layout."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from int4_routed_expert_layer_amd import binding as B
+from int4_routed_expert_layer_amd import configs, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coli_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coli_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 16
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(coli_\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(names) == set(B.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    assert B.lib.coli_abi_version() == 1
+    for st, name in enumerate(["COLI_OK", "COLI_E_INVALID", "COLI_E_NOMEM", "COLI_E_DEVICE",
+                               "COLI_E_STATE", "COLI_E_UNSUPPORTED"]):
+        assert B.status_str(st) == name
+
+
+def test_blob_bytes_matches_layout():
+    for h, i in ((6144, 2048), (256, 128), (512, 256)):
+        assert B.blob_bytes(h, i) == configs.blob_bytes(h, i)
+    assert B.blob_bytes(6144, 2048) == 21233664
+    assert B.blob_bytes(0, 128) == 0 and B.blob_bytes(100, 128) == 0
+
+
+def create(**kw):
+    d = dict(hidden=256, inter=128, n_experts=16, top_k=4, has_shared=0, max_tokens=8, act=0)
+    d.update(kw)
+    h = C.c_void_p()
+    st = B.lib.coli_layer_create(C.byref(B.Dims(**d)), 0, C.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=17), B.E_INVALID),
+    (dict(top_k=0), B.E_INVALID),
+    (dict(top_k=33, n_experts=64), B.E_INVALID),
+    (dict(max_tokens=0), B.E_INVALID),
+    (dict(has_shared=2), B.E_INVALID),
+    (dict(act=7), B.E_INVALID),
+    (dict(hidden=192), B.E_UNSUPPORTED),
+    (dict(inter=96), B.E_UNSUPPORTED),
+    (dict(n_experts=1024, has_shared=1), B.E_UNSUPPORTED),
+])
+def test_create_validates_dims_before_the_device(kw, status):
+    st, h = create(**kw)
+    assert st == status
+    assert not h.value
+    assert B.lib.coli_last_error(None)
+
+
+def test_create_without_a_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, h = create()
+    assert st == B.E_DEVICE and not h.value
+
+
+def test_null_layer_calls_are_invalid():
+    L = B.lib
+    assert L.coli_router_set(None, None, None) == B.E_INVALID
+    assert L.coli_expert_place(None, 0, None, 0, 0) == B.E_INVALID
+    assert L.coli_moe_route(None, None, 1, None, None, None) == B.E_INVALID
+    assert L.coli_moe_router_logits(None, None, 1, None, None) == B.E_INVALID
+    assert L.coli_moe_union(None, None, 1, None, None, None, None, None, None) == B.E_INVALID
+    assert L.coli_moe_forward(None, None, 1, *([None] * 8), None, None) == B.E_INVALID
+    assert L.coli_layer_set_path(None, 0) == B.E_INVALID
+    assert L.coli_layer_stream_stats(None, None, None) == B.E_INVALID
+    assert L.coli_layer_device_errors(None, None) == B.E_INVALID
+    assert L.coli_layer_destroy(None) == B.OK
+
+
+def documented_layout(blob, H, I):
+    """The device layout described in coli_moe.h, written with numpy."""
+    sec = configs.blob_sections(H, I)
+    out = np.zeros_like(blob)
+    for name, rows, K in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        qo, qs = sec[name + "_q"]
+        so, ss = sec[name + "_s"]
+        b = blob[qo:qo + qs].reshape(rows, K // 2)
+        q = np.empty((rows, K), np.int64)
+        q[:, 0::2] = b & 15
+        q[:, 1::2] = b >> 4
+        u = q ^ 8                                           # q + 8 for two's complement
+        P, Cn = rows // 16, K // 128
+        L = np.arange(64)
+        s = np.arange(4)
+        i = np.arange(8)
+        r = (np.arange(P)[:, None, None, None, None] * 16 + (L % 16)[None, None, :, None, None])
+        k = (np.arange(Cn)[None, :, None, None, None] * 128 + 32 * s[None, None, None, :, None]
+             + 8 * (L // 16)[None, None, :, None, None] + i[None, None, None, None, :])
+        vals = u[r, k]                                      # [P, C, 64, 4, 8]
+        slot = np.where(i % 2 == 0, i // 2, 4 + i // 2)
+        words = (vals << (4 * slot)).sum(-1).astype(np.uint32)
+        out[qo:qo + qs] = words.reshape(-1).view(np.uint8)
+        sc = blob[so:so + ss].view(np.uint16).reshape(rows, K // 32)
+        tiles = sc.reshape(P, 16, Cn, 4).transpose(0, 2, 1, 3)   # [P, C, row, group]
+        out[so:so + ss] = np.ascontiguousarray(tiles).reshape(-1).view(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("spec", [configs.TINY, configs.TINY.with_(hidden=512, inter=384)])
+def test_repack_writes_the_documented_layout(spec):
+    blob = inputs.expert_blob(spec, 0, 2)
+    got = B.repack(blob, spec.hidden, spec.inter)
+    np.testing.assert_array_equal(got, documented_layout(blob, spec.hidden, spec.inter))
+
+
+def test_repack_rejects_bad_sizes():
+    buf = np.zeros(1024, np.uint8)
+    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 96, 128) == B.E_INVALID
+    assert B.lib.coli_expert_repack(None, buf.ctypes.data, 128, 128) == B.E_INVALID

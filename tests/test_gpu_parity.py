@@ -1,0 +1,216 @@
+"""GPU parity: the HIP library against the CPU oracle on seeded inputs.
+
+Routing (logits, top-k ids), the union (ids, counts, offsets, gather) are
+compared bit for bit; routing weights to fp32 rounding; layer outputs to
+max|y_gpu - y_ref| <= 2e-3 * max|y_ref|.  Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+
+from int4_routed_expert_layer_amd import configs, inputs
+from moe_case import (Data, check_outputs, check_routing, gpu_run, log, make_layer,
+                      oracle_route, oracle_y)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from int4_routed_expert_layer_amd import binding as B  # noqa: E402
+
+PATHS = {"gemv": B.PATH_GEMV, "grouped": B.PATH_GROUPED}
+
+MEDIUM = configs.Spec("medium_h512_i256_e32_k4_b37", 512, 256, 32, 4, 37, "bf16", True,
+                      "zipf", seed=777)
+
+
+def full_check(spec, path, tokens=None, n_tok=None):
+    data = Data(spec, n_tok=n_tok)
+    log(f"case {spec.name} path={path} n_tok={data.x.shape[0]}")
+    L = make_layer(B, data, path=PATHS[path] if path else None)
+    gpu = gpu_run(B, L, data)
+    ref = oracle_route(data)
+    check_routing(gpu, ref)
+    toks = range(data.x.shape[0]) if tokens is None else tokens
+    y_ref = oracle_y(data, ref, toks)
+    check_outputs(gpu["y"][list(toks)], y_ref, f"{spec.name}/{path}")
+    L.close()
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_tiny_parity(path):
+    full_check(configs.TINY, path)
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_medium_ragged_parity(path, act):
+    full_check(MEDIUM.with_(act=act), path)
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_medium_single_token(path):
+    full_check(MEDIUM, path, n_tok=1)
+
+
+def test_special_case_e1_k1():
+    full_check(configs.TINY.with_(n_experts=1, top_k=1, has_shared=True, act="bf16"), "gemv")
+    full_check(configs.TINY.with_(n_experts=1, top_k=1, has_shared=True, act="bf16"), "grouped")
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_special_case_k_equals_e(path):
+    full_check(configs.TINY.with_(n_experts=8, top_k=8, n_tok=5), path)
+
+
+@pytest.fixture(scope="module")
+def decode_b1():
+    data = Data(configs.DECODE_B1)
+    log("case decode_b1: placing 257 experts")
+    L = make_layer(B, data)
+    yield data, L
+    L.close()
+
+
+@pytest.mark.parametrize("path", ["auto", "gemv", "grouped"])
+def test_decode_b1_parity(decode_b1, path):
+    data, L = decode_b1
+    L.set_path({"auto": B.PATH_AUTO, **PATHS}[path])
+    log(f"case decode_b1 path={path}")
+    gpu = gpu_run(B, L, data)
+    ref = oracle_route(data)
+    check_routing(gpu, ref)
+    check_outputs(gpu["y"], oracle_y(data, ref, [0]), f"decode_b1/{path}")
+
+
+def test_decode_b1_deterministic(decode_b1):
+    data, L = decode_b1
+    L.set_path(B.PATH_AUTO)
+    a = gpu_run(B, L, data, with_logits=False)
+    b = gpu_run(B, L, data, with_logits=False)
+    assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
+
+
+@pytest.mark.parametrize("path", ["auto", "gemv"])
+def test_decode_b64_zipf_parity(path):
+    spec = configs.DECODE_B64
+    data = Data(spec)
+    log(f"case decode_b64 path={path}")
+    L = make_layer(B, data, path={"auto": B.PATH_AUTO, **PATHS}[path])
+    gpu = gpu_run(B, L, data)
+    ref = oracle_route(data)
+    check_routing(gpu, ref)
+    log(f"  union size {ref['n_union']} of {spec.n_tok * spec.top_k} selections")
+    assert ref["n_union"] < spec.n_tok * spec.top_k // 2
+    tokens = list(range(0, 64, 4)) + [63]
+    check_outputs(gpu["y"][tokens], oracle_y(data, ref, tokens), f"decode_b64/{path}")
+    L.close()
+
+
+def test_prefill_b4096_parity():
+    spec = configs.PREFILL_B4096
+    data = Data(spec)
+    log("case prefill_b4096: placing 257 experts")
+    L = make_layer(B, data)
+    gpu = gpu_run(B, L, data)
+    log("  oracle routing over 4096 tokens")
+    ref = oracle_route(data)
+    check_routing(gpu, ref)
+    c = ref["counts"]
+    log(f"  tokens per expert: min {c.min()} max {c.max()}")
+    tokens = [0, 1, 777, 2048, 3001, 4095]
+    check_outputs(gpu["y"][tokens], oracle_y(data, ref, tokens), "prefill_b4096")
+    L.close()
+
+
+@pytest.mark.parametrize("layer", range(configs.TIERED_12L.n_layers))
+def test_tiered_layer_matches_resident_and_oracle(layer):
+    spec = configs.TIERED_12L
+    data = Data(spec, layer)
+    resident = inputs.resident_mask(spec, layer)
+    log(f"case tiered layer {layer}: {resident.sum()} resident / {spec.n_experts}")
+    L = make_layer(B, data)
+    all_vram = gpu_run(B, L, data, with_logits=False)
+    # Move the 40% host-tier experts to pinned host memory.
+    host = [e for e in range(spec.n_experts) if not resident[e]]
+    for i in range(0, len(host), 32):
+        for e, blob in data.blobs(host[i:i + 32]).items():
+            L.place(e, blob, B.TIER_HOST)
+        data.drop_blobs()
+    tiered = gpu_run(B, L, data, with_logits=False)
+    n_streamed, nbytes = L.stream_stats()
+    log(f"  streamed {n_streamed} experts, {nbytes / 1e6:.1f} MB")
+    assert n_streamed == sum(1 for e in all_vram["union_ids"] if not resident[e])
+    for key in ("idx", "weight", "union_ids", "counts", "offsets", "gather", "y"):
+        assert np.array_equal(np.asarray(tiered[key]).view(np.uint8),
+                              np.asarray(all_vram[key]).view(np.uint8)), key
+    ref = oracle_route(data)
+    check_routing(tiered, ref, check_logits=False)
+    check_outputs(tiered["y"], oracle_y(data, ref, range(spec.n_tok)), f"tiered/L{layer}")
+    L.close()
+
+
+def test_tie_break_prefers_lower_expert_id():
+    spec = configs.TINY.with_(act="bf16")
+    data = Data(spec)
+    data.w[:, 9] = data.w[:, 2]      # experts 2 and 9 always tie exactly
+    data.w[:, 12] = data.w[:, 5]
+    L = make_layer(B, data)
+    gpu = gpu_run(B, L, data)
+    ref = oracle_route(data)
+    check_routing(gpu, ref)
+    L.close()
+
+
+def test_zero_tokens_is_a_no_op():
+    data = Data(configs.TINY)
+    L = make_layer(B, data)
+    x = B.activations_to_device(data.x[:0])
+    idx, w = L.route(x)
+    u = L.union(idx)
+    y = L.forward(x, idx, w, u)
+    assert y.shape == (0, configs.TINY.hidden)
+    L.close()
+
+
+def test_unplaced_routed_expert_is_a_state_error():
+    spec = configs.TINY
+    data = Data(spec)
+    ref = oracle_route(data)
+    missing = int(ref["idx"][0, 0])
+    L = make_layer(B, data, place=[e for e in range(spec.n_experts) if e != missing])
+    x = B.activations_to_device(data.x)
+    idx, w = L.route(x)
+    u = L.union(idx)
+    with pytest.raises(B.ColiError) as ei:
+        L.forward(x, idx, w, u)
+    assert ei.value.status == B.E_STATE
+    # the layer stays usable once the expert is placed
+    L.place(missing, data.blobs([missing])[missing])
+    y = L.forward(x, idx, w, u)
+    torch.cuda.synchronize()
+    check_outputs(y.cpu().numpy(), oracle_y(data, ref, range(spec.n_tok)), "after placing")
+    L.close()
+
+
+def test_union_flags_out_of_range_ids():
+    data = Data(configs.TINY)
+    L = make_layer(B, data)
+    bad = torch.tensor([[0, 1, 2, 99], [3, 4, 5, 6]], dtype=torch.int32, device="cuda")
+    u = L.union(bad)
+    torch.cuda.synchronize()
+    assert L.device_errors() & 1
+    assert int(u["n_union"].cpu()[0]) == 7
+    assert L.device_errors() == 0
+    L.close()
+
+
+def test_max_tokens_is_enforced():
+    data = Data(configs.TINY)
+    L = make_layer(B, data, max_tokens=4)
+    x = B.activations_to_device(data.x)          # 8 tokens > 4
+    with pytest.raises(B.ColiError) as ei:
+        L.route(x)
+    assert ei.value.status == B.E_INVALID
+    L.close()
