@@ -103,12 +103,9 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
         x = x_all[(s % n_slices) * n_tok:(s % n_slices + 1) * n_tok]
         st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
         p = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
-        B._check(lib.coli_moe_route(L.handle, p(x), n_tok, p(bf["idx"]), p(bf["w"]), st), L.handle)
-        B._check(lib.coli_moe_union(L.handle, p(bf["idx"]), n_tok, p(bf["n_union"]), p(bf["union_ids"]),
-                                    p(bf["counts"]), p(bf["offsets"]), p(bf["gather"]), st), L.handle)
-        B._check(lib.coli_moe_forward(L.handle, p(x), n_tok, p(bf["idx"]), p(bf["w"]), p(bf["n_union"]),
-                                      p(bf["union_ids"]), p(bf["counts"]), p(bf["offsets"]),
-                                      p(bf["gather"]), p(bf["y"]), st), L.handle)
+        B._check(lib.coli_moe_layer(L.handle, p(x), n_tok, p(bf["idx"]), p(bf["w"]), p(bf["n_union"]),
+                                    p(bf["union_ids"]), p(bf["counts"]), p(bf["offsets"]),
+                                    p(bf["gather"]), p(bf["y"]), st), L.handle)
         return bf
 
     # 1) eager pass with per-kernel events (roofline of the dominant kernel)

@@ -187,6 +187,20 @@ coli_status coli_moe_forward(coli_layer *layer, const void *x, int32_t n_tok,
                              const int32_t *counts, const int32_t *offsets,
                              const int32_t *gather, float *y, void *stream);
 
+/* The whole layer in one call: route, union and forward of n_tok tokens,
+ * writing the same outputs as coli_moe_route, coli_moe_union and
+ * coli_moe_forward called in sequence (same pointer conventions).  For small
+ * batches (n_tok <= 4, n_experts <= 256, every expert in VRAM, GEMV
+ * strategy) it runs as three launches: router + top-k + union together with
+ * the shared expert's gate/up, then the routed gate/up, then the down
+ * projection which also combines; the results are bit-identical to the
+ * three separate calls.  Otherwise it issues the three calls. */
+coli_status coli_moe_layer(coli_layer *layer, const void *x, int32_t n_tok,
+                           int32_t *topk_idx, float *topk_w, int32_t *n_union,
+                           int32_t *union_ids, int32_t *counts,
+                           int32_t *offsets, int32_t *gather, float *y,
+                           void *stream);
+
 /* Choose the forward strategy (coli_path).  Default COLI_PATH_AUTO. */
 coli_status coli_layer_set_path(coli_layer *layer, int32_t path);
 

@@ -38,6 +38,7 @@ SIGNATURES = {
     "coli_moe_union": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p]),
     "coli_moe_forward": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "coli_layer_set_path": (C.c_int, [_p, _i32]),
+    "coli_moe_layer": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "coli_layer_stream_stats": (C.c_int, [_p, _p, _p]),
     "coli_layer_device_errors": (C.c_int, [_p, _p]),
     "coli_layer_set_timing": (C.c_int, [_p, _i32]),
@@ -192,6 +193,28 @@ class MoELayer:
                                     _dptr(u["offsets"]), _dptr(u["gather"]), _dptr(y), _stream()),
                self.handle)
         return y
+
+    def _union_bufs(self, n):
+        import torch
+        E = self.dims.n_experts
+        return dict(n_union=self._new((1,), torch.int32),
+                    union_ids=self._new((E,), torch.int32),
+                    counts=self._new((E,), torch.int32),
+                    offsets=self._new((E + 1,), torch.int32),
+                    gather=self._new((max(n * self.dims.top_k, 1),), torch.int32))
+
+    def layer(self, x):
+        """Route, union and forward in one call (coli_moe_layer)."""
+        import torch
+        n, k = x.shape[0], self.dims.top_k
+        idx = self._new((n, k), torch.int32)
+        w = self._new((n, k), torch.float32)
+        u = self._union_bufs(n)
+        y = self._new((n, self.dims.hidden), torch.float32)
+        _check(lib.coli_moe_layer(self.handle, _dptr(x), n, _dptr(idx), _dptr(w), _dptr(u["n_union"]),
+                                  _dptr(u["union_ids"]), _dptr(u["counts"]), _dptr(u["offsets"]),
+                                  _dptr(u["gather"]), _dptr(y), _stream()), self.handle)
+        return y, idx, w, u
 
     def __call__(self, x):
         idx, w = self.route(x)

@@ -171,6 +171,7 @@ struct coli_layer {
     int32_t *n_chunks = nullptr;
     int max_chunks = 0;
     int32_t *err = nullptr;
+    int32_t *sync_counters = nullptr;  // [1 + H/32] arrival counters, zero at rest
     uint8_t *pin_stage = nullptr;    // pinned staging for placement
 
     // tiered forward
@@ -300,6 +301,35 @@ int choose_path(const coli_layer *L, int n_tok) {
     return n_tok <= 2 ? COLI_PATH_GEMV : COLI_PATH_GROUPED;
 }
 
+FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, const int32_t *n_union,
+                  const int32_t *union_ids, const int32_t *counts, const int32_t *offsets,
+                  const int32_t *gather, float *y) {
+    FwdArgs a{};
+    a.x = x;
+    a.act_bf16 = L->d.act == COLI_ACT_BF16;
+    a.table = L->table_dev;
+    a.n_union = n_union;
+    a.union_ids = union_ids;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.gather = gather;
+    a.topk_w = topk_w;
+    a.n_tok = n_tok;
+    a.k = L->d.top_k;
+    a.hidden = L->d.hidden;
+    a.inter = L->d.inter;
+    a.n_experts = L->d.n_experts;
+    a.has_shared = L->d.has_shared;
+    a.lay = L->lay;
+    a.h = L->h;
+    a.ys = L->ys;
+    a.y = y;
+    a.chunks = L->chunks;
+    a.n_chunks = L->n_chunks;
+    a.skip_shared = 0;
+    return a;
+}
+
 coli_status launch_experts(coli_layer *L, const FwdArgs &a, int path, hipStream_t s) {
     hipError_t e;
     if (path == COLI_PATH_GEMV) {
@@ -339,7 +369,8 @@ void free_layer(coli_layer *L) {
     for (auto p : L->pin_tables) (void)hipHostFree(const_cast<uint8_t **>(p));
     for (auto p : L->dev_tables) (void)hipFree(const_cast<uint8_t **>(p));
     if (L->side) (void)hipStreamDestroy(L->side);
-    void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->ys, L->chunks, L->n_chunks, L->err};
+    void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->ys, L->chunks, L->n_chunks, L->err,
+                    L->sync_counters};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (L->pin_stage) (void)hipHostFree(L->pin_stage);
@@ -446,6 +477,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->chunks), sizeof(ChunkDesc) * L->max_chunks, "work list"},
         {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
         {reinterpret_cast<void **>(&L->err), sizeof(int32_t), "error flags"},
+        {reinterpret_cast<void **>(&L->sync_counters), sizeof(int32_t) * (1 + H / 32), "arrival counters"},
     };
     for (auto &a : allocs) {
         if ((he = hipMalloc(a.p, a.n)) != hipSuccess) {
@@ -457,6 +489,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     }
     if ((he = hipMemset(L->table_dev, 0, sizeof(void *) * (E + 1))) != hipSuccess ||
         (he = hipMemset(L->err, 0, sizeof(int32_t))) != hipSuccess ||
+        (he = hipMemset(L->sync_counters, 0, sizeof(int32_t) * (1 + H / 32))) != hipSuccess ||
         (he = hipMemset(L->bias, 0, sizeof(float) * E)) != hipSuccess ||
         (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_stage), L->lay.total, hipHostMallocDefault)) != hipSuccess ||
         (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_union), sizeof(int32_t) * (E + 1), hipHostMallocDefault)) != hipSuccess ||
@@ -614,28 +647,7 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int path = choose_path(L, n_tok);
 
-    FwdArgs a{};
-    a.x = x;
-    a.act_bf16 = L->d.act == COLI_ACT_BF16;
-    a.table = L->table_dev;
-    a.n_union = n_union;
-    a.union_ids = union_ids;
-    a.counts = counts;
-    a.offsets = offsets;
-    a.gather = gather;
-    a.topk_w = topk_w;
-    a.n_tok = n_tok;
-    a.k = L->d.top_k;
-    a.hidden = L->d.hidden;
-    a.inter = L->d.inter;
-    a.n_experts = L->d.n_experts;
-    a.has_shared = L->d.has_shared;
-    a.lay = L->lay;
-    a.h = L->h;
-    a.ys = L->ys;
-    a.y = y;
-    a.chunks = L->chunks;
-    a.n_chunks = L->n_chunks;
+    FwdArgs a = make_args(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y);
 
     L->last_streamed = 0;
     L->last_bytes = 0;
@@ -703,6 +715,59 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
         HIP_TRY(L, launch_combine(a, s), "combine launch");
     }
     if (!streamed.empty() || !all_routed_resident(L)) HIP_TRY(L, hipStreamSynchronize(s), "tiered forward sync");
+    return COLI_OK;
+}
+
+coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t *topk_idx, float *topk_w,
+                           int32_t *n_union, int32_t *union_ids, int32_t *counts, int32_t *offsets,
+                           int32_t *gather, float *y, void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
+        return fail(L, COLI_E_INVALID, "NULL device pointer");
+    const bool fused = n_tok <= kFrontMaxTok && L->d.n_experts <= 256 && all_routed_resident(L) &&
+                       choose_path(L, n_tok) == COLI_PATH_GEMV && L->router_set &&
+                       (!L->d.has_shared || L->experts[L->d.n_experts].tier == COLI_TIER_VRAM);
+    if (!fused) {
+        if ((st = coli_moe_route(L, x, n_tok, topk_idx, topk_w, stream)) != COLI_OK) return st;
+        if ((st = coli_moe_union(L, topk_idx, n_tok, n_union, union_ids, counts, offsets, gather, stream)) != COLI_OK)
+            return st;
+        return coli_moe_forward(L, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
+                                stream);
+    }
+    DeviceGuard guard(L->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FwdArgs a = make_args(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y);
+    FrontArgs f{};
+    f.wt = L->wt;
+    f.bias = L->bias;
+    f.logits = L->logits;
+    f.topk_idx = topk_idx;
+    f.topk_w = topk_w;
+    f.n_union = n_union;
+    f.union_ids = union_ids;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.gather = gather;
+    f.counter = L->sync_counters;
+    hipError_t e;
+    {
+        KernelMark m(L, COLI_K_ROUTER, s);
+        if ((e = launch_decode_front(a, f, L->max_lds, s)) != hipSuccess) return hip_fail(L, e, "decode front launch");
+    }
+    {
+        KernelMark m(L, COLI_K_GATEUP, s);
+        FwdArgs ar = a;
+        ar.skip_shared = 1;
+        const int routed = std::min(n_tok * L->d.top_k, L->d.n_experts);
+        if ((e = launch_gemv_gateup(ar, L->max_lds, s, 0, routed)) != hipSuccess)
+            return hip_fail(L, e, "gemv gate/up launch");
+    }
+    KernelMark m(L, COLI_K_DOWN, s);
+    if ((e = launch_gemv_down(a, L->max_lds, s, L->sync_counters + 1)) != hipSuccess)
+        return hip_fail(L, e, "gemv down launch");
     return COLI_OK;
 }
 

@@ -1,0 +1,185 @@
+// decode.hip -- front half of a small-batch layer call in one launch:
+//   * router blocks: one wave per expert computes its logit for every token
+//     in the fixed summation order (identical bits to the standalone router
+//     kernel);
+//   * shared-expert blocks: the always-on shared expert does not depend on
+//     routing, so its gate/up panels stream from HBM while the router runs;
+//   * the last router block to finish (arrival counter) selects the top-k of
+//     every token and builds the union, so the routed gate/up kernel can
+//     start right after this launch.
+// Top-k: each wave ranks its 64 candidates locally (keys are unique:
+// (logit desc, id asc)), the k best of each wave are the only possible
+// winners, and ranking those 4k finalists gives the global slots.  Union:
+// LDS histogram, block scans, and an in-order rank for the gather.
+#include "dev_gemv.h"
+
+#pragma clang fp contract(off)
+
+namespace coli {
+namespace {
+
+constexpr int kFrontThreads = 256;
+constexpr int kFrontMaxExperts = 256;
+
+template <int NT, bool BF16>
+__device__ __forceinline__ void wave_router(const FwdArgs &a, const FrontArgs &f, int e) {
+    const int lane = threadIdx.x & 63;
+    const int H = a.hidden, E = a.n_experts;
+    const float *wrow = f.wt + static_cast<size_t>(e) * H + lane;
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+    constexpr int U = NT == 1 ? 32 : 16;
+    const int steps = H / 64;
+    int j0 = 0;
+    for (; j0 + U <= steps; j0 += U) {
+        float wv[U], xv[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (j0 + u) * 64 + lane;
+            wv[u] = wrow[(j0 + u) * 64];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const size_t idx = static_cast<size_t>(min(t, a.n_tok - 1)) * H + k;
+                xv[u][t] = BF16 ? dev::bf16_bits_to_f32(static_cast<const uint16_t *>(a.x)[idx])
+                                : static_cast<const float *>(a.x)[idx];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(xv[u][t], wv[u], acc[t]);
+    }
+    for (; j0 < steps; ++j0) {
+        const int k = j0 * 64 + lane;
+        const float wv = wrow[j0 * 64];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const size_t idx = static_cast<size_t>(min(t, a.n_tok - 1)) * H + k;
+            const float xv = BF16 ? dev::bf16_bits_to_f32(static_cast<const uint16_t *>(a.x)[idx])
+                                  : static_cast<const float *>(a.x)[idx];
+            acc[t] = __builtin_fmaf(xv, wv, acc[t]);
+        }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = acc[t] + __shfl_down(acc[t], s, 64);
+    if (lane == 0) {
+        const float b = f.bias ? f.bias[e] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (t < a.n_tok) dev::store_coherent(f.logits + static_cast<size_t>(t) * E + e, acc[t] + b);
+    }
+}
+
+// Top-k of every token and the union, by the last router block.
+__device__ void select_and_union(const FwdArgs &a, const FrontArgs &f) {
+    __shared__ uint64_t s_key[kFrontMaxExperts];
+    __shared__ uint64_t s_fin[4 * kMaxTopK];
+    __shared__ float s_sig[kMaxTopK];
+    __shared__ int s_idx[kFrontMaxTok * kMaxTopK];
+    __shared__ int s_cnt[kFrontMaxExperts];
+    __shared__ int s_off[kFrontMaxExperts];
+    __shared__ int s_tmp[kFrontThreads / 64 + 1];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int E = a.n_experts, k = a.k, n_tok = a.n_tok;
+    for (int t = 0; t < n_tok; ++t) {
+        // key = (logit order, then lower id first); unique per expert.
+        const uint32_t low = 0xFFFFFFFFu - static_cast<uint32_t>(tid);
+        uint64_t key = low;
+        if (tid < E)
+            key |= static_cast<uint64_t>(dev::float_key(dev::load_coherent(f.logits + static_cast<size_t>(t) * E + tid)))
+                   << 32;
+        s_key[tid] = key;
+        __syncthreads();
+        int r = 0;
+        for (int j = 0; j < 64; ++j) r += s_key[64 * wave + j] > key ? 1 : 0;
+        if (r < k) s_fin[wave * k + r] = key;
+        __syncthreads();
+        if (tid < 4 * k) {
+            const uint64_t fk = s_fin[tid];
+            int R = 0;
+            for (int j = 0; j < 4 * k; ++j) R += s_fin[j] > fk ? 1 : 0;
+            if (R < k) {
+                const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(fk));
+                const float l = dev::load_coherent(f.logits + static_cast<size_t>(t) * E + e);
+                s_idx[t * k + R] = e;
+                f.topk_idx[static_cast<size_t>(t) * k + R] = e;
+                s_sig[R] = 1.0f / (1.0f + expf(-l));
+            }
+        }
+        __syncthreads();
+        if (tid < k) {
+            float sum = 0.0f;
+            for (int j = 0; j < k; ++j) sum = sum + s_sig[j];
+            f.topk_w[static_cast<size_t>(t) * k + tid] = s_sig[tid] / sum;
+        }
+        __syncthreads();
+    }
+    // Union of the n_tok * k selections.
+    const int n_ent = n_tok * k;
+    s_cnt[tid] = 0;
+    __syncthreads();
+    if (tid < n_ent) atomicAdd(&s_cnt[s_idx[tid]], 1);
+    __syncthreads();
+    const int c = tid < E ? s_cnt[tid] : 0;
+    int total = 0;
+    const int excl = dev::block_exclusive_scan<kFrontThreads>(c, s_tmp, &total);
+    if (tid < E) {
+        f.counts[tid] = c;
+        f.offsets[tid] = excl;
+        s_off[tid] = excl;
+    }
+    if (tid == 0) f.offsets[E] = total;
+    const int flag = (tid < E && c > 0) ? 1 : 0;
+    int nu = 0;
+    const int pos = dev::block_exclusive_scan<kFrontThreads>(flag, s_tmp, &nu);
+    if (flag) f.union_ids[pos] = tid;
+    if (tid == 0) *f.n_union = nu;
+    __syncthreads();
+    if (tid < n_ent) {
+        const int e = s_idx[tid];
+        int before = 0;
+        for (int i = 0; i < tid; ++i) before += s_idx[i] == e ? 1 : 0;
+        f.gather[s_off[e] + before] = tid;
+    }
+}
+
+template <int NT, bool BF16>
+__global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, FrontArgs f, int router_blocks) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    if (static_cast<int>(blockIdx.x) >= router_blocks) {
+        const int p = blockIdx.x - router_blocks;
+        dev::gateup_panel<NT>(a, a.table[a.n_experts], a.n_tok * a.k, a.n_tok, p, lds);
+        return;
+    }
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e < a.n_experts) wave_router<NT, BF16>(a, f, e);
+    if (dev::arrive_last(f.counter, router_blocks)) select_and_union(a, f);
+}
+
+template <int NT>
+hipError_t launch_t(const FwdArgs &a, const FrontArgs &f, size_t lds, hipStream_t s) {
+    const int router_blocks = (a.n_experts + 3) / 4;
+    const int grid = router_blocks + (a.has_shared ? a.inter / kPanel : 0);
+    if (a.act_bf16)
+        decode_front_kernel<NT, true><<<grid, kFrontThreads, lds, s>>>(a, f, router_blocks);
+    else
+        decode_front_kernel<NT, false><<<grid, kFrontThreads, lds, s>>>(a, f, router_blocks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_lds, hipStream_t s) {
+    if (a.n_tok < 1 || a.n_tok > kFrontMaxTok || a.n_experts > kFrontMaxExperts) return hipErrorInvalidValue;
+    const int nt = a.n_tok == 1 ? 1 : (a.n_tok == 2 ? 2 : 4);
+    const size_t lds = a.has_shared ? dev::gateup_lds_bytes(nt, a.hidden) : 0;
+    if (lds > max_lds) return hipErrorInvalidValue;
+    if (nt == 1) return launch_t<1>(a, f, lds, s);
+    if (nt == 2) return launch_t<2>(a, f, lds, s);
+    return launch_t<4>(a, f, lds, s);
+}
+
+}  // namespace coli

@@ -1,0 +1,127 @@
+// dev_common.h -- small device helpers shared by the kernel files.
+#pragma once
+
+#include "internal.h"
+
+namespace coli {
+namespace dev {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
+}
+
+// Keeps a constant in a VGPR so the compiler can use three-operand
+// v_and_or_b32 (VOP3 cannot encode literals on this ISA).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+    asm volatile("" : "+v"(c));
+    return c;
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+
+// Work unit u of a forward call: routed union entry (u < n_union) or the
+// shared expert (u == n_union).  Returns false when u is past the last unit.
+__device__ __forceinline__ bool resolve(const FwdArgs &a, int u, int &e, int &r0, int &m) {
+    const int nu = *a.n_union;
+    if (u < nu) {
+        e = a.union_ids[u];
+        r0 = a.offsets[e];
+        m = a.counts[e];
+        return true;
+    }
+    if (u == nu && a.has_shared) {
+        e = a.n_experts;
+        r0 = a.n_tok * a.k;
+        m = a.n_tok;
+        return true;
+    }
+    return false;
+}
+
+// Token of hidden-buffer row `row`: routed rows are in gather order, shared
+// rows follow at n_tok*k + t.
+__device__ __forceinline__ int token_of_row(const FwdArgs &a, int row) {
+    const int routed = a.n_tok * a.k;
+    return row < routed ? a.gather[row] / a.k : row - routed;
+}
+
+// Monotonic unsigned key of a finite float (larger float -> larger key);
+// -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t float_key(float f) {
+    const uint32_t b = __float_as_uint(f + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exclusive scan of one int per thread over a block of NT threads; *total
+// gets the sum.  s_tmp needs NT/64 + 1 ints.  Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
+    constexpr int kWaves = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) s_tmp[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int wv = lane < kWaves ? s_tmp[lane] : 0;
+        int inc = wv;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane < kWaves) s_tmp[lane] = inc - wv;
+        if (lane == kWaves - 1) s_tmp[kWaves] = inc;
+    }
+    __syncthreads();
+    const int excl = s_tmp[wave] + x - v;
+    *total = s_tmp[kWaves];
+    __syncthreads();
+    return excl;
+}
+
+// Device-coherent store / load of data handed from one workgroup to another
+// inside a launch.  Relaxed atomics at agent scope compile to plain global
+// stores/loads with the device-coherence bit (sc1): they bypass the per-XCD
+// L2 without the whole-cache writeback and invalidate that a fence costs.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns true in exactly one workgroup: the last of `expected` workgroups
+// to arrive at `counter` (which it resets to 0 for the next launch).  The
+// data a workgroup hands over must have been written with store_coherent and
+// must be read with load_coherent: each wave waits for its stores to complete
+// before the workgroup arrives, so the last workgroup finds all of them.
+// All threads of the workgroup must call it.
+__device__ __forceinline__ bool arrive_last(int32_t *counter, int expected) {
+    __shared__ int s_last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == expected - 1) ? 1 : 0;
+        if (s_last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return s_last != 0;
+}
+
+}  // namespace dev
+}  // namespace coli

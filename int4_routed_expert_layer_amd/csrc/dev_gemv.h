@@ -1,0 +1,361 @@
+// dev_gemv.h -- decode-shaped expert FFN work items on the vector ALUs.
+//
+// When each union expert serves one to four tokens the expert matmuls are
+// matrix-vector products bound by HBM bandwidth: every weight byte is used
+// once per token, so the work stays on the VALU and is shaped for streaming.
+// A 256-thread workgroup owns one 16-row panel (gate/up) or two panels
+// (down) of one expert; its waves split the reduction axis, each lane issues
+// one 16-byte load per 1 KB chunk (fully coalesced), weight loads are double
+// buffered in registers (the next group of chunks is in flight while the
+// current one is multiplied), and the activations sit in LDS.
+//
+// Int4 expansion costs five integer ops per 8 weights.  A packed dword holds
+// columns k0..k0+7 as u = q + 8 in nibble slots (j, 4+j) for the column pair
+// (2j, 2j+1).  With the fp16 exponent pattern 0x6400 (1024, ulp 1):
+//   pair 0: (w & 0x000F000F) | 0x64006400           -> 1024 + u
+//   pair 1: (w & 0x00F000F0) | 0x64006400           -> 1024 + 16 u
+//   pairs 2, 3: the same on w >> 8.
+// The activations of pairs 1 and 3 are staged pre-divided by 16 (exact), so
+// every v_dot2 product is (1024 + u) x or (64 + u) x.  The offsets are
+// removed by seeding the dot with
+//   c = -1032 (x0 + x1 + x4 + x5) - 1152 (x2' + x3' + x6' + x7')
+// (x' the staged, divided values), computed once per 8 activations, so the
+// dot of one dword is sum (u-8) x = sum q x up to fp32 rounding, and one
+// fused multiply-add applies the fp16 group scale.  Activations enter as
+// fp16 (bf16/fp32 inputs are rounded once when staged; they must lie inside
+// the fp16 range).
+//
+// Partial sums are reduced across the four lanes that share a row and then
+// across waves in a fixed order, so results are deterministic.
+#pragma once
+
+#include "dev_common.h"
+
+namespace coli {
+namespace dev {
+
+// sum over the 8 columns of one packed dword of q * x, given the staged
+// activations xv (pairs 1 and 3 pre-divided by 16) and their seed c.
+__device__ __forceinline__ float dot8(uint32_t w, uint4 xv, float c, uint32_t M0, uint32_t M1,
+                                      uint32_t G) {
+    const uint32_t w8 = w >> 8;
+    float d = dot2_f16((w & M0) | G, xv.x, c);
+    d = dot2_f16((w & M1) | G, xv.y, d);
+    d = dot2_f16((w8 & M0) | G, xv.z, d);
+    d = dot2_f16((w8 & M1) | G, xv.w, d);
+    return d;
+}
+
+// Stage 8 activations into LDS as fp16 with the pair-1/3 columns divided by
+// 16, and their dot seed.
+__device__ __forceinline__ void stage8(const float *v, uint8_t *dst_x, float *dst_c) {
+    _Float16 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bool odd_pair = (i & 2) != 0;          // columns 2,3,6,7
+        h[i] = static_cast<_Float16>(odd_pair ? v[i] * 0.0625f : v[i]);
+    }
+    float ce = 0.0f, co = 0.0f;
+    ce = ce + static_cast<float>(h[0]);
+    ce = ce + static_cast<float>(h[1]);
+    ce = ce + static_cast<float>(h[4]);
+    ce = ce + static_cast<float>(h[5]);
+    co = co + static_cast<float>(h[2]);
+    co = co + static_cast<float>(h[3]);
+    co = co + static_cast<float>(h[6]);
+    co = co + static_cast<float>(h[7]);
+    // (1024+u) x - 1032 x = (u-8) x;  (1024+16u) x' - 1152 x' = (u-8) (16 x').
+    *dst_c = -1032.0f * ce - 1152.0f * co;
+    *reinterpret_cast<uint4 *>(dst_x) = __builtin_bit_cast(uint4, h);
+}
+
+// LDS bytes of one gate/up panel item / one down panel-group item.
+__host__ __device__ inline size_t gateup_lds_bytes(int maxm, int hidden) {
+    return static_cast<size_t>(maxm) * hidden * 2 + static_cast<size_t>(maxm) * (hidden / 8) * 4 +
+           static_cast<size_t>(4) * maxm * 16 * 2 * 4;
+}
+__host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
+    return static_cast<size_t>(maxm) * inter * 2 + static_cast<size_t>(maxm) * (inter / 8) * 4 +
+           static_cast<size_t>(4) * maxm * 16 * 4;
+}
+
+constexpr int kPipeGroup = 2;   // chunks per register buffer
+
+struct GateUpBuf {
+    uint4 gw[kPipeGroup], uw[kPipeGroup];
+    uint2 gs[kPipeGroup], us[kPipeGroup];
+};
+
+struct GateUpPtrs {
+    const uint8_t *gq, *uq, *gs, *us;
+};
+
+__device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpPtrs &P, int first, int step,
+                                            int C) {
+#pragma unroll
+    for (int g = 0; g < kPipeGroup; ++g) {
+        const int c = min(first + step * g, C - 1);
+        b.gw[g] = *reinterpret_cast<const uint4 *>(P.gq + static_cast<size_t>(c) * kChunkBytes);
+        b.uw[g] = *reinterpret_cast<const uint4 *>(P.uq + static_cast<size_t>(c) * kChunkBytes);
+        b.gs[g] = *reinterpret_cast<const uint2 *>(P.gs + static_cast<size_t>(c) * kScaleChunkBytes);
+        b.us[g] = *reinterpret_cast<const uint2 *>(P.us + static_cast<size_t>(c) * kScaleChunkBytes);
+    }
+}
+
+template <int MAXM>
+__device__ __forceinline__ void gateup_math(const GateUpBuf &b, const uint8_t *xs, const float *cs, int H,
+                                            int first, int step, int count, int kq, int mc,
+                                            uint32_t M0, uint32_t M1, uint32_t G, float *gacc,
+                                            float *vacc) {
+#pragma unroll
+    for (int g = 0; g < kPipeGroup; ++g) {
+        if (g >= count) continue;
+        const int c = first + step * g;
+        const uint32_t gws[4] = {b.gw[g].x, b.gw[g].y, b.gw[g].z, b.gw[g].w};
+        const uint32_t uws[4] = {b.uw[g].x, b.uw[g].y, b.uw[g].z, b.uw[g].w};
+        const uint32_t gss[2] = {b.gs[g].x, b.gs[g].y};
+        const uint32_t uss[2] = {b.us[g].x, b.us[g].y};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float sg = half_bits_to_f32((gss[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+            const float su = half_bits_to_f32((uss[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+            const int k0 = c * kChunkK + 32 * s + 8 * kq;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                if (m < mc) {
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(xs + (static_cast<size_t>(m) * H + k0) * 2);
+                    const float c8 = cs[m * (H / 8) + (k0 >> 3)];
+                    gacc[m] = __builtin_fmaf(sg, dot8(gws[s], xv, c8, M0, M1, G), gacc[m]);
+                    vacc[m] = __builtin_fmaf(su, dot8(uws[s], xv, c8, M0, M1, G), vacc[m]);
+                }
+            }
+        }
+    }
+}
+
+// One gate/up work item: rows 16p..16p+15 of expert blob `blob`, for the M
+// tokens of hidden-buffer rows r0..r0+M-1.  Writes h rows (fp16).  All 256
+// threads must call it (it synchronises the workgroup).
+template <int MAXM>
+__device__ void gateup_panel(const FwdArgs &a, const uint8_t *blob, int r0, int M, int p, uint8_t *lds) {
+    const int H = a.hidden, I = a.inter;
+    const int C = H / kChunkK;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 15, kq = lane >> 4;
+    GateUpPtrs P;
+    P.gq = blob + a.lay.gate_q + static_cast<size_t>(p) * C * kChunkBytes + lane * 16;
+    P.uq = blob + a.lay.up_q + static_cast<size_t>(p) * C * kChunkBytes + lane * 16;
+    P.gs = blob + a.lay.gate_s + static_cast<size_t>(p) * C * kScaleChunkBytes + row * 8;
+    P.us = blob + a.lay.up_s + static_cast<size_t>(p) * C * kScaleChunkBytes + row * 8;
+    // Chunks of this wave: wave, wave + 4, ...
+    const int nper = wave < C ? (C - wave + 3) / 4 : 0;
+    const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+
+    // LDS: x [MAXM][H] fp16, seeds [MAXM][H/8] fp32, partials [4][MAXM][16][2].
+    uint8_t *xs = lds;
+    float *cs = reinterpret_cast<float *>(lds + static_cast<size_t>(MAXM) * H * 2);
+    float *red = cs + MAXM * (H / 8);
+
+    for (int mb = 0; mb < M; mb += MAXM) {
+        const int mc = min(MAXM, M - mb);
+        float gacc[MAXM], vacc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) gacc[m] = vacc[m] = 0.0f;
+
+        GateUpBuf A, B;
+        gateup_load(A, P, wave, 4, C);          // weights do not depend on x
+        __syncthreads();
+        for (int i = tid; i < mc * (H / 8); i += 256) {
+            const int m = i / (H / 8), q = i % (H / 8);
+            const int t = token_of_row(a, r0 + mb + m);
+            float v[8];
+            if (a.act_bf16) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * H + 8 * q);
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = bf16_bits_to_f32(w4[j] & 0xFFFFu);
+                    v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
+                }
+            } else {
+                const float4 *src = reinterpret_cast<const float4 *>(
+                    static_cast<const float *>(a.x) + static_cast<size_t>(t) * H + 8 * q);
+                const float4 lo = src[0], hi = src[1];
+                v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+                v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+            }
+            stage8(v, xs + (static_cast<size_t>(m) * H + 8 * q) * 2, cs + m * (H / 8) + q);
+        }
+        __syncthreads();
+        // i indexes this wave's chunk list; buffers alternate A, B.
+        for (int i = 0; i < nper; i += 2 * kPipeGroup) {
+            if (i + kPipeGroup < nper) gateup_load(B, P, wave + 4 * (i + kPipeGroup), 4, C);
+            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(kPipeGroup, nper - i), kq, mc, M0, M1, G,
+                              gacc, vacc);
+            if (i + 2 * kPipeGroup < nper) gateup_load(A, P, wave + 4 * (i + 2 * kPipeGroup), 4, C);
+            if (i + kPipeGroup < nper)
+                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + kPipeGroup), 4,
+                                  min(kPipeGroup, nper - i - kPipeGroup), kq, mc, M0, M1, G, gacc, vacc);
+        }
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            gacc[m] = gacc[m] + __shfl_xor(gacc[m], 16, 64);
+            gacc[m] = gacc[m] + __shfl_xor(gacc[m], 32, 64);
+            vacc[m] = vacc[m] + __shfl_xor(vacc[m], 16, 64);
+            vacc[m] = vacc[m] + __shfl_xor(vacc[m], 32, 64);
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                red[((wave * MAXM + m) * 16 + row) * 2 + 0] = gacc[m];
+                red[((wave * MAXM + m) * 16 + row) * 2 + 1] = vacc[m];
+            }
+        }
+        __syncthreads();
+        if (tid < mc * 16) {
+            const int m = tid >> 4, r = tid & 15;
+            float g = 0.0f, v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                g = g + red[((w * MAXM + m) * 16 + r) * 2 + 0];
+                v = v + red[((w * MAXM + m) * 16 + r) * 2 + 1];
+            }
+            const float hval = g / (1.0f + expf(-g)) * v;
+            a.h[static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r] = static_cast<_Float16>(hval);
+        }
+    }
+}
+
+struct DownBuf {
+    uint4 w[kPipeGroup];
+    uint2 s[kPipeGroup];
+};
+
+__device__ __forceinline__ void down_load(DownBuf &b, const uint8_t *dq, const uint8_t *ds, int first,
+                                          int C) {
+#pragma unroll
+    for (int g = 0; g < kPipeGroup; ++g) {
+        const int c = min(first + g, C - 1);
+        b.w[g] = *reinterpret_cast<const uint4 *>(dq + static_cast<size_t>(c) * kChunkBytes);
+        b.s[g] = *reinterpret_cast<const uint2 *>(ds + static_cast<size_t>(c) * kScaleChunkBytes);
+    }
+}
+
+template <int MAXM>
+__device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, const float *cs, int I,
+                                          int first, int count, int kq, int mc, uint32_t M0,
+                                          uint32_t M1, uint32_t G, float *acc) {
+#pragma unroll
+    for (int g = 0; g < kPipeGroup; ++g) {
+        if (g >= count) continue;
+        const int c = first + g;
+        const uint32_t ws[4] = {b.w[g].x, b.w[g].y, b.w[g].z, b.w[g].w};
+        const uint32_t ss[2] = {b.s[g].x, b.s[g].y};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float sf = half_bits_to_f32((ss[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+            const int k0 = c * kChunkK + 32 * s + 8 * kq;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                if (m < mc) {
+                    const uint4 hv = *reinterpret_cast<const uint4 *>(hs + (static_cast<size_t>(m) * I + k0) * 2);
+                    const float c8 = cs[m * (I / 8) + (k0 >> 3)];
+                    acc[m] = __builtin_fmaf(sf, dot8(ws[s], hv, c8, M0, M1, G), acc[m]);
+                }
+            }
+        }
+    }
+}
+
+// One down work item: output panels 2pg and 2pg+1 of expert blob `blob` for
+// hidden rows r0..r0+M-1.  Wave w takes panel 2pg + (w & 1) and reduction
+// half (w >> 1); the halves are summed through LDS in a fixed order.  Writes
+// the entry rows of ys (routed rows times their routing weight, shared rows
+// with weight 1).  All 256 threads must call it.
+template <int MAXM, bool COHERENT = false>
+__device__ void down_panelgroup(const FwdArgs &a, const uint8_t *blob, int r0, int M, int pg, uint8_t *lds) {
+    const int H = a.hidden, I = a.inter;
+    const int C = I / kChunkK;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 15, kq = lane >> 4;
+    const int p = 2 * pg + (wave & 1), half = wave >> 1;
+    const int c_begin = half == 0 ? 0 : (C + 1) / 2;
+    const int c_end = half == 0 ? (C + 1) / 2 : C;
+    const int nper = c_end - c_begin;
+    const uint8_t *dq = blob + a.lay.down_q + static_cast<size_t>(p) * C * kChunkBytes + lane * 16;
+    const uint8_t *ds = blob + a.lay.down_s + static_cast<size_t>(p) * C * kScaleChunkBytes + row * 8;
+    uint8_t *hs = lds;
+    float *cs = reinterpret_cast<float *>(lds + static_cast<size_t>(MAXM) * I * 2);
+    float *red = cs + MAXM * (I / 8);
+    const int routed = a.n_tok * a.k;
+    const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+
+    for (int mb = 0; mb < M; mb += MAXM) {
+        const int mc = min(MAXM, M - mb);
+        float acc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+        DownBuf A, B;
+        down_load(A, dq, ds, c_begin, C);
+        __syncthreads();
+        for (int i = tid; i < mc * (I / 8); i += 256) {
+            const int m = i / (I / 8), q = i % (I / 8);
+            const uint4 raw = *reinterpret_cast<const uint4 *>(a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q);
+            const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
+            stage8(v, hs + (static_cast<size_t>(m) * I + 8 * q) * 2, cs + m * (I / 8) + q);
+        }
+        __syncthreads();
+        for (int i = 0; i < nper; i += 2 * kPipeGroup) {
+            if (i + kPipeGroup < nper) down_load(B, dq, ds, c_begin + i + kPipeGroup, C);
+            down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), kq, mc, M0, M1, G, acc);
+            if (i + 2 * kPipeGroup < nper) down_load(A, dq, ds, c_begin + i + 2 * kPipeGroup, C);
+            if (i + kPipeGroup < nper)
+                down_math<MAXM>(B, hs, cs, I, c_begin + i + kPipeGroup, min(kPipeGroup, nper - i - kPipeGroup),
+                                kq, mc, M0, M1, G, acc);
+        }
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            acc[m] = acc[m] + __shfl_xor(acc[m], 16, 64);
+            acc[m] = acc[m] + __shfl_xor(acc[m], 32, 64);
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) red[(wave * MAXM + m) * 16 + row] = acc[m];
+        }
+        __syncthreads();
+        if (tid < 2 * mc * 16) {
+            const int side = tid / (mc * 16), rest = tid % (mc * 16);
+            const int m = rest >> 4, r = rest & 15;
+            // waves `side` (first half) and `side + 2` (second half)
+            const float d = red[(side * MAXM + m) * 16 + r] + red[((side + 2) * MAXM + m) * 16 + r];
+            const int hrow = r0 + mb + m;
+            const int entry = hrow < routed ? a.gather[hrow] : hrow;
+            const float wgt = hrow < routed ? a.topk_w[entry] : 1.0f;
+            float *dst = a.ys + static_cast<size_t>(entry) * H + (2 * pg + side) * kPanel + r;
+            if (COHERENT) store_coherent(dst, wgt * d);
+            else *dst = wgt * d;
+        }
+    }
+}
+
+// y rows for output panels 2pg, 2pg+1: per token, its k routed rows in slot
+// order, then the shared row.  Same order as the standalone combine kernel.
+// The rows were written by other workgroups with store_coherent.
+__device__ __forceinline__ void combine_panelgroup(const FwdArgs &a, int pg) {
+    const int H = a.hidden;
+    const int n = a.n_tok * 2 * kPanel;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int t = i / (2 * kPanel), col = 2 * kPanel * pg + i % (2 * kPanel);
+        float acc = load_coherent(a.ys + static_cast<size_t>(t * a.k) * H + col);
+        for (int j = 1; j < a.k; ++j) acc = acc + load_coherent(a.ys + static_cast<size_t>(t * a.k + j) * H + col);
+        if (a.has_shared) acc = acc + load_coherent(a.ys + static_cast<size_t>(a.n_tok * a.k + t) * H + col);
+        a.y[static_cast<size_t>(t) * H + col] = acc;
+    }
+}
+
+}  // namespace dev
+}  // namespace coli

@@ -69,6 +69,7 @@ struct FwdArgs {
     float *y;                       // [n_tok x H]
     const ChunkDesc *chunks;        // grouped path work list
     const int32_t *n_chunks;
+    int skip_shared;                // gate/up: the shared unit was already done
 };
 
 // route.hip
@@ -84,9 +85,26 @@ hipError_t launch_union(const int32_t *idx, int n_tok, int k, int n_experts,
                         hipStream_t s);
 hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
                        hipStream_t s);
-// gemv.hip
-hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s);
-hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s);
+// gemv.hip.  gate/up covers units [u_begin, u_begin + u_count) (u_count < 0:
+// to the end).  down with non-NULL combine_counters ([H/32] ints, zero at
+// rest) also writes y and needs every unit to be computed in this launch.
+hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, int u_begin = 0,
+                              int u_count = -1);
+hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s,
+                            int32_t *combine_counters = nullptr);
+// decode.hip: route + top-k + union of up to kFrontMaxTok tokens and, in the
+// same launch, the shared expert's gate/up.  Needs n_experts <= 256.
+constexpr int kFrontMaxTok = 4;
+struct FrontArgs {
+    const float *wt;          // router weight [E x H]
+    const float *bias;        // [E]
+    float *logits;            // [n_tok x E] scratch
+    int32_t *topk_idx;        // [n_tok x k]
+    float *topk_w;            // [n_tok x k]
+    int32_t *n_union, *union_ids, *counts, *offsets, *gather;
+    int32_t *counter;         // one int, zero at rest
+};
+hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_lds, hipStream_t s);
 // grouped.hip
 hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu,
                                  hipStream_t s);

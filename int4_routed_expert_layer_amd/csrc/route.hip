@@ -22,6 +22,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+template <bool BF16>
+__device__ __forceinline__ float load_x(const void *x, size_t i) {
+    if (BF16) return bf16_to_f32(static_cast<const uint16_t *>(x)[i]);
+    return static_cast<const float *>(x)[i];
+}
+
 // One 64-thread block per tile of TB tokens x TE experts.  wt is the router
 // weight transposed to [E x H] so lane l reads 64 consecutive floats.
 template <int TB, int TE, bool BF16, int UNROLL>
@@ -52,33 +58,39 @@ __global__ __launch_bounds__(64) void router_logits_kernel(
 #pragma unroll
         for (int i = 0; i < TE; ++i) acc[b][i] = 0.0f;
 
+    // Loads of a whole batch are issued before its FMAs; the chain order of
+    // every accumulator stays k = lane, lane+64, ... ascending.
     const int steps = hidden / 64;
-    for (int j0 = 0; j0 < steps; j0 += UNROLL) {
+    int j0 = 0;
+    for (; j0 + UNROLL <= steps; j0 += UNROLL) {
         float xv[UNROLL][TB], wv[UNROLL][TE];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int k = (j0 + u) * 64;
-            const bool ok = (j0 + u) < steps;
 #pragma unroll
-            for (int b = 0; b < TB; ++b) {
-                if (BF16)
-                    xv[u][b] = ok ? bf16_to_f32(static_cast<const uint16_t *>(x)[xoff[b] + k]) : 0.0f;
-                else
-                    xv[u][b] = ok ? static_cast<const float *>(x)[xoff[b] + k] : 0.0f;
-            }
+            for (int b = 0; b < TB; ++b) xv[u][b] = load_x<BF16>(x, xoff[b] + k);
 #pragma unroll
-            for (int i = 0; i < TE; ++i) wv[u][i] = ok ? wrow[i][k] : 0.0f;
+            for (int i = 0; i < TE; ++i) wv[u][i] = wrow[i][k];
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            if ((j0 + u) < steps) {
+        for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-                for (int b = 0; b < TB; ++b)
+            for (int b = 0; b < TB; ++b)
 #pragma unroll
-                    for (int i = 0; i < TE; ++i)
-                        acc[b][i] = __builtin_fmaf(xv[u][b], wv[u][i], acc[b][i]);
-            }
-        }
+                for (int i = 0; i < TE; ++i)
+                    acc[b][i] = __builtin_fmaf(xv[u][b], wv[u][i], acc[b][i]);
+    }
+    for (; j0 < steps; ++j0) {
+        const int k = j0 * 64;
+        float xv[TB], wv[TE];
+#pragma unroll
+        for (int b = 0; b < TB; ++b) xv[b] = load_x<BF16>(x, xoff[b] + k);
+#pragma unroll
+        for (int i = 0; i < TE; ++i) wv[i] = wrow[i][k];
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int i = 0; i < TE; ++i) acc[b][i] = __builtin_fmaf(xv[b], wv[i], acc[b][i]);
     }
     // Fixed tree: after step s, lanes i < s hold p[i] + p[i+s].
 #pragma unroll
@@ -101,68 +113,52 @@ __global__ __launch_bounds__(64) void router_logits_kernel(
     }
 }
 
-__device__ __forceinline__ bool ranks_before(float la, int a, float lb, int b) {
-    // b == INT_MAX marks "no candidate".
-    if (b == 0x7fffffff) return a != 0x7fffffff;
-    if (a == 0x7fffffff) return false;
-    return la > lb || (la == lb && a < b);
-}
-
-// One wave per token.  Each lane holds up to 16 logits (experts lane + 64i).
-__global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ logits,
-                                                  int n_tok, int n_experts, int k,
-                                                  int32_t *__restrict__ idx,
-                                                  float *__restrict__ w) {
+// Top-k by rank counting: the rank of expert e is the number of experts
+// whose key (logit desc, id asc) comes first; e is selected iff rank < k and
+// lands in slot `rank`.  Keys are distinct, so ranks are a permutation.  One
+// 1024-thread block per token: thread (part, e) counts over one slice of the
+// experts, then the parts are summed.  -0 and +0 compare equal.
+__global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ logits,
+                                                    int n_tok, int n_experts, int k,
+                                                    int32_t *__restrict__ idx,
+                                                    float *__restrict__ w) {
+    __shared__ float s_l[kMaxExperts];
+    __shared__ int s_rank[kMaxExperts];
+    __shared__ float s_sig[kMaxTopK];
     const int t = blockIdx.x;
-    const int lane = threadIdx.x;
-    constexpr int kPer = kMaxExperts / 64;
-    float v[kPer];
-    uint32_t avail = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = 0.0f;
-        if (e < n_experts) {
-            // + 0.0f maps -0 to +0; the compare below already treats them
-            // as equal, this keeps the stored key canonical.
-            v[i] = logits[static_cast<size_t>(t) * n_experts + e] + 0.0f;
-            avail |= 1u << i;
+    const int tid = threadIdx.x;
+    const int epad = (n_experts + 63) & ~63;
+    const int parts = 1024 / epad;           // >= 1 since n_experts <= 1024
+    const int span = (n_experts + parts - 1) / parts;
+    for (int e = tid; e < n_experts; e += 1024) {
+        s_l[e] = logits[static_cast<size_t>(t) * n_experts + e];
+        s_rank[e] = 0;
+    }
+    __syncthreads();
+    const int e = tid % epad, part = tid / epad;
+    if (e < n_experts && part < parts) {
+        const float v = s_l[e];
+        const int j0 = part * span, j1 = min(n_experts, j0 + span);
+        int r = 0;
+        for (int j = j0; j < j1; ++j) {
+            const float o = s_l[j];
+            r += (o > v || (o == v && j < e)) ? 1 : 0;
+        }
+        atomicAdd(&s_rank[e], r);
+    }
+    __syncthreads();
+    if (tid < n_experts) {
+        const int r = s_rank[tid];
+        if (r < k) {
+            idx[static_cast<size_t>(t) * k + r] = tid;
+            s_sig[r] = 1.0f / (1.0f + expf(-s_l[tid]));
         }
     }
-    int my_idx = 0;
-    float my_logit = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane + 64 * i;
-            if (((avail >> i) & 1u) && ranks_before(v[i], e, bv, bi)) {
-                bv = v[i];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (ranks_before(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
-        if (lane == j) {
-            my_idx = bi;
-            my_logit = bv;
-        }
-    }
-    const float sig = 1.0f / (1.0f + expf(-my_logit));
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum = sum + __shfl(sig, j, 64);
-    if (lane < k) {
-        idx[static_cast<size_t>(t) * k + lane] = my_idx;
-        w[static_cast<size_t>(t) * k + lane] = sig / sum;
+    __syncthreads();
+    if (tid < k) {
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum = sum + s_sig[j];
+        w[static_cast<size_t>(t) * k + tid] = s_sig[tid] / sum;
     }
 }
 
@@ -199,7 +195,7 @@ hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
 hipError_t launch_topk(const float *logits, int n_tok, int n_experts, int k,
                        int32_t *idx, float *w, hipStream_t s) {
     if (n_tok <= 0) return hipSuccess;
-    topk_kernel<<<n_tok, 64, 0, s>>>(logits, n_tok, n_experts, k, idx, w);
+    topk_kernel<<<n_tok, 1024, 0, s>>>(logits, n_tok, n_experts, k, idx, w);
     return hipGetLastError();
 }
 

@@ -8,60 +8,33 @@
 // (expert, token) -- a stable counting sort -- so each expert's tokens form
 // one contiguous run of rows for the expert FFNs.
 //
-// One 1024-thread block does the whole batch: an LDS histogram (integer
-// atomics, order-free), two block scans (offsets, compaction of the union),
-// then the gather in chunks of 1024 entries where each entry's rank among
+// One block (256 threads for up to 256 experts, else 1024) does the whole
+// batch: an LDS histogram (integer atomics, order-free), two block scans
+// (offsets, compaction of the union), then the gather in chunks of one entry
+// per thread, where each entry's rank among
 // equal experts comes from wave ballots (match-any over the id bits) plus
 // per-wave counts in LDS.  Everything is integer, so results are exact and
 // independent of scheduling.
-#include "internal.h"
+#include "dev_common.h"
 
 namespace coli {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
 
-// Exclusive scan of one int per thread over the block; *total gets the sum.
-// s_tmp needs kWaves + 1 ints.  Contains __syncthreads().
-__device__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    __syncthreads();
-    if (lane == 63) s_tmp[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-        int wv = lane < kWaves ? s_tmp[lane] : 0;
-        int inc = wv;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        if (lane < kWaves) s_tmp[lane] = inc - wv;
-        if (lane == kWaves - 1) s_tmp[kWaves] = inc;
-    }
-    __syncthreads();
-    const int excl = s_tmp[wave] + x - v;
-    *total = s_tmp[kWaves];
-    __syncthreads();
-    return excl;
-}
-
-__global__ __launch_bounds__(kThreads) void union_kernel(
+// NT threads handle up to NT experts.
+template <int NT>
+__global__ __launch_bounds__(NT) void union_kernel(
     const int32_t *__restrict__ idx, int n_ent, int n_experts,
     int32_t *__restrict__ n_union, int32_t *__restrict__ union_ids,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ gather, int32_t *__restrict__ err) {
-    __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_off[kMaxExperts];
-    __shared__ int s_base[kMaxExperts];
-    __shared__ unsigned short s_wc[kWaves][kMaxExperts];
+    constexpr int kThreads = NT;
+    constexpr int kWaves = NT / 64;
+    __shared__ int s_cnt[NT];
+    __shared__ int s_off[NT];
+    __shared__ int s_base[NT];
+    __shared__ unsigned short s_wc[kWaves][NT];
     __shared__ int s_tmp[kWaves + 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -85,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void union_kernel(
 
     const int c = tid < n_experts ? s_cnt[tid] : 0;
     int total = 0;
-    const int excl = block_exclusive_scan(c, s_tmp, &total);
+    const int excl = dev::block_exclusive_scan<NT>(c, s_tmp, &total);
     if (tid < n_experts) {
         counts[tid] = c;
         offsets[tid] = excl;
@@ -94,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void union_kernel(
     if (tid == 0) offsets[n_experts] = total;
     const int flag = (tid < n_experts && c > 0) ? 1 : 0;
     int nu = 0;
-    const int pos = block_exclusive_scan(flag, s_tmp, &nu);
+    const int pos = dev::block_exclusive_scan<NT>(flag, s_tmp, &nu);
     if (flag) union_ids[pos] = tid;
     if (tid == 0) *n_union = nu;
     __syncthreads();
@@ -138,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void union_kernel(
 __global__ __launch_bounds__(kThreads) void plan_kernel(FwdArgs a,
                                                         ChunkDesc *__restrict__ chunks,
                                                         int32_t *__restrict__ n_chunks) {
-    __shared__ int s_tmp[kWaves + 1];
+    __shared__ int s_tmp[kThreads / 64 + 1];
     const int tid = threadIdx.x;
     const int nu = *a.n_union;
     int e = 0, m = 0, row0 = 0;
@@ -153,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(FwdArgs a,
     }
     const int nch = (m + kChunkRows - 1) / kChunkRows;
     int total = 0;
-    const int first = block_exclusive_scan(nch, s_tmp, &total);
+    const int first = dev::block_exclusive_scan<kThreads>(nch, s_tmp, &total);
     for (int c = 0; c < nch; ++c) {
         ChunkDesc d;
         d.expert = e;
@@ -171,8 +144,12 @@ hipError_t launch_union(const int32_t *idx, int n_tok, int k, int n_experts,
                         int32_t *n_union, int32_t *union_ids, int32_t *counts,
                         int32_t *offsets, int32_t *gather, int32_t *err,
                         hipStream_t s) {
-    union_kernel<<<1, kThreads, 0, s>>>(idx, n_tok * k, n_experts, n_union,
-                                        union_ids, counts, offsets, gather, err);
+    if (n_experts <= 256)
+        union_kernel<256><<<1, 256, 0, s>>>(idx, n_tok * k, n_experts, n_union, union_ids,
+                                            counts, offsets, gather, err);
+    else
+        union_kernel<1024><<<1, 1024, 0, s>>>(idx, n_tok * k, n_experts, n_union, union_ids,
+                                              counts, offsets, gather, err);
     return hipGetLastError();
 }
 

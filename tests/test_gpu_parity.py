@@ -84,6 +84,47 @@ def test_decode_b1_parity(decode_b1, path):
     check_outputs(gpu["y"], oracle_y(data, ref, [0]), f"decode_b1/{path}")
 
 
+def test_decode_b1_fused_layer_call(decode_b1):
+    data, L = decode_b1
+    L.set_path(B.PATH_AUTO)
+    x = B.activations_to_device(data.x)
+    y, idx, w, u = L.layer(x)
+    torch.cuda.synchronize()
+    three = gpu_run(B, L, data, with_logits=False)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), three["y"].view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), three["idx"])
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), three["weight"].view(np.uint32))
+    ref = oracle_route(data)
+    check_outputs(y.cpu().numpy(), oracle_y(data, ref, [0]), "decode_b1/fused")
+
+
+@pytest.mark.parametrize("n_tok", [1, 2, 3, 4])
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_fused_layer_small_batches(n_tok, act):
+    spec = MEDIUM.with_(act=act)
+    data = Data(spec, n_tok=n_tok)
+    log(f"case fused layer {spec.name} n_tok={n_tok}")
+    L = make_layer(B, data, path=B.PATH_GEMV)
+    x = B.activations_to_device(data.x)
+    outs = []
+    for _ in range(2):      # twice: arrival counters must reset between calls
+        y, idx, w, u = L.layer(x)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    three = gpu_run(B, L, data, with_logits=False)
+    assert np.array_equal(outs[0].view(np.uint32), three["y"].view(np.uint32))
+    nu = int(u["n_union"].cpu()[0])
+    assert nu == three["n_union"]
+    np.testing.assert_array_equal(u["union_ids"].cpu().numpy()[:nu], three["union_ids"])
+    np.testing.assert_array_equal(u["gather"].cpu().numpy(), three["gather"])
+    np.testing.assert_array_equal(u["offsets"].cpu().numpy(), three["offsets"])
+    ref = oracle_route(data)
+    check_routing(three, ref, check_logits=False)
+    check_outputs(outs[0], oracle_y(data, ref, range(n_tok)), f"fused n_tok={n_tok}")
+    L.close()
+
+
 def test_decode_b1_deterministic(decode_b1):
     data, L = decode_b1
     L.set_path(B.PATH_AUTO)
