@@ -32,15 +32,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def fused_decode(spec):
+    """coli_moe_layer's small-batch path: the shared expert's gate/up runs in
+    the router launch, so the gate/up kernel streams the routed experts only."""
+    return spec.n_tok <= 2 and spec.n_experts <= 256
+
+
 def algorithmic_bytes(spec, n_union, n_tok):
     """Bytes one layer call must move at minimum: each union expert's blob
     once, the shared expert's blob, the router weight, activations in, output
-    out."""
+    out; and the share of them each expert kernel streams."""
     from int4_routed_expert_layer_amd import configs
     blob = configs.blob_bytes(spec.hidden, spec.inter)
     experts = n_union + (1 if spec.has_shared else 0)
     h, i = spec.hidden, spec.inter
-    gateup = experts * (2 * i * h // 2 + 2 * i * (h // 32) * 2)
+    gu_experts = n_union if (fused_decode(spec) and spec.has_shared) else experts
+    gateup = gu_experts * (2 * i * h // 2 + 2 * i * (h // 32) * 2)
     down = experts * (h * i // 2 + h * (i // 32) * 2)
     router = h * spec.n_experts * 4
     act = n_tok * h * spec.act_bytes + n_tok * h * 4
@@ -108,7 +115,10 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
                                     p(bf["gather"]), p(bf["y"]), st), L.handle)
         return bf
 
-    # 1) eager pass with per-kernel events (roofline of the dominant kernel)
+    # 1) eager pass with per-kernel events (roofline of the dominant kernel).
+    # A bounded GPU sleep is queued first so the host has enqueued every step
+    # before the GPU reaches them: kernels then run back to back and each
+    # event pair brackets its kernel without host gaps.
     for s in range(wl.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -118,6 +128,7 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
     unions = []
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * max(0.02, 1e-4 * wl.steps)))   # ~20+ ms of GPU clock cycles
     ev0.record()
     for s in range(wl.steps):
         bf = step(s)
@@ -169,6 +180,33 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
     return res
 
 
+KERNEL_SOURCES = ["int4_routed_expert_layer_amd/csrc/dev_gemv.h", "int4_routed_expert_layer_amd/csrc/gemv.hip",
+                  "int4_routed_expert_layer_amd/csrc/dev_common.h", "int4_routed_expert_layer_amd/csrc/internal.h"]
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up GEMV from the committed rocprofv3
+    counter runs (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
+    size), or None when the kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_gemv_gateup_decode_b1.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_sha():
+        return None
+    return t["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(spec, x, w, b, blobs, shared, seconds):
     from oracle import oracle as orc
     n = 0
@@ -199,6 +237,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy 4 times (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -218,6 +258,15 @@ def main():
     blobs = inputs.expert_blobs(spec1, 0, range(spec1.n_experts), threads=8)
     shared = inputs.expert_blob(spec1, 0, inputs.SHARED)
     w1, b1 = inputs.router_weight(spec1), inputs.router_bias(spec1)
+
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 4 x 256 MiB read + 256 MiB write")
+        del src, dst
 
     results = {}
     decode_layers = []
@@ -306,8 +355,10 @@ def main():
                    "layer_instances_rotated": args.instances, "hip_graph": not args.no_graph,
                    "all_experts_vram": True},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemv_gateup (gate+up+SwiGLU)",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if head_name == "decode_b1" else None,
+                     "kernel": "gemv_gateup_kernel (routed gate+up+SwiGLU)" if fused_decode(head_spec)
+                               else "gate/up expert kernel",
                      "bytes_per_launch": nb["gateup"], "avg_launch_us": kg * 1e3},
         "also": out_also,
     }

@@ -214,15 +214,16 @@ coli_status coli_layer_stream_stats(const coli_layer *layer,
 coli_status coli_layer_device_errors(coli_layer *layer, int32_t *flags);
 
 /* Kernel timing, for tracing and benchmarks.  While enabled, every kernel
- * the layer launches is bracketed by two HIP events on its launch stream and
- * its elapsed time is added to the total of its kind.  coli_layer_kernel_times
+ * the layer launches carries two HIP events that receive that kernel's own
+ * start and end timestamps (hipExtLaunchKernel), and its duration is added to
+ * the total of its kind; launch gaps between kernels are not counted.  coli_layer_kernel_times
  * synchronises the device, writes per-kind totals (host arrays of
  * COLI_KERNEL_KINDS entries, either may be NULL) and resets them. */
 typedef enum {
     COLI_K_ROUTER = 0,   /* router logits */
     COLI_K_TOPK = 1,     /* top-k and weights */
     COLI_K_UNION = 2,    /* batch union */
-    COLI_K_PLAN = 3,     /* grouped work list */
+    COLI_K_PLAN = 3,     /* grouped work list; fp16 activations (2 launches) */
     COLI_K_GATEUP = 4,   /* gate/up + SwiGLU (GEMV or grouped) */
     COLI_K_DOWN = 5,     /* down projection x routing weight */
     COLI_K_COMBINE = 6,  /* per-token sum of expert rows */

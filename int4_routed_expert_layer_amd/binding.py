@@ -60,6 +60,11 @@ class ColiError(RuntimeError):
 
 
 def _load():
+    # torch carries its own HIP runtime under the soname libamdhip64.so.7.
+    # Importing it first makes the library bind to that same copy, so the
+    # process holds one HIP runtime: a second runtime loaded beside it finds
+    # no device once torch's has claimed the GPU.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: the HIP library must be built "

@@ -166,6 +166,7 @@ struct coli_layer {
 
     float *logits = nullptr;    // [max_tokens x E]
     _Float16 *h = nullptr;      // [(max_tokens*k + max_tokens) x I]
+    _Float16 *xh = nullptr;     // [max_tokens x H]
     float *ys = nullptr;        // [(max_tokens*k + max_tokens) x H]
     ChunkDesc *chunks = nullptr;
     int32_t *n_chunks = nullptr;
@@ -221,6 +222,15 @@ coli_status hip_fail(coli_layer *L, hipError_t e, const char *what) {
         if (e_ != hipSuccess) return hip_fail(L, e_, what); \
     } while (0)
 
+}  // namespace
+
+LaunchTiming &coli::launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+
+namespace {
+
 hipEvent_t take_event(coli_layer *L) {
     if (!L->ev_pool.empty()) {
         hipEvent_t e = L->ev_pool.back();
@@ -232,23 +242,33 @@ hipEvent_t take_event(coli_layer *L) {
     return e;
 }
 
-// Brackets one kernel launch with events when timing is enabled.
+// Times the one kernel launched while it is alive: when timing is enabled it
+// arms the thread's launch slot with two events, which the launch fills with
+// the kernel's own start and end timestamps.
 struct KernelMark {
     coli_layer *L;
     int kind;
-    hipStream_t s;
-    hipEvent_t a = nullptr;
-    KernelMark(coli_layer *L_, int kind_, hipStream_t s_) : L(L_), kind(kind_), s(s_) {
-        if (L->timing && (a = take_event(L)) != nullptr) (void)hipEventRecord(a, s);
+    hipEvent_t a = nullptr, b = nullptr;
+    KernelMark(coli_layer *L_, int kind_, hipStream_t) : L(L_), kind(kind_) {
+        if (!L->timing) return;
+        a = take_event(L);
+        b = a ? take_event(L) : nullptr;
+        if (!b) {
+            if (a) L->ev_pool.push_back(a);
+            a = nullptr;
+            return;
+        }
+        launch_timing() = {a, b};
     }
     ~KernelMark() {
         if (!a) return;
-        hipEvent_t b = take_event(L);
-        if (b && hipEventRecord(b, s) == hipSuccess) {
-            L->marks.push_back({kind, a, b});
+        LaunchTiming &t = launch_timing();
+        if (t.start == nullptr) {
+            L->marks.push_back({kind, a, b});  // the launch used the events
         } else {
+            t = {};
             L->ev_pool.push_back(a);
-            if (b) L->ev_pool.push_back(b);
+            L->ev_pool.push_back(b);
         }
     }
 };
@@ -322,6 +342,7 @@ FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, 
     a.has_shared = L->d.has_shared;
     a.lay = L->lay;
     a.h = L->h;
+    a.xh = L->xh;
     a.ys = L->ys;
     a.y = y;
     a.chunks = L->chunks;
@@ -369,7 +390,7 @@ void free_layer(coli_layer *L) {
     for (auto p : L->pin_tables) (void)hipHostFree(const_cast<uint8_t **>(p));
     for (auto p : L->dev_tables) (void)hipFree(const_cast<uint8_t **>(p));
     if (L->side) (void)hipStreamDestroy(L->side);
-    void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->ys, L->chunks, L->n_chunks, L->err,
+    void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->xh, L->ys, L->chunks, L->n_chunks, L->err,
                     L->sync_counters};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -473,6 +494,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->table_dev), sizeof(void *) * (E + 1), "expert table"},
         {reinterpret_cast<void **>(&L->logits), sizeof(float) * T * E, "logits scratch"},
         {reinterpret_cast<void **>(&L->h), sizeof(_Float16) * rows * I, "hidden scratch"},
+        {reinterpret_cast<void **>(&L->xh), sizeof(_Float16) * T * H, "fp16 activation scratch"},
         {reinterpret_cast<void **>(&L->ys), sizeof(float) * rows * H, "per-entry output scratch"},
         {reinterpret_cast<void **>(&L->chunks), sizeof(ChunkDesc) * L->max_chunks, "work list"},
         {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
@@ -670,8 +692,12 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
     }
 
     if (path == COLI_PATH_GROUPED) {
+        {
+            KernelMark m(L, COLI_K_PLAN, s);
+            HIP_TRY(L, launch_plan(a, L->chunks, L->n_chunks, s), "plan launch");
+        }
         KernelMark m(L, COLI_K_PLAN, s);
-        HIP_TRY(L, launch_plan(a, L->chunks, L->n_chunks, s), "plan launch");
+        HIP_TRY(L, launch_to_half(a, s), "fp16 activation launch");
     }
     // Resident experts (the table holds NULL for pinned-host experts).
     if ((st = launch_experts(L, a, path, s)) != COLI_OK) return st;

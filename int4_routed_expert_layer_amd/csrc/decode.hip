@@ -164,9 +164,9 @@ hipError_t launch_t(const FwdArgs &a, const FrontArgs &f, size_t lds, hipStream_
     const int router_blocks = (a.n_experts + 3) / 4;
     const int grid = router_blocks + (a.has_shared ? a.inter / kPanel : 0);
     if (a.act_bf16)
-        decode_front_kernel<NT, true><<<grid, kFrontThreads, lds, s>>>(a, f, router_blocks);
+        launch(decode_front_kernel<NT, true>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     else
-        decode_front_kernel<NT, false><<<grid, kFrontThreads, lds, s>>>(a, f, router_blocks);
+        launch(decode_front_kernel<NT, false>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     return hipGetLastError();
 }
 

@@ -8,6 +8,28 @@ namespace dev {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
+// Load through a global-address-space pointer.  Expert weights are reached
+// through pointers read from the device expert table, which the compiler
+// cannot prove to be global; plain dereferences would become flat loads,
+// which also count against the LDS wait counter and serialise LDS traffic
+// behind the weight stream.
+template <typename T>
+__device__ __forceinline__ T gload(const void *p) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    if constexpr (sizeof(T) == 16) {
+        const v4u v = *(const __attribute__((address_space(1))) v4u *)(p);
+        return __builtin_bit_cast(T, v);
+    } else if constexpr (sizeof(T) == 8) {
+        const v2u v = *(const __attribute__((address_space(1))) v2u *)(p);
+        return __builtin_bit_cast(T, v);
+    } else {
+        static_assert(sizeof(T) == 4, "gload: 4, 8 or 16 bytes");
+        const uint32_t v = *(const __attribute__((address_space(1))) uint32_t *)(p);
+        return __builtin_bit_cast(T, v);
+    }
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }

@@ -95,10 +95,10 @@ __device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpPtrs &P, i
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
         const int c = min(first + step * g, C - 1);
-        b.gw[g] = *reinterpret_cast<const uint4 *>(P.gq + static_cast<size_t>(c) * kChunkBytes);
-        b.uw[g] = *reinterpret_cast<const uint4 *>(P.uq + static_cast<size_t>(c) * kChunkBytes);
-        b.gs[g] = *reinterpret_cast<const uint2 *>(P.gs + static_cast<size_t>(c) * kScaleChunkBytes);
-        b.us[g] = *reinterpret_cast<const uint2 *>(P.us + static_cast<size_t>(c) * kScaleChunkBytes);
+        b.gw[g] = gload<uint4>(P.gq + static_cast<size_t>(c) * kChunkBytes);
+        b.uw[g] = gload<uint4>(P.uq + static_cast<size_t>(c) * kChunkBytes);
+        b.gs[g] = gload<uint2>(P.gs + static_cast<size_t>(c) * kScaleChunkBytes);
+        b.us[g] = gload<uint2>(P.us + static_cast<size_t>(c) * kScaleChunkBytes);
     }
 }
 
@@ -170,8 +170,7 @@ __device__ void gateup_panel(const FwdArgs &a, const uint8_t *blob, int r0, int 
             const int t = token_of_row(a, r0 + mb + m);
             float v[8];
             if (a.act_bf16) {
-                const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * H + 8 * q);
+                const uint4 raw = gload<uint4>(static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * H + 8 * q);
                 const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -179,9 +178,8 @@ __device__ void gateup_panel(const FwdArgs &a, const uint8_t *blob, int r0, int 
                     v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
                 }
             } else {
-                const float4 *src = reinterpret_cast<const float4 *>(
-                    static_cast<const float *>(a.x) + static_cast<size_t>(t) * H + 8 * q);
-                const float4 lo = src[0], hi = src[1];
+                const float *src = static_cast<const float *>(a.x) + static_cast<size_t>(t) * H + 8 * q;
+                const float4 lo = gload<float4>(src), hi = gload<float4>(src + 4);
                 v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
                 v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
             }
@@ -237,8 +235,8 @@ __device__ __forceinline__ void down_load(DownBuf &b, const uint8_t *dq, const u
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
         const int c = min(first + g, C - 1);
-        b.w[g] = *reinterpret_cast<const uint4 *>(dq + static_cast<size_t>(c) * kChunkBytes);
-        b.s[g] = *reinterpret_cast<const uint2 *>(ds + static_cast<size_t>(c) * kScaleChunkBytes);
+        b.w[g] = gload<uint4>(dq + static_cast<size_t>(c) * kChunkBytes);
+        b.s[g] = gload<uint2>(ds + static_cast<size_t>(c) * kScaleChunkBytes);
     }
 }
 
@@ -301,7 +299,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const uint8_t *blob, int r0, i
         __syncthreads();
         for (int i = tid; i < mc * (I / 8); i += 256) {
             const int m = i / (I / 8), q = i % (I / 8);
-            const uint4 raw = *reinterpret_cast<const uint4 *>(a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q);
+            const uint4 raw = gload<uint4>(a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q);
             const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
             float v[8];
 #pragma unroll

@@ -55,9 +55,9 @@ hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, i
     const int units = u_count >= 0 ? u_count : units_bound(a) - u_begin;
     if (units <= 0) return hipSuccess;
     const int grid = units * (a.inter / kPanel);
-    if (maxm == 4) gemv_gateup_kernel<4><<<grid, 256, lds, s>>>(a, u_begin);
-    else if (maxm == 2) gemv_gateup_kernel<2><<<grid, 256, lds, s>>>(a, u_begin);
-    else gemv_gateup_kernel<1><<<grid, 256, lds, s>>>(a, u_begin);
+    if (maxm == 4) launch(gemv_gateup_kernel<4>, grid, 256, lds, s, a, u_begin);
+    else if (maxm == 2) launch(gemv_gateup_kernel<2>, grid, 256, lds, s, a, u_begin);
+    else launch(gemv_gateup_kernel<1>, grid, 256, lds, s, a, u_begin);
     return hipGetLastError();
 }
 
@@ -68,13 +68,13 @@ hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s, int
     if (lds > max_lds) return hipErrorInvalidValue;
     const int grid = units_bound(a) * (a.hidden / (2 * kPanel));
     if (combine_counters) {
-        if (maxm == 4) gemv_down_kernel<4, true><<<grid, 256, lds, s>>>(a, combine_counters);
-        else if (maxm == 2) gemv_down_kernel<2, true><<<grid, 256, lds, s>>>(a, combine_counters);
-        else gemv_down_kernel<1, true><<<grid, 256, lds, s>>>(a, combine_counters);
+        if (maxm == 4) launch(gemv_down_kernel<4, true>, grid, 256, lds, s, a, combine_counters);
+        else if (maxm == 2) launch(gemv_down_kernel<2, true>, grid, 256, lds, s, a, combine_counters);
+        else launch(gemv_down_kernel<1, true>, grid, 256, lds, s, a, combine_counters);
     } else {
-        if (maxm == 4) gemv_down_kernel<4, false><<<grid, 256, lds, s>>>(a, nullptr);
-        else if (maxm == 2) gemv_down_kernel<2, false><<<grid, 256, lds, s>>>(a, nullptr);
-        else gemv_down_kernel<1, false><<<grid, 256, lds, s>>>(a, nullptr);
+        if (maxm == 4) launch(gemv_down_kernel<4, false>, grid, 256, lds, s, a, nullptr);
+        else if (maxm == 2) launch(gemv_down_kernel<2, false>, grid, 256, lds, s, a, nullptr);
+        else launch(gemv_down_kernel<1, false>, grid, 256, lds, s, a, nullptr);
     }
     return hipGetLastError();
 }

@@ -7,15 +7,17 @@
 // with N-blocks; a persistent grid walks that list (consecutive items, which
 // share the same activation rows, land on the same XCD and its L2).
 //
-// Per item a 256-thread workgroup stages the chunk's activation rows for 128
-// reduction columns at a time into LDS as fp16 (XOR-swizzled 16-byte units,
-// conflict-free for the fragment reads), while each wave streams its own
-// int4 weight panels straight from HBM: one 16-byte load per lane per 1 KB
-// chunk, already in B-fragment order of v_mfma_f32_16x16x32_f16.  Each
+// Per item a 256-thread workgroup copies the chunk's fp16 activation rows for
+// 128 reduction columns at a time straight from global memory into LDS
+// (global_load_lds, double-buffered: the next 128 columns are in flight while
+// the current ones are multiplied; XOR-swizzled 16-byte units, conflict-free
+// for the fragment reads), while each wave streams its own int4 weight
+// panels from HBM (prefetched one step ahead): one 16-byte load per lane per
+// 1 KB chunk, already in B-fragment order of v_mfma_f32_16x16x32_f16.  Each
 // dword is turned into eight fp16 weights in registers: q = (1024 + u) -
 // 1032 (exact) times the group's fp16 scale (one rounding), so a fragment
 // covers exactly one 32-wide scale group and the MFMA accumulates in fp32.
-//   gate/up: A = gathered token rows (bf16 or fp32 -> fp16); each wave owns
+//   gate/up: A = gathered token rows (fp16 copy of x); each wave owns
 //            32 intermediate rows of both gate and up, so SwiGLU is applied
 //            in registers and h is stored as fp16.
 //   down:    A = h rows of the chunk; each wave owns 64 output columns; the
@@ -23,11 +25,12 @@
 //            shared expert) and writes the entry's fp32 output row.
 // The combine then sums, per token, its k routed rows in slot order and the
 // shared row.  All sums have a fixed order: results are deterministic.
-#include "internal.h"
+#include "dev_common.h"
 
 namespace coli {
 namespace {
 
+using dev::gload;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -38,18 +41,30 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
 
+// Keeps a constant in a VGPR so the compiler can use three-operand
+// v_and_or_b32 (VOP3 cannot encode literals on this ISA).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+    asm volatile("" : "+v"(c));
+    return c;
+}
+
 // Eight fp16 weights (columns k0..k0+7) of one packed dword times scale.
-__device__ __forceinline__ half8 dequant8(uint32_t w, half2v scale) {
+// Column pairs (0,1) and (4,5) come out as 1024 + u, pairs (2,3) and (6,7)
+// as 1024 + 16 u (no shift needed); both are turned into the exact integer
+// q = u - 8 and then multiplied by the fp16 group scale (one rounding).
+__device__ __forceinline__ half8 dequant8(uint32_t w, half2v scale, uint32_t M0, uint32_t M1, uint32_t G) {
     const half2v k1032 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    half2v p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t bits = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        p[j] = (__builtin_bit_cast(half2v, bits) - k1032) * scale;
-    }
+    const half2v k16th = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+    const half2v km72 = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+    const uint32_t w8 = w >> 8;
+    const half2v p0 = __builtin_bit_cast(half2v, (w & M0) | G) - k1032;
+    const half2v p1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, (w & M1) | G), k16th, km72);
+    const half2v p2 = __builtin_bit_cast(half2v, (w8 & M0) | G) - k1032;
+    const half2v p3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, (w8 & M1) | G), k16th, km72);
+    const half2v q0 = p0 * scale, q1 = p1 * scale, q2 = p2 * scale, q3 = p3 * scale;
     half8 r;
-    r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
-    r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
+    r[0] = q0[0]; r[1] = q0[1]; r[2] = q1[0]; r[3] = q1[1];
+    r[4] = q2[0]; r[5] = q2[1]; r[6] = q3[0]; r[7] = q3[1];
     return r;
 }
 
@@ -64,9 +79,22 @@ __device__ __forceinline__ int lds_unit(int m, int q) {
     return m * kRowBytes + ((q ^ (m & 15)) << 4);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at
+// lds_base + 16 L (lds_base must be wave-uniform).
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint8_t *lds_base) {
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(src),
+                                     (void __attribute__((address_space(3))) *)(lds_base), 16, 0, 0);
+}
+
+struct BFrag {
+    uint4 q[4];
+    uint2 s[4];
+};
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
-    __shared__ __align__(16) uint8_t s_a[kChunkRows * kRowBytes];
+    // Two A tiles (double buffer): kChunkRows rows x 128 fp16 each.
+    __shared__ __align__(16) uint8_t s_a[2][kChunkRows * kRowBytes];
     __shared__ int s_tok[kChunkRows];
     const int H = a.hidden, I = a.inter;
     const int K = GATEUP ? H : I;
@@ -76,6 +104,8 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     const int l15 = lane & 15, l4 = lane >> 4;
     const int n_items = *a.n_chunks * NB;
     const int routed = a.n_tok * a.k;
+    const _Float16 *asrc = GATEUP ? a.xh : a.h;     // fp16 rows
+    const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
 
     // Consecutive virtual block ids on the same XCD (blocks go round-robin
     // over 8 XCDs).
@@ -116,13 +146,46 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
             soff[b] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * C * kScaleChunkBytes);
         }
 
-        __syncthreads();
-        if (GATEUP) {
-            for (int m = tid; m < nf * 16; m += 256) {
-                const int r = d.row0 + m;
-                s_tok[m] = m < rows ? (r < routed ? a.gather[r] / a.k : r - routed) : -1;
-            }
+        __syncthreads();   // previous item is done with s_tok and the A tiles
+        for (int m = tid; m < kChunkRows; m += 256) {
+            // Rows past `rows` repeat row 0: their results are discarded.
+            const int mm = m < rows ? m : 0;
+            const int r = d.row0 + mm;
+            s_tok[m] = GATEUP ? (r < routed ? a.gather[r] / a.k : r - routed) : r;
         }
+        __syncthreads();
+        // This wave stages 16-row groups wave, wave+4 of the first nf*16 rows
+        // (nf <= 8): one copy16 per 4 rows, swizzled on the source side so
+        // that lane L fills slot (L & 15) of row (L >> 4).  Source offsets
+        // (in fp16 elements, column 0) are fixed for the item.
+        const int my_groups = nf > wave ? (nf - wave + 3) / 4 : 0;
+        uint32_t src_off[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = (wave + 4 * g) * 16 + i * 4 + l4;
+                const int q = l15 ^ (m & 15);
+                src_off[g][i] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
+            }
+        auto stage = [&](int c, int buf) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                if (g < my_groups) {
+                    const int grp = wave + 4 * g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        copy16_to_lds(asrc + src_off[g][i] + c * kChunkK, &s_a[buf][(grp * 16 + i * 4) * kRowBytes]);
+                }
+            }
+        };
+        auto load_b = [&](int c, BFrag &f) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                f.q[b] = gload<uint4>(qbase + qoff[b] + c * kChunkBytes);
+                f.s[b] = gload<uint2>(sbase + soff[b] + c * kScaleChunkBytes);
+            }
+        };
 
         floatx4 acc[kMaxFrags][4];
 #pragma unroll
@@ -130,66 +193,37 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[f][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
+        // LDS byte offset of this lane's A fragment for k-step s (frag f adds
+        // f * 16 rows).
+        uint32_t a_off[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) a_off[st] = lds_unit(l15, 4 * st + l4);
+        const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+
+        BFrag bn, bc;
+        stage(0, 0);
+        load_b(0, bn);
         for (int c = 0; c < C; ++c) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            // Stage rows x 128 columns of A as fp16.
-            for (int i = tid; i < nf * 16 * 16; i += 256) {
-                const int m = i >> 4, q = i & 15;
-                half8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (m < rows) {
-                    const size_t col = static_cast<size_t>(c) * kChunkK + 8 * q;
-                    if (GATEUP) {
-                        const size_t off = static_cast<size_t>(s_tok[m]) * H + col;
-                        if (a.act_bf16) {
-                            const uint4 raw = *reinterpret_cast<const uint4 *>(
-                                static_cast<const uint16_t *>(a.x) + off);
-                            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                v[2 * j] = static_cast<_Float16>(bf16_bits_to_f32(w4[j] & 0xFFFFu));
-                                v[2 * j + 1] = static_cast<_Float16>(bf16_bits_to_f32(w4[j] >> 16));
-                            }
-                        } else {
-                            const float4 *src = reinterpret_cast<const float4 *>(
-                                static_cast<const float *>(a.x) + off);
-                            const float4 lo = src[0], hi = src[1];
-                            v[0] = static_cast<_Float16>(lo.x); v[1] = static_cast<_Float16>(lo.y);
-                            v[2] = static_cast<_Float16>(lo.z); v[3] = static_cast<_Float16>(lo.w);
-                            v[4] = static_cast<_Float16>(hi.x); v[5] = static_cast<_Float16>(hi.y);
-                            v[6] = static_cast<_Float16>(hi.z); v[7] = static_cast<_Float16>(hi.w);
-                        }
-                    } else {
-                        v = *reinterpret_cast<const half8 *>(a.h + static_cast<size_t>(d.row0 + m) * I + col);
-                    }
-                }
-                *reinterpret_cast<half8 *>(s_a + lds_unit(m, q)) = v;
+            bc = bn;
+            if (c + 1 < C) {
+                stage(c + 1, (c + 1) & 1);
+                load_b(c + 1, bn);
             }
-            uint4 wq[4];
-            uint2 ws[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if (bvalid[b]) {
-                    wq[b] = *reinterpret_cast<const uint4 *>(qbase + qoff[b] + c * kChunkBytes);
-                    ws[b] = *reinterpret_cast<const uint2 *>(sbase + soff[b] + c * kScaleChunkBytes);
-                } else {
-                    wq[b] = uint4{0, 0, 0, 0};
-                    ws[b] = uint2{0, 0};
-                }
-            }
-            __syncthreads();
+            const uint8_t *tile = s_a[c & 1];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 half8 bf[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const uint32_t w = (s == 0) ? wq[b].x : (s == 1) ? wq[b].y : (s == 2) ? wq[b].z : wq[b].w;
-                    bf[b] = dequant8(w, scale_pair(ws[b], s));
+                    const uint32_t w = (s == 0) ? bc.q[b].x : (s == 1) ? bc.q[b].y : (s == 2) ? bc.q[b].z : bc.q[b].w;
+                    bf[b] = dequant8(w, scale_pair(bc.s[b], s), M0, M1, G);
                 }
 #pragma unroll
                 for (int f = 0; f < kMaxFrags; ++f) {
                     if (f < nf) {
-                        const half8 av = *reinterpret_cast<const half8 *>(
-                            s_a + lds_unit(16 * f + l15, 4 * s + l4));
+                        const half8 av = *reinterpret_cast<const half8 *>(tile + a_off[s] + f * 16 * kRowBytes);
 #pragma unroll
                         for (int b = 0; b < 4; ++b)
                             acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bf[b], acc[f][b], 0, 0, 0);
@@ -233,6 +267,31 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     }
 }
 
+// fp16 copy of the activations (the A operand of the gate/up GEMM).
+__global__ __launch_bounds__(256) void to_half_kernel(const void *x, int act_bf16, size_t n8, _Float16 *xh) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n8) return;
+    float v[8];
+    if (act_bf16) {
+        const uint4 raw = reinterpret_cast<const uint4 *>(x)[i];
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_bits_to_f32(w4[j] & 0xFFFFu);
+            v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
+        }
+    } else {
+        const float4 lo = reinterpret_cast<const float4 *>(x)[2 * i];
+        const float4 hi = reinterpret_cast<const float4 *>(x)[2 * i + 1];
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    }
+    half8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = static_cast<_Float16>(v[j]);
+    reinterpret_cast<half8 *>(xh)[i] = h;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a) {
     const int H4 = a.hidden / 4;
     const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -260,22 +319,29 @@ int grid_for(int items, int n_cu) {
 
 }  // namespace
 
+hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
+    const size_t n8 = static_cast<size_t>(a.n_tok) * a.hidden / 8;
+    if (n8 == 0) return hipSuccess;
+    launch(to_half_kernel, static_cast<unsigned>((n8 + 255) / 256), 256, 0, s, a.x, a.act_bf16, n8, a.xh);
+    return hipGetLastError();
+}
+
 hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
     const int grid = grid_for(max_chunks * (a.inter / 128), n_cu);
-    grouped_kernel<true><<<grid, 256, 0, s>>>(a);
+    launch(grouped_kernel<true>, grid, 256, 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
     const int grid = grid_for(max_chunks * ((a.hidden + 255) / 256), n_cu);
-    grouped_kernel<false><<<grid, 256, 0, s>>>(a);
+    launch(grouped_kernel<false>, grid, 256, 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s) {
     const size_t n = static_cast<size_t>(a.n_tok) * (a.hidden / 4);
     if (n == 0) return hipSuccess;
-    combine_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(a);
+    launch(combine_kernel, static_cast<unsigned>((n + 255) / 256), 256, 0, s, a);
     return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -65,12 +66,35 @@ struct FwdArgs {
     int n_tok, k, hidden, inter, n_experts, has_shared;
     BlobLayout lay;
     _Float16 *h;                    // [(n_tok*k + n_tok) x I]
+    _Float16 *xh;                   // [n_tok x H] fp16 copy of x (grouped path)
     float *ys;                      // [(n_tok*k + n_tok) x H]
     float *y;                       // [n_tok x H]
     const ChunkDesc *chunks;        // grouped path work list
     const int32_t *n_chunks;
     int skip_shared;                // gate/up: the shared unit was already done
 };
+
+// Kernel launch used by every launcher.  When the calling thread has armed
+// a pair of events (timing mode), the next launch records the kernel's own
+// start and end timestamps into them (hipExtLaunchKernel); otherwise it is a
+// plain launch.  The slot is thread-local and disarmed by that launch.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTiming &launch_timing();
+
+template <typename... P, typename... A>
+void launch(void (*kern)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s, A... args) {
+    LaunchTiming &t = launch_timing();
+    if (t.start) {
+        hipEvent_t a = t.start, b = t.stop;
+        t.start = t.stop = nullptr;
+        hipExtLaunchKernelGGL(kern, grid, block, lds, s, a, b, 0u, static_cast<P>(args)...);
+    } else {
+        kern<<<grid, block, lds, s>>>(static_cast<P>(args)...);
+    }
+}
 
 // route.hip
 hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
@@ -111,6 +135,7 @@ hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu,
 hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu,
                                hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
+hipError_t launch_to_half(const FwdArgs &a, hipStream_t s);
 
 // Upper bound on grouped work chunks for n_tok tokens.
 int max_work_chunks(int n_tok, int k, int n_experts, int has_shared);

@@ -168,10 +168,10 @@ hipError_t launch_logits_t(const void *x, int act_bf16, const float *wt,
                            int n_experts, float *logits, hipStream_t s) {
     const int tiles = ((n_tok + TB - 1) / TB) * ((n_experts + TE - 1) / TE);
     if (act_bf16)
-        router_logits_kernel<TB, TE, true, UNROLL><<<tiles, 64, 0, s>>>(
+        launch(router_logits_kernel<TB, TE, true, UNROLL>, tiles, 64, 0, s,
             x, wt, bias, n_tok, hidden, n_experts, logits);
     else
-        router_logits_kernel<TB, TE, false, UNROLL><<<tiles, 64, 0, s>>>(
+        launch(router_logits_kernel<TB, TE, false, UNROLL>, tiles, 64, 0, s,
             x, wt, bias, n_tok, hidden, n_experts, logits);
     return hipGetLastError();
 }
@@ -195,7 +195,7 @@ hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
 hipError_t launch_topk(const float *logits, int n_tok, int n_experts, int k,
                        int32_t *idx, float *w, hipStream_t s) {
     if (n_tok <= 0) return hipSuccess;
-    topk_kernel<<<n_tok, 1024, 0, s>>>(logits, n_tok, n_experts, k, idx, w);
+    launch(topk_kernel, n_tok, 1024, 0, s, logits, n_tok, n_experts, k, idx, w);
     return hipGetLastError();
 }
 

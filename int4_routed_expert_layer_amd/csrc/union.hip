@@ -145,17 +145,17 @@ hipError_t launch_union(const int32_t *idx, int n_tok, int k, int n_experts,
                         int32_t *offsets, int32_t *gather, int32_t *err,
                         hipStream_t s) {
     if (n_experts <= 256)
-        union_kernel<256><<<1, 256, 0, s>>>(idx, n_tok * k, n_experts, n_union, union_ids,
+        launch(union_kernel<256>, 1, 256, 0, s, idx, n_tok * k, n_experts, n_union, union_ids,
                                             counts, offsets, gather, err);
     else
-        union_kernel<1024><<<1, 1024, 0, s>>>(idx, n_tok * k, n_experts, n_union, union_ids,
+        launch(union_kernel<1024>, 1, 1024, 0, s, idx, n_tok * k, n_experts, n_union, union_ids,
                                               counts, offsets, gather, err);
     return hipGetLastError();
 }
 
 hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
                        hipStream_t s) {
-    plan_kernel<<<1, kThreads, 0, s>>>(a, chunks, n_chunks);
+    launch(plan_kernel, 1, kThreads, 0, s, a, chunks, n_chunks);
     return hipGetLastError();
 }
 
