@@ -194,7 +194,8 @@ coli_status coli_moe_forward(coli_layer *layer, const void *x, int32_t n_tok,
  * strategy) it runs as three launches: router + top-k + union together with
  * the shared expert's gate/up, then the routed gate/up, then the down
  * projection which also combines; the results are bit-identical to the
- * three separate calls.  Otherwise it issues the three calls. */
+ * three separate calls.  Otherwise it issues the three calls.  Calls on one
+ * layer must not overlap in time (they share the layer's arrival counters). */
 coli_status coli_moe_layer(coli_layer *layer, const void *x, int32_t n_tok,
                            int32_t *topk_idx, float *topk_w, int32_t *n_union,
                            int32_t *union_ids, int32_t *counts,

@@ -30,6 +30,40 @@ __device__ __forceinline__ T gload(const void *p) {
     }
 }
 
+// Buffer loads: base and size in a resource descriptor (scalar registers),
+// the per-lane offset in one vector register and the wave-uniform part of the
+// offset in a scalar register, so a stream of loads needs no per-load vector
+// address arithmetic.  Reads past `bytes` return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(T) == 16) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                                           static_cast<int>(soff), 0));
+    } else if constexpr (sizeof(T) == 8) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff),
+                                                                          static_cast<int>(soff), 0));
+    } else {
+        static_assert(sizeof(T) == 4, "bload: 4, 8 or 16 bytes");
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff),
+                                                                          static_cast<int>(soff), 0));
+    }
+}
+
+// Wave index as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
+
+// Thread index the optimiser cannot hoist computations of out of a
+// persistent loop (keeps per-item address math from holding registers).
+__device__ __forceinline__ int opaque_tid() {
+    int t = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
@@ -124,6 +158,24 @@ __device__ __forceinline__ void store_coherent(float *p, float v) {
 }
 __device__ __forceinline__ float load_coherent(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent(const int32_t *p) {
+    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(_Float16 *p, _Float16 v) {
+    __hip_atomic_store(reinterpret_cast<uint16_t *>(p), __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes as two coherent 8-byte loads.
+__device__ __forceinline__ uint4 load_coherent_16B(const void *p) {
+    uint64_t *q = const_cast<uint64_t *>(static_cast<const uint64_t *>(p));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4(static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32), static_cast<uint32_t>(hi),
+                      static_cast<uint32_t>(hi >> 32));
 }
 
 // Returns true in exactly one workgroup: the last of `expected` workgroups

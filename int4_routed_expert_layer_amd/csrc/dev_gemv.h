@@ -86,19 +86,22 @@ struct GateUpBuf {
     uint2 gs[kPipeGroup], us[kPipeGroup];
 };
 
-struct GateUpPtrs {
-    const uint8_t *gq, *uq, *gs, *us;
+// Sources of one gate/up panel: the blob descriptor, the lane offsets of a
+// weight chunk and of its scales, and the panel's section offsets.
+struct GateUpSrc {
+    rsrc_t r;
+    uint32_t vq, vs;          // per lane
+    uint32_t gq, uq, gs, us;  // uniform
 };
 
-__device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpPtrs &P, int first, int step,
-                                            int C) {
+__device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpSrc &S, int first, int step, int C) {
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
-        const int c = min(first + step * g, C - 1);
-        b.gw[g] = gload<uint4>(P.gq + static_cast<size_t>(c) * kChunkBytes);
-        b.uw[g] = gload<uint4>(P.uq + static_cast<size_t>(c) * kChunkBytes);
-        b.gs[g] = gload<uint2>(P.gs + static_cast<size_t>(c) * kScaleChunkBytes);
-        b.us[g] = gload<uint2>(P.us + static_cast<size_t>(c) * kScaleChunkBytes);
+        const uint32_t c = static_cast<uint32_t>(min(first + step * g, C - 1));
+        b.gw[g] = bload<uint4>(S.r, S.vq, S.gq + c * kChunkBytes);
+        b.uw[g] = bload<uint4>(S.r, S.vq, S.uq + c * kChunkBytes);
+        b.gs[g] = bload<uint2>(S.r, S.vs, S.gs + c * kScaleChunkBytes);
+        b.us[g] = bload<uint2>(S.r, S.vs, S.us + c * kScaleChunkBytes);
     }
 }
 
@@ -134,19 +137,25 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf &b, const uint8_t *x
 }
 
 // One gate/up work item: rows 16p..16p+15 of expert blob `blob`, for the M
-// tokens of hidden-buffer rows r0..r0+M-1.  Writes h rows (fp16).  All 256
-// threads must call it (it synchronises the workgroup).
-template <int MAXM>
-__device__ void gateup_panel(const FwdArgs &a, const uint8_t *blob, int r0, int M, int p, uint8_t *lds) {
+// tokens of hidden-buffer rows r0..r0+M-1 (rows.token(row) names the token of
+// a row).  Writes h rows (fp16; device-coherent stores when COHERENT, for a
+// consumer in the same launch).  All 256 threads must call it (it
+// synchronises the workgroup).
+template <int MAXM, bool COHERENT = false, class Rows>
+__device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int p,
+                             uint8_t *lds) {
     const int H = a.hidden, I = a.inter;
     const int C = H / kChunkK;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
     const int row = lane & 15, kq = lane >> 4;
-    GateUpPtrs P;
-    P.gq = blob + a.lay.gate_q + static_cast<size_t>(p) * C * kChunkBytes + lane * 16;
-    P.uq = blob + a.lay.up_q + static_cast<size_t>(p) * C * kChunkBytes + lane * 16;
-    P.gs = blob + a.lay.gate_s + static_cast<size_t>(p) * C * kScaleChunkBytes + row * 8;
-    P.us = blob + a.lay.up_s + static_cast<size_t>(p) * C * kScaleChunkBytes + row * 8;
+    GateUpSrc P;
+    P.r = make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
+    P.vq = static_cast<uint32_t>(lane) * 16;
+    P.vs = static_cast<uint32_t>(row) * 8;
+    P.gq = static_cast<uint32_t>(a.lay.gate_q + static_cast<size_t>(p) * C * kChunkBytes);
+    P.uq = static_cast<uint32_t>(a.lay.up_q + static_cast<size_t>(p) * C * kChunkBytes);
+    P.gs = static_cast<uint32_t>(a.lay.gate_s + static_cast<size_t>(p) * C * kScaleChunkBytes);
+    P.us = static_cast<uint32_t>(a.lay.up_s + static_cast<size_t>(p) * C * kScaleChunkBytes);
     // Chunks of this wave: wave, wave + 4, ...
     const int nper = wave < C ? (C - wave + 3) / 4 : 0;
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
@@ -167,7 +176,7 @@ __device__ void gateup_panel(const FwdArgs &a, const uint8_t *blob, int r0, int 
         __syncthreads();
         for (int i = tid; i < mc * (H / 8); i += 256) {
             const int m = i / (H / 8), q = i % (H / 8);
-            const int t = token_of_row(a, r0 + mb + m);
+            const int t = rows.token(r0 + mb + m);
             float v[8];
             if (a.act_bf16) {
                 const uint4 raw = gload<uint4>(static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * H + 8 * q);
@@ -220,23 +229,39 @@ __device__ void gateup_panel(const FwdArgs &a, const uint8_t *blob, int r0, int 
                 v = v + red[((w * MAXM + m) * 16 + r) * 2 + 1];
             }
             const float hval = g / (1.0f + expf(-g)) * v;
-            a.h[static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r] = static_cast<_Float16>(hval);
+            _Float16 *dst = a.h + static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r;
+            if (COHERENT) store_coherent(dst, static_cast<_Float16>(hval));
+            else *dst = static_cast<_Float16>(hval);
         }
     }
 }
+
+// Nothing to wait for.
+struct NoWait {
+    __device__ void operator()() const {}
+};
+
+// Rows of a forward call read straight from its routing arrays (kernels that
+// run after the routing kernels have finished).
+struct PlainRows {
+    const FwdArgs &a;
+    __device__ int token(int row) const { return token_of_row(a, row); }
+    __device__ int entry(int row) const { return row < a.n_tok * a.k ? a.gather[row] : row; }
+    __device__ float weight(int row) const { return row < a.n_tok * a.k ? a.topk_w[a.gather[row]] : 1.0f; }
+};
 
 struct DownBuf {
     uint4 w[kPipeGroup];
     uint2 s[kPipeGroup];
 };
 
-__device__ __forceinline__ void down_load(DownBuf &b, const uint8_t *dq, const uint8_t *ds, int first,
-                                          int C) {
+__device__ __forceinline__ void down_load(DownBuf &b, rsrc_t r, uint32_t vq, uint32_t vs, uint32_t sq, uint32_t ss,
+                                          int first, int C) {
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
-        const int c = min(first + g, C - 1);
-        b.w[g] = gload<uint4>(dq + static_cast<size_t>(c) * kChunkBytes);
-        b.s[g] = gload<uint2>(ds + static_cast<size_t>(c) * kScaleChunkBytes);
+        const uint32_t c = static_cast<uint32_t>(min(first + g, C - 1));
+        b.w[g] = bload<uint4>(r, vq, sq + c * kChunkBytes);
+        b.s[g] = bload<uint2>(r, vs, ss + c * kScaleChunkBytes);
     }
 }
 
@@ -269,24 +294,29 @@ __device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, c
 // One down work item: output panels 2pg and 2pg+1 of expert blob `blob` for
 // hidden rows r0..r0+M-1.  Wave w takes panel 2pg + (w & 1) and reduction
 // half (w >> 1); the halves are summed through LDS in a fixed order.  Writes
-// the entry rows of ys (routed rows times their routing weight, shared rows
-// with weight 1).  All 256 threads must call it.
-template <int MAXM, bool COHERENT = false>
-__device__ void down_panelgroup(const FwdArgs &a, const uint8_t *blob, int r0, int M, int pg, uint8_t *lds) {
+// ys row rows.entry(row) scaled by rows.weight(row) (the routing weight of a
+// routed row, 1 for a shared row).  With COHERENT, h is read and ys written
+// device-coherently (producer and consumer in the same launch); before_h()
+// runs, by all threads, after the first weight loads are issued and before h
+// is read (a wait for h's producers).  All 256 threads must call it.
+template <int MAXM, bool COHERENT = false, class Rows, class BeforeH>
+__device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int pg,
+                                uint8_t *lds, const BeforeH &before_h) {
     const int H = a.hidden, I = a.inter;
     const int C = I / kChunkK;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
     const int row = lane & 15, kq = lane >> 4;
     const int p = 2 * pg + (wave & 1), half = wave >> 1;
     const int c_begin = half == 0 ? 0 : (C + 1) / 2;
     const int c_end = half == 0 ? (C + 1) / 2 : C;
     const int nper = c_end - c_begin;
-    const uint8_t *dq = blob + a.lay.down_q + static_cast<size_t>(p) * C * kChunkBytes + lane * 16;
-    const uint8_t *ds = blob + a.lay.down_s + static_cast<size_t>(p) * C * kScaleChunkBytes + row * 8;
+    const rsrc_t rs = make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
+    const uint32_t vq = static_cast<uint32_t>(lane) * 16, vs = static_cast<uint32_t>(row) * 8;
+    const uint32_t sq = static_cast<uint32_t>(a.lay.down_q + static_cast<size_t>(p) * C * kChunkBytes);
+    const uint32_t ss = static_cast<uint32_t>(a.lay.down_s + static_cast<size_t>(p) * C * kScaleChunkBytes);
     uint8_t *hs = lds;
     float *cs = reinterpret_cast<float *>(lds + static_cast<size_t>(MAXM) * I * 2);
     float *red = cs + MAXM * (I / 8);
-    const int routed = a.n_tok * a.k;
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
 
     for (int mb = 0; mb < M; mb += MAXM) {
@@ -295,11 +325,13 @@ __device__ void down_panelgroup(const FwdArgs &a, const uint8_t *blob, int r0, i
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
         DownBuf A, B;
-        down_load(A, dq, ds, c_begin, C);
+        down_load(A, rs, vq, vs, sq, ss, c_begin, C);
+        if (mb == 0) before_h();
         __syncthreads();
         for (int i = tid; i < mc * (I / 8); i += 256) {
             const int m = i / (I / 8), q = i % (I / 8);
-            const uint4 raw = gload<uint4>(a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q);
+            const _Float16 *src = a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q;
+            const uint4 raw = COHERENT ? load_coherent_16B(src) : gload<uint4>(src);
             const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
             float v[8];
 #pragma unroll
@@ -308,9 +340,9 @@ __device__ void down_panelgroup(const FwdArgs &a, const uint8_t *blob, int r0, i
         }
         __syncthreads();
         for (int i = 0; i < nper; i += 2 * kPipeGroup) {
-            if (i + kPipeGroup < nper) down_load(B, dq, ds, c_begin + i + kPipeGroup, C);
+            if (i + kPipeGroup < nper) down_load(B, rs, vq, vs, sq, ss, c_begin + i + kPipeGroup, C);
             down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), kq, mc, M0, M1, G, acc);
-            if (i + 2 * kPipeGroup < nper) down_load(A, dq, ds, c_begin + i + 2 * kPipeGroup, C);
+            if (i + 2 * kPipeGroup < nper) down_load(A, rs, vq, vs, sq, ss, c_begin + i + 2 * kPipeGroup, C);
             if (i + kPipeGroup < nper)
                 down_math<MAXM>(B, hs, cs, I, c_begin + i + kPipeGroup, min(kPipeGroup, nper - i - kPipeGroup),
                                 kq, mc, M0, M1, G, acc);
@@ -331,8 +363,8 @@ __device__ void down_panelgroup(const FwdArgs &a, const uint8_t *blob, int r0, i
             // waves `side` (first half) and `side + 2` (second half)
             const float d = red[(side * MAXM + m) * 16 + r] + red[((side + 2) * MAXM + m) * 16 + r];
             const int hrow = r0 + mb + m;
-            const int entry = hrow < routed ? a.gather[hrow] : hrow;
-            const float wgt = hrow < routed ? a.topk_w[entry] : 1.0f;
+            const int entry = rows.entry(hrow);
+            const float wgt = rows.weight(hrow);
             float *dst = a.ys + static_cast<size_t>(entry) * H + (2 * pg + side) * kPanel + r;
             if (COHERENT) store_coherent(dst, wgt * d);
             else *dst = wgt * d;

@@ -1,5 +1,6 @@
 // gemv.hip -- decode-shaped expert FFN kernels (VALU GEMV work items from
-// dev_gemv.h), one workgroup per (unit, panel) or (unit, panel pair).
+// dev_gemv.h), one workgroup per (unit, panel) or (unit, panel pair), for a
+// forward call whose routing was computed by earlier launches.
 //
 // The down kernel can also finish the layer: with a per-panel-pair arrival
 // counter, the last workgroup to finish a panel pair (over all units) sums
@@ -20,7 +21,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin
     if (a.skip_shared && e == a.n_experts) return;
     const uint8_t *blob = a.table[e];
     if (!blob || M <= 0) return;
-    dev::gateup_panel<MAXM>(a, blob, r0, M, p, lds);
+    dev::gateup_panel<MAXM>(a, dev::PlainRows{a}, blob, r0, M, p, lds);
 }
 
 template <int MAXM, bool FUSED_COMBINE>
@@ -31,7 +32,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
     int e, r0, M;
     if (!dev::resolve(a, u, e, r0, M)) return;
     const uint8_t *blob = a.table[e];
-    if (blob && M > 0) dev::down_panelgroup<MAXM, FUSED_COMBINE>(a, blob, r0, M, pg, lds);
+    if (blob && M > 0)
+        dev::down_panelgroup<MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::NoWait{});
     if (FUSED_COMBINE) {
         const int units = *a.n_union + (a.has_shared ? 1 : 0);
         if (dev::arrive_last(counters + pg, units)) dev::combine_panelgroup(a, pg);

@@ -22,6 +22,8 @@
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 

@@ -90,6 +90,7 @@ def test_decode_b1_fused_layer_call(decode_b1):
     x = B.activations_to_device(data.x)
     y, idx, w, u = L.layer(x)
     torch.cuda.synchronize()
+    assert L.device_errors() == 0
     three = gpu_run(B, L, data, with_logits=False)
     assert np.array_equal(y.cpu().numpy().view(np.uint32), three["y"].view(np.uint32))
     assert np.array_equal(idx.cpu().numpy(), three["idx"])
@@ -112,6 +113,7 @@ def test_fused_layer_small_batches(n_tok, act):
         torch.cuda.synchronize()
         outs.append(y.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert L.device_errors() == 0
     three = gpu_run(B, L, data, with_logits=False)
     assert np.array_equal(outs[0].view(np.uint32), three["y"].view(np.uint32))
     nu = int(u["n_union"].cpu()[0])
@@ -122,6 +124,26 @@ def test_fused_layer_small_batches(n_tok, act):
     ref = oracle_route(data)
     check_routing(three, ref, check_logits=False)
     check_outputs(outs[0], oracle_y(data, ref, range(n_tok)), f"fused n_tok={n_tok}")
+    L.close()
+
+
+def test_fused_layer_alternating_sizes():
+    """One layer, fused calls of changing batch size back to back: the launch
+    counters must be clean after every call."""
+    spec = MEDIUM.with_(act="bf16")
+    data = Data(spec, n_tok=4)
+    L = make_layer(B, data, path=B.PATH_GEMV, max_tokens=4)
+    ref = oracle_route(data)
+    y_ref = oracle_y(data, ref, range(4))
+    for n in (1, 4, 2, 3, 1, 4):
+        x = B.activations_to_device(data.x[:n])
+        y, idx, w, u = L.layer(x)
+        torch.cuda.synchronize()
+        log(f"  fused call n_tok={n}")
+        assert L.device_errors() == 0
+        # routing of a token does not depend on the other tokens of the batch
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"][:n])
+        check_outputs(y.cpu().numpy(), y_ref[:n], f"alternating n_tok={n}")
     L.close()
 
 
