@@ -91,6 +91,122 @@ struct BFrag {
     uint2 s[4];
 };
 
+// State of one work item (chunk x N-block) shared by its K loop and
+// epilogue.
+struct ItemState {
+    const _Float16 *asrc;
+    uint32_t src_off[2][4];      // A rows staged by this wave (fp16 elements, column 0)
+    int my_groups;
+    dev::rsrc_t brs;             // weight blob
+    uint32_t qlane, slane;
+    uint32_t qoff[4], soff[4];   // this wave's 4 B panels
+    bool bvalid[4];
+    int row0, rows, nb, C;
+};
+
+// K loop and epilogue of one item with NF 16-row fragments (rows of the
+// chunk past `rows` are padding, computed and discarded).  A fixed fragment
+// count keeps the MFMA stream free of per-fragment branches.
+template <bool GATEUP, int NF>
+__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, uint8_t (*s_a)[kChunkRows * kRowBytes]) {
+    const int H = a.hidden, I = a.inter;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l15 = lane & 15, l4 = lane >> 4;
+    const int routed = a.n_tok * a.k;
+    auto stage = [&](int c, int buf) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if (g < st.my_groups) {
+                const int grp = wave + 4 * g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    copy16_to_lds(st.asrc + st.src_off[g][i] + c * kChunkK, &s_a[buf][(grp * 16 + i * 4) * kRowBytes]);
+            }
+        }
+    };
+    auto load_b = [&](int c, BFrag &f) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f.q[b] = dev::bload<uint4>(st.brs, st.qlane, st.qoff[b] + static_cast<uint32_t>(c) * kChunkBytes);
+            f.s[b] = dev::bload<uint2>(st.brs, st.slane, st.soff[b] + static_cast<uint32_t>(c) * kScaleChunkBytes);
+        }
+    };
+
+    floatx4 acc[NF][4];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[f][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // LDS byte offset of this lane's A fragment for k-step s (frag f adds
+    // f * 16 rows).
+    uint32_t a_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a_off[s] = lds_unit(l15, 4 * s + l4);
+    const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+
+    BFrag bn, bc;
+    stage(0, 0);
+    load_b(0, bn);
+    for (int c = 0; c < st.C; ++c) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        bc = bn;
+        if (c + 1 < st.C) {
+            stage(c + 1, (c + 1) & 1);
+            load_b(c + 1, bn);
+        }
+        const uint8_t *tile = s_a[c & 1];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            half8 bf[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t w = (s == 0) ? bc.q[b].x : (s == 1) ? bc.q[b].y : (s == 2) ? bc.q[b].z : bc.q[b].w;
+                bf[b] = dequant8(w, scale_pair(bc.s[b], s), M0, M1, G);
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const half8 av = *reinterpret_cast<const half8 *>(tile + a_off[s] + f * 16 * kRowBytes);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bf[b], acc[f][b], 0, 0, 0);
+            }
+        }
+    }
+
+    // Epilogue.  Lane holds D[m = 4*l4 + j][n = l15] of each 16x16 tile.
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = 16 * f + 4 * l4 + j;
+            if (m < st.rows) {
+                if (GATEUP) {
+#pragma unroll
+                    for (int pb = 0; pb < 2; ++pb) {
+                        const float g = acc[f][pb][j], v = acc[f][2 + pb][j];
+                        const float hval = g / (1.0f + expf(-g)) * v;
+                        const int col = st.nb * 128 + wave * 32 + pb * 16 + l15;
+                        a.h[static_cast<size_t>(st.row0 + m) * I + col] = static_cast<_Float16>(hval);
+                    }
+                } else {
+                    const int hrow = st.row0 + m;
+                    const int entry = hrow < routed ? a.gather[hrow] : hrow;
+                    const float wgt = hrow < routed ? a.topk_w[entry] : 1.0f;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        if (st.bvalid[b]) {
+                            const int col = (st.nb * 16 + wave * 4 + b) * kPanel + l15;
+                            a.ys[static_cast<size_t>(entry) * H + col] = wgt * acc[f][b][j];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     // Two A tiles (double buffer): kChunkRows rows x 128 fp16 each.
@@ -98,14 +214,11 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     __shared__ int s_tok[kChunkRows];
     const int H = a.hidden, I = a.inter;
     const int K = GATEUP ? H : I;
-    const int C = K / kChunkK;
     const int NB = GATEUP ? I / 128 : (H + 255) / 256;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l15 = lane & 15, l4 = lane >> 4;
     const int n_items = *a.n_chunks * NB;
     const int routed = a.n_tok * a.k;
-    const _Float16 *asrc = GATEUP ? a.xh : a.h;     // fp16 rows
-    const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
 
     // Consecutive virtual block ids on the same XCD (blocks go round-robin
     // over 8 XCDs).
@@ -117,15 +230,22 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         const ChunkDesc d = a.chunks[chunk];
         const uint8_t *blob = a.table[d.expert];
         if (!blob) continue;
-        const int rows = d.rows;
-        const int nf = (rows + 15) >> 4;
+        ItemState st;
+        st.asrc = GATEUP ? a.xh : a.h;
+        st.row0 = d.row0;
+        st.rows = d.rows;
+        st.nb = nb;
+        st.C = K / kChunkK;
+        const int nf = (d.rows + 15) >> 4;
+        // Fragment count: 2 for small chunks, else 8 (padding rows are
+        // computed and discarded).
+        const int nfc = nf > 2 ? 8 : 2;
 
         // Weight panels of this wave (4 B fragments of 16 rows each), as
-        // wave-uniform byte offsets into the blob.
-        const uint8_t *qbase = blob + lane * 16;
-        const uint8_t *sbase = blob + l15 * 8;
-        uint32_t qoff[4], soff[4];
-        bool bvalid[4];
+        // wave-uniform byte offsets into the blob, read with buffer loads.
+        st.brs = dev::make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
+        st.qlane = static_cast<uint32_t>(lane) * 16;
+        st.slane = static_cast<uint32_t>(l15) * 8;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             int panel;
@@ -134,136 +254,41 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
                 panel = nb * 8 + wave * 2 + (b & 1);
                 qs = (b < 2) ? a.lay.gate_q : a.lay.up_q;
                 ss = (b < 2) ? a.lay.gate_s : a.lay.up_s;
-                bvalid[b] = true;
+                st.bvalid[b] = true;
             } else {
                 panel = nb * 16 + wave * 4 + b;
                 qs = a.lay.down_q;
                 ss = a.lay.down_s;
-                bvalid[b] = panel < H / kPanel;
-                if (!bvalid[b]) panel = 0;
+                st.bvalid[b] = panel < H / kPanel;
+                if (!st.bvalid[b]) panel = 0;
             }
-            qoff[b] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * C * kChunkBytes);
-            soff[b] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * C * kScaleChunkBytes);
+            st.qoff[b] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * st.C * kChunkBytes);
+            st.soff[b] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * st.C * kScaleChunkBytes);
         }
 
         __syncthreads();   // previous item is done with s_tok and the A tiles
         for (int m = tid; m < kChunkRows; m += 256) {
             // Rows past `rows` repeat row 0: their results are discarded.
-            const int mm = m < rows ? m : 0;
+            const int mm = m < d.rows ? m : 0;
             const int r = d.row0 + mm;
             s_tok[m] = GATEUP ? (r < routed ? a.gather[r] / a.k : r - routed) : r;
         }
         __syncthreads();
-        // This wave stages 16-row groups wave, wave+4 of the first nf*16 rows
-        // (nf <= 8): one copy16 per 4 rows, swizzled on the source side so
-        // that lane L fills slot (L & 15) of row (L >> 4).  Source offsets
-        // (in fp16 elements, column 0) are fixed for the item.
-        const int my_groups = nf > wave ? (nf - wave + 3) / 4 : 0;
-        uint32_t src_off[2][4];
+        // This wave stages 16-row groups wave, wave+4 of the first nfc*16
+        // rows: one copy16 per 4 rows, swizzled on the source side so that
+        // lane L fills slot (L & 15) of row (L >> 4).
+        const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
+        st.my_groups = nfc > wave ? (nfc - wave + 3) / 4 : 0;
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = (wave + 4 * g) * 16 + i * 4 + l4;
                 const int q = l15 ^ (m & 15);
-                src_off[g][i] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
+                st.src_off[g][i] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
             }
-        auto stage = [&](int c, int buf) {
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                if (g < my_groups) {
-                    const int grp = wave + 4 * g;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        copy16_to_lds(asrc + src_off[g][i] + c * kChunkK, &s_a[buf][(grp * 16 + i * 4) * kRowBytes]);
-                }
-            }
-        };
-        auto load_b = [&](int c, BFrag &f) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                f.q[b] = gload<uint4>(qbase + qoff[b] + c * kChunkBytes);
-                f.s[b] = gload<uint2>(sbase + soff[b] + c * kScaleChunkBytes);
-            }
-        };
-
-        floatx4 acc[kMaxFrags][4];
-#pragma unroll
-        for (int f = 0; f < kMaxFrags; ++f)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[f][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-        // LDS byte offset of this lane's A fragment for k-step s (frag f adds
-        // f * 16 rows).
-        uint32_t a_off[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) a_off[st] = lds_unit(l15, 4 * st + l4);
-        const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
-
-        BFrag bn, bc;
-        stage(0, 0);
-        load_b(0, bn);
-        for (int c = 0; c < C; ++c) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            bc = bn;
-            if (c + 1 < C) {
-                stage(c + 1, (c + 1) & 1);
-                load_b(c + 1, bn);
-            }
-            const uint8_t *tile = s_a[c & 1];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8 bf[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t w = (s == 0) ? bc.q[b].x : (s == 1) ? bc.q[b].y : (s == 2) ? bc.q[b].z : bc.q[b].w;
-                    bf[b] = dequant8(w, scale_pair(bc.s[b], s), M0, M1, G);
-                }
-#pragma unroll
-                for (int f = 0; f < kMaxFrags; ++f) {
-                    if (f < nf) {
-                        const half8 av = *reinterpret_cast<const half8 *>(tile + a_off[s] + f * 16 * kRowBytes);
-#pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bf[b], acc[f][b], 0, 0, 0);
-                    }
-                }
-            }
-        }
-
-        // Epilogue.  Lane holds D[m = 4*l4 + j][n = l15] of each 16x16 tile.
-#pragma unroll
-        for (int f = 0; f < kMaxFrags; ++f) {
-            if (f < nf) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int m = 16 * f + 4 * l4 + j;
-                    if (m < rows) {
-                        if (GATEUP) {
-#pragma unroll
-                            for (int pb = 0; pb < 2; ++pb) {
-                                const float g = acc[f][pb][j], v = acc[f][2 + pb][j];
-                                const float hval = g / (1.0f + expf(-g)) * v;
-                                const int col = nb * 128 + wave * 32 + pb * 16 + l15;
-                                a.h[static_cast<size_t>(d.row0 + m) * I + col] = static_cast<_Float16>(hval);
-                            }
-                        } else {
-                            const int hrow = d.row0 + m;
-                            const int entry = hrow < routed ? a.gather[hrow] : hrow;
-                            const float wgt = hrow < routed ? a.topk_w[entry] : 1.0f;
-#pragma unroll
-                            for (int b = 0; b < 4; ++b) {
-                                if (bvalid[b]) {
-                                    const int col = (nb * 16 + wave * 4 + b) * kPanel + l15;
-                                    a.ys[static_cast<size_t>(entry) * H + col] = wgt * acc[f][b][j];
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-        }
+        if (nfc == 8) run_item<GATEUP, 8>(a, st, s_a);
+        else run_item<GATEUP, 2>(a, st, s_a);
     }
 }
 
