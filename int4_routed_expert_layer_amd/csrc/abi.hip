@@ -173,6 +173,7 @@ struct coli_layer {
     int max_chunks = 0;
     int32_t *err = nullptr;
     int32_t *sync_counters = nullptr;  // [1 + H/32] arrival counters, zero at rest
+    int32_t *queues = nullptr;         // [kQueueInts] grouped work-queue counters, zero at rest
     uint8_t *pin_stage = nullptr;    // pinned staging for placement
 
     // tiered forward
@@ -347,6 +348,7 @@ FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, 
     a.y = y;
     a.chunks = L->chunks;
     a.n_chunks = L->n_chunks;
+    a.queues = L->queues;
     a.skip_shared = 0;
     return a;
 }
@@ -391,7 +393,7 @@ void free_layer(coli_layer *L) {
     for (auto p : L->dev_tables) (void)hipFree(const_cast<uint8_t **>(p));
     if (L->side) (void)hipStreamDestroy(L->side);
     void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->xh, L->ys, L->chunks, L->n_chunks, L->err,
-                    L->sync_counters};
+                    L->sync_counters, L->queues};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (L->pin_stage) (void)hipHostFree(L->pin_stage);
@@ -500,6 +502,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
         {reinterpret_cast<void **>(&L->err), sizeof(int32_t), "error flags"},
         {reinterpret_cast<void **>(&L->sync_counters), sizeof(int32_t) * (1 + H / 32), "arrival counters"},
+        {reinterpret_cast<void **>(&L->queues), sizeof(int32_t) * kQueueInts, "work-queue counters"},
     };
     for (auto &a : allocs) {
         if ((he = hipMalloc(a.p, a.n)) != hipSuccess) {
@@ -512,6 +515,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     if ((he = hipMemset(L->table_dev, 0, sizeof(void *) * (E + 1))) != hipSuccess ||
         (he = hipMemset(L->err, 0, sizeof(int32_t))) != hipSuccess ||
         (he = hipMemset(L->sync_counters, 0, sizeof(int32_t) * (1 + H / 32))) != hipSuccess ||
+        (he = hipMemset(L->queues, 0, sizeof(int32_t) * kQueueInts)) != hipSuccess ||
         (he = hipMemset(L->bias, 0, sizeof(float) * E)) != hipSuccess ||
         (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_stage), L->lay.total, hipHostMallocDefault)) != hipSuccess ||
         (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_union), sizeof(int32_t) * (E + 1), hipHostMallocDefault)) != hipSuccess ||

@@ -34,6 +34,7 @@ using dev::gload;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRowBytes = kChunkK * 2;     // one staged row: 128 fp16
 
@@ -98,20 +99,28 @@ struct ItemState {
     uint32_t src_off[2][4];      // A rows staged by this wave (fp16 elements, column 0)
     int my_groups;
     dev::rsrc_t brs;             // weight blob
-    uint32_t qlane, slane;
-    uint32_t qoff[4], soff[4];   // this wave's 4 B panels
-    bool bvalid[4];
+    uint32_t qv_even, qv_odd, sv; // per-lane byte offsets of the B slots and scales
+    uint32_t qoff[2], soff[2];   // this wave's two 32-row B tiles (uniform)
+    bool bvalid[2];
     int row0, rows, nb, C;
 };
 
-// K loop and epilogue of one item with NF 16-row fragments (rows of the
-// chunk past `rows` are padding, computed and discarded).  A fixed fragment
-// count keeps the MFMA stream free of per-fragment branches.
-template <bool GATEUP, int NF>
-__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, uint8_t (*s_a)[kChunkRows * kRowBytes]) {
+// K loop and epilogue of one item on v_mfma_f32_32x32x16_f16 with MT 32-row
+// tiles of the chunk (rows past `rows` are padding, computed and discarded).
+//
+// B tile nt covers 32 weight rows = two 16-row panels.  For the 16-wide K
+// slice t of a 128-wide chunk, lane L needs rows n = L % 32, columns
+// 16t + 8(L / 32) + 0..7: in the device layout those are dword t / 2 of the
+// 16-byte slot (n % 16) + 16 (L / 32) (t even) or (n % 16) + 16 (2 + L / 32)
+// (t odd) of panel n / 16, so each lane loads two 16-byte slots per tile and
+// step and every byte is used once.  The A fragment of slice t is the 16-byte
+// unit 2t + L / 32 of row L % 32 in the staged tile.
+template <bool GATEUP, int MT>
+__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, uint8_t (*s_a)[kChunkRows * kRowBytes],
+                                         const int *s_ent, const float *s_w) {
     const int H = a.hidden, I = a.inter;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int l15 = lane & 15, l4 = lane >> 4;
+    const int l31 = lane & 31, lh = lane >> 5;
     const int routed = a.n_tok * a.k;
     auto stage = [&](int c, int buf) {
 #pragma unroll
@@ -124,28 +133,31 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
             }
         }
     };
-    auto load_b = [&](int c, BFrag &f) {
+    struct B32 {
+        uint4 qe[2], qo[2];
+        uint2 sc[2];
+    };
+    auto load_b = [&](int c, B32 &f) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            f.q[b] = dev::bload<uint4>(st.brs, st.qlane, st.qoff[b] + static_cast<uint32_t>(c) * kChunkBytes);
-            f.s[b] = dev::bload<uint2>(st.brs, st.slane, st.soff[b] + static_cast<uint32_t>(c) * kScaleChunkBytes);
+        for (int nt = 0; nt < 2; ++nt) {
+            const uint32_t cq = st.qoff[nt] + static_cast<uint32_t>(c) * kChunkBytes;
+            f.qe[nt] = dev::bload<uint4>(st.brs, st.qv_even, cq);
+            f.qo[nt] = dev::bload<uint4>(st.brs, st.qv_odd, cq);
+            f.sc[nt] = dev::bload<uint2>(st.brs, st.sv, st.soff[nt] + static_cast<uint32_t>(c) * kScaleChunkBytes);
         }
     };
 
-    floatx4 acc[NF][4];
+    floatx16 acc[MT][2];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[f][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
 
-    // LDS byte offset of this lane's A fragment for k-step s (frag f adds
-    // f * 16 rows).
-    uint32_t a_off[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a_off[s] = lds_unit(l15, 4 * s + l4);
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
 
-    BFrag bn, bc;
+    B32 bn, bc;
     stage(0, 0);
     load_b(0, bn);
     for (int c = 0; c < st.C; ++c) {
@@ -157,48 +169,61 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
             load_b(c + 1, bn);
         }
         const uint8_t *tile = s_a[c & 1];
+        // A fragments are read one slice ahead so LDS latency overlaps the
+        // MFMAs of the current slice.
+        half8 av[MT];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            half8 bf[4];
+        for (int mt = 0; mt < MT; ++mt)
+            av[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, lh));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t w = (s == 0) ? bc.q[b].x : (s == 1) ? bc.q[b].y : (s == 2) ? bc.q[b].z : bc.q[b].w;
-                bf[b] = dequant8(w, scale_pair(bc.s[b], s), M0, M1, G);
+        for (int t = 0; t < 8; ++t) {
+            half8 an[MT];
+            if (t + 1 < 8) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    an[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, 2 * (t + 1) + lh));
+            }
+            half8 bf[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const uint4 &q = (t & 1) ? bc.qo[nt] : bc.qe[nt];
+                const int s2 = t >> 1;
+                const uint32_t w = s2 == 0 ? q.x : s2 == 1 ? q.y : s2 == 2 ? q.z : q.w;
+                bf[nt] = dequant8(w, scale_pair(bc.sc[nt], s2), M0, M1, G);
             }
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const half8 av = *reinterpret_cast<const half8 *>(tile + a_off[s] + f * 16 * kRowBytes);
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bf[b], acc[f][b], 0, 0, 0);
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+            if (t + 1 < 8) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) av[mt] = an[mt];
             }
         }
     }
 
-    // Epilogue.  Lane holds D[m = 4*l4 + j][n = l15] of each 16x16 tile.
+    // Epilogue.  Lane holds D[m = 8(i / 4) + 4(L / 32) + i % 4][n = L % 32]
+    // of each 32x32 tile.
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = 16 * f + 4 * l4 + j;
+        for (int i = 0; i < 16; ++i) {
+            const int m = mt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
             if (m < st.rows) {
                 if (GATEUP) {
-#pragma unroll
-                    for (int pb = 0; pb < 2; ++pb) {
-                        const float g = acc[f][pb][j], v = acc[f][2 + pb][j];
-                        const float hval = g / (1.0f + expf(-g)) * v;
-                        const int col = st.nb * 128 + wave * 32 + pb * 16 + l15;
-                        a.h[static_cast<size_t>(st.row0 + m) * I + col] = static_cast<_Float16>(hval);
-                    }
+                    const float g = acc[mt][0][i], v = acc[mt][1][i];
+                    const float hval = g / (1.0f + expf(-g)) * v;
+                    const int col = st.nb * 128 + wave * 32 + l31;
+                    a.h[static_cast<size_t>(st.row0 + m) * I + col] = static_cast<_Float16>(hval);
                 } else {
-                    const int hrow = st.row0 + m;
-                    const int entry = hrow < routed ? a.gather[hrow] : hrow;
-                    const float wgt = hrow < routed ? a.topk_w[entry] : 1.0f;
+                    const int entry = s_ent[m];
+                    const float wgt = s_w[m];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        if (st.bvalid[b]) {
-                            const int col = (st.nb * 16 + wave * 4 + b) * kPanel + l15;
-                            a.ys[static_cast<size_t>(entry) * H + col] = wgt * acc[f][b][j];
+                    for (int nt = 0; nt < 2; ++nt) {
+                        if (st.bvalid[nt]) {
+                            const int col = st.nb * 256 + wave * 64 + nt * 32 + l31;
+                            a.ys[static_cast<size_t>(entry) * H + col] = wgt * acc[mt][nt][i];
                         }
                     }
                 }
@@ -212,20 +237,36 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     // Two A tiles (double buffer): kChunkRows rows x 128 fp16 each.
     __shared__ __align__(16) uint8_t s_a[2][kChunkRows * kRowBytes];
     __shared__ int s_tok[kChunkRows];
+    __shared__ int s_ent[GATEUP ? 1 : kChunkRows];     // down: output entry and routing weight per row
+    __shared__ float s_w[GATEUP ? 1 : kChunkRows];
     const int H = a.hidden, I = a.inter;
     const int K = GATEUP ? H : I;
     const int NB = GATEUP ? I / 128 : (H + 255) / 256;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l15 = lane & 15, l4 = lane >> 4;
-    const int n_items = *a.n_chunks * NB;
+    const int l31 = lane & 31, lh = lane >> 5;
     const int routed = a.n_tok * a.k;
 
-    // Consecutive virtual block ids on the same XCD (blocks go round-robin
-    // over 8 XCDs).
-    int vb = blockIdx.x;
-    if ((gridDim.x & 7) == 0) vb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    // Work items (chunk, N-block) are dealt to kGroupedQueues queues by
+    // chunk (chunk c to queue c mod 8) and taken dynamically: workgroup b
+    // draws from queue b mod 8, which on an 8-XCD part is the queue of its
+    // XCD, so the N-blocks of a chunk (same activation rows) share an L2.
+    // Items differ in cost (chunks of 1 to 128 rows); dynamic claiming keeps
+    // every workgroup busy until its queue is empty.
+    const int nq = gridDim.x >= kGroupedQueues ? kGroupedQueues : 1;
+    const int q = blockIdx.x % nq;
+    const int n_chunks = *a.n_chunks;
+    const int q_items = (n_chunks > q ? (n_chunks - q + nq - 1) / nq : 0) * NB;
+    int32_t *ticket = a.queues + q * kQueueStride;
+    __shared__ int s_item;
 
-    for (int item = vb; item < n_items; item += gridDim.x) {
+    for (;;) {
+        __syncthreads();       // every thread has read the previous s_item
+        if (tid == 0) s_item = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int j = s_item;
+        if (j >= q_items) break;
+        const int item = (q + nq * (j / NB)) * NB + j % NB;
         const int chunk = item / NB, nb = item % NB;
         const ChunkDesc d = a.chunks[chunk];
         const uint8_t *blob = a.table[d.expert];
@@ -236,34 +277,35 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         st.rows = d.rows;
         st.nb = nb;
         st.C = K / kChunkK;
-        const int nf = (d.rows + 15) >> 4;
-        // Fragment count: 2 for small chunks, else 8 (padding rows are
-        // computed and discarded).
-        const int nfc = nf > 2 ? 8 : 2;
+        // 32-row tiles: 1, 2 or 4 (padding rows are computed and discarded).
+        const int mt = d.rows > 64 ? 4 : (d.rows > 32 ? 2 : 1);
 
-        // Weight panels of this wave (4 B fragments of 16 rows each), as
-        // wave-uniform byte offsets into the blob, read with buffer loads.
+        // This wave's two 32-row B tiles (two 16-row panels each), as
+        // uniform offsets, and the per-lane slot offsets inside them.
         st.brs = dev::make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
-        st.qlane = static_cast<uint32_t>(lane) * 16;
-        st.slane = static_cast<uint32_t>(l15) * 8;
+        const uint32_t pstep = static_cast<uint32_t>(st.C) * kChunkBytes;   // bytes per panel
+        const uint32_t r16 = static_cast<uint32_t>(l31 & 15), hi = static_cast<uint32_t>(l31 >> 4);
+        st.qv_even = hi * pstep + 16 * (r16 + 16 * static_cast<uint32_t>(lh));
+        st.qv_odd = hi * pstep + 16 * (r16 + 16 * (2 + static_cast<uint32_t>(lh)));
+        st.sv = hi * static_cast<uint32_t>(st.C) * kScaleChunkBytes + r16 * 8;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int nt = 0; nt < 2; ++nt) {
             int panel;
             size_t qs, ss;
             if (GATEUP) {
-                panel = nb * 8 + wave * 2 + (b & 1);
-                qs = (b < 2) ? a.lay.gate_q : a.lay.up_q;
-                ss = (b < 2) ? a.lay.gate_s : a.lay.up_s;
-                st.bvalid[b] = true;
+                panel = nb * 8 + wave * 2;          // gate (nt 0) or up (nt 1) rows of the same columns
+                qs = nt == 0 ? a.lay.gate_q : a.lay.up_q;
+                ss = nt == 0 ? a.lay.gate_s : a.lay.up_s;
+                st.bvalid[nt] = true;
             } else {
-                panel = nb * 16 + wave * 4 + b;
+                panel = nb * 16 + wave * 4 + nt * 2;
                 qs = a.lay.down_q;
                 ss = a.lay.down_s;
-                st.bvalid[b] = panel < H / kPanel;
-                if (!st.bvalid[b]) panel = 0;
+                st.bvalid[nt] = panel + 1 < H / kPanel;
+                if (!st.bvalid[nt]) panel = 0;
             }
-            st.qoff[b] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * st.C * kChunkBytes);
-            st.soff[b] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * st.C * kScaleChunkBytes);
+            st.qoff[nt] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * st.C * kChunkBytes);
+            st.soff[nt] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * st.C * kScaleChunkBytes);
         }
 
         __syncthreads();   // previous item is done with s_tok and the A tiles
@@ -272,13 +314,19 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
             const int mm = m < d.rows ? m : 0;
             const int r = d.row0 + mm;
             s_tok[m] = GATEUP ? (r < routed ? a.gather[r] / a.k : r - routed) : r;
+            if (!GATEUP) {
+                const int entry = r < routed ? a.gather[r] : r;
+                s_ent[m] = entry;
+                s_w[m] = r < routed ? a.topk_w[entry] : 1.0f;
+            }
         }
         __syncthreads();
-        // This wave stages 16-row groups wave, wave+4 of the first nfc*16
+        // This wave stages 16-row groups wave, wave+4 of the first mt*32
         // rows: one copy16 per 4 rows, swizzled on the source side so that
         // lane L fills slot (L & 15) of row (L >> 4).
         const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
-        st.my_groups = nfc > wave ? (nfc - wave + 3) / 4 : 0;
+        const int ng = 2 * mt;
+        st.my_groups = ng > wave ? (ng - wave + 3) / 4 : 0;
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -287,9 +335,13 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
                 const int q = l15 ^ (m & 15);
                 st.src_off[g][i] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
             }
-        if (nfc == 8) run_item<GATEUP, 8>(a, st, s_a);
-        else run_item<GATEUP, 2>(a, st, s_a);
+        if (mt == 4) run_item<GATEUP, 4>(a, st, s_a, s_ent, s_w);
+        else if (mt == 2) run_item<GATEUP, 2>(a, st, s_a, s_ent, s_w);
+        else run_item<GATEUP, 1>(a, st, s_a, s_ent, s_w);
     }
+    // The last workgroup out clears the queue counters for the next launch.
+    if (dev::arrive_last(a.queues + kGroupedQueues * kQueueStride, gridDim.x) && tid < kGroupedQueues)
+        dev::store_coherent(a.queues + tid * kQueueStride, 0);
 }
 
 // fp16 copy of the activations (the A operand of the gate/up GEMM).
@@ -335,8 +387,8 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a) {
     reinterpret_cast<float4 *>(a.y)[idx] = acc;
 }
 
-int grid_for(int items, int n_cu) {
-    int g = 2 * n_cu;
+int grid_for(int items, int slots) {
+    int g = slots;
     if (items < g) g = items;
     if (g >= 8) g &= ~7;
     return g < 1 ? 1 : g;
@@ -352,14 +404,12 @@ hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
-    const int grid = grid_for(max_chunks * (a.inter / 128), n_cu);
-    launch(grouped_kernel<true>, grid, 256, 0, s, a);
+    launch(grouped_kernel<true>, grid_for(max_chunks * (a.inter / 128), 2 * n_cu), 256, 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
-    const int grid = grid_for(max_chunks * ((a.hidden + 255) / 256), n_cu);
-    launch(grouped_kernel<false>, grid, 256, 0, s, a);
+    launch(grouped_kernel<false>, grid_for(max_chunks * ((a.hidden + 255) / 256), 2 * n_cu), 256, 0, s, a);
     return hipGetLastError();
 }
 

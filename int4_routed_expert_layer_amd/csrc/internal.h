@@ -73,6 +73,7 @@ struct FwdArgs {
     float *y;                       // [n_tok x H]
     const ChunkDesc *chunks;        // grouped path work list
     const int32_t *n_chunks;
+    int32_t *queues;                // grouped path: kQueueInts counters, zero at rest
     int skip_shared;                // gate/up: the shared unit was already done
 };
 
@@ -138,6 +139,12 @@ hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu,
                                hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
 hipError_t launch_to_half(const FwdArgs &a, hipStream_t s);
+
+// Grouped-path work queues: one counter per XCD (8), each on its own
+// 256-byte line, plus the exit count.
+constexpr int kGroupedQueues = 8;
+constexpr int kQueueStride = 64;
+constexpr int kQueueInts = (kGroupedQueues + 1) * kQueueStride;
 
 // Upper bound on grouped work chunks for n_tok tokens.
 int max_work_chunks(int n_tok, int k, int n_experts, int has_shared);
