@@ -165,7 +165,8 @@ coli_status coli_moe_router_logits(coli_layer *layer, const void *x,
  * counts [E] (tokens per expert); offsets [E+1] (exclusive prefix sum of
  * counts); gather [n_tok*k] (entries t*k+j ordered by expert id, then token).
  * Out-of-range ids are skipped and raise the layer's device error flag
- * (coli_layer_device_errors). */
+ * (coli_layer_device_errors).  Two launches that use the layer's scratch:
+ * calls on one layer must not overlap. */
 coli_status coli_moe_union(coli_layer *layer, const int32_t *topk_idx,
                            int32_t n_tok, int32_t *n_union, int32_t *union_ids,
                            int32_t *counts, int32_t *offsets, int32_t *gather,
@@ -223,7 +224,7 @@ coli_status coli_layer_device_errors(coli_layer *layer, int32_t *flags);
 typedef enum {
     COLI_K_ROUTER = 0,   /* router logits */
     COLI_K_TOPK = 1,     /* top-k and weights */
-    COLI_K_UNION = 2,    /* batch union */
+    COLI_K_UNION = 2,    /* batch union (2 launches: slab ranks, scatter) */
     COLI_K_PLAN = 3,     /* grouped work list; fp16 activations (2 launches) */
     COLI_K_GATEUP = 4,   /* gate/up + SwiGLU (GEMV or grouped) */
     COLI_K_DOWN = 5,     /* down projection x routing weight */

@@ -174,6 +174,8 @@ struct coli_layer {
     int32_t *err = nullptr;
     int32_t *sync_counters = nullptr;  // [1 + H/32] arrival counters, zero at rest
     int32_t *queues = nullptr;         // [kQueueInts] grouped work-queue counters, zero at rest
+    int32_t *union_blk = nullptr;      // [kUnionMaxBlocks x E + 64]; counter at [kUnionMaxBlocks x E]
+    int32_t *union_rank = nullptr;     // [max_tokens x k]
     uint8_t *pin_stage = nullptr;    // pinned staging for placement
 
     // tiered forward
@@ -393,7 +395,7 @@ void free_layer(coli_layer *L) {
     for (auto p : L->dev_tables) (void)hipFree(const_cast<uint8_t **>(p));
     if (L->side) (void)hipStreamDestroy(L->side);
     void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->xh, L->ys, L->chunks, L->n_chunks, L->err,
-                    L->sync_counters, L->queues};
+                    L->sync_counters, L->queues, L->union_blk, L->union_rank};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (L->pin_stage) (void)hipHostFree(L->pin_stage);
@@ -503,6 +505,8 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->err), sizeof(int32_t), "error flags"},
         {reinterpret_cast<void **>(&L->sync_counters), sizeof(int32_t) * (1 + H / 32), "arrival counters"},
         {reinterpret_cast<void **>(&L->queues), sizeof(int32_t) * kQueueInts, "work-queue counters"},
+        {reinterpret_cast<void **>(&L->union_blk), sizeof(int32_t) * (kUnionMaxBlocks * E + 64), "union slab counts"},
+        {reinterpret_cast<void **>(&L->union_rank), sizeof(int32_t) * T * dims->top_k, "union ranks"},
     };
     for (auto &a : allocs) {
         if ((he = hipMalloc(a.p, a.n)) != hipSuccess) {
@@ -516,6 +520,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         (he = hipMemset(L->err, 0, sizeof(int32_t))) != hipSuccess ||
         (he = hipMemset(L->sync_counters, 0, sizeof(int32_t) * (1 + H / 32))) != hipSuccess ||
         (he = hipMemset(L->queues, 0, sizeof(int32_t) * kQueueInts)) != hipSuccess ||
+        (he = hipMemset(L->union_blk, 0, sizeof(int32_t) * (kUnionMaxBlocks * E + 64))) != hipSuccess ||
         (he = hipMemset(L->bias, 0, sizeof(float) * E)) != hipSuccess ||
         (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_stage), L->lay.total, hipHostMallocDefault)) != hipSuccess ||
         (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_union), sizeof(int32_t) * (E + 1), hipHostMallocDefault)) != hipSuccess ||
@@ -650,10 +655,17 @@ coli_status coli_moe_union(coli_layer *L, const int32_t *topk_idx, int32_t n_tok
     if (!n_union || !union_ids || !counts || !offsets || (n_tok > 0 && (!topk_idx || !gather)))
         return fail(L, COLI_E_INVALID, "NULL device pointer");
     DeviceGuard guard(L->device);
-    KernelMark m(L, COLI_K_UNION, static_cast<hipStream_t>(stream));
-    HIP_TRY(L, launch_union(topk_idx, n_tok, L->d.top_k, L->d.n_experts, n_union, union_ids, counts, offsets,
-                            gather, L->err, static_cast<hipStream_t>(stream)),
-            "union launch");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const UnionScratch ws{L->union_blk, L->union_blk + kUnionMaxBlocks * L->d.n_experts, L->union_rank};
+    {
+        KernelMark m(L, COLI_K_UNION, s);
+        HIP_TRY(L, launch_union_rank(topk_idx, n_tok, L->d.top_k, L->d.n_experts, ws, n_union, union_ids, counts,
+                                     offsets, L->err, s),
+                "union launch");
+    }
+    KernelMark m(L, COLI_K_UNION, s);
+    HIP_TRY(L, launch_union_scatter(topk_idx, n_tok, L->d.top_k, L->d.n_experts, ws, offsets, gather, s),
+            "union scatter launch");
     return COLI_OK;
 }
 

@@ -106,10 +106,25 @@ hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
 hipError_t launch_topk(const float *logits, int n_tok, int n_experts, int k,
                        int32_t *idx, float *w, hipStream_t s);
 // union.hip
-hipError_t launch_union(const int32_t *idx, int n_tok, int k, int n_experts,
-                        int32_t *n_union, int32_t *union_ids, int32_t *counts,
-                        int32_t *offsets, int32_t *gather, int32_t *err,
-                        hipStream_t s);
+// The union runs in two launches (rank, then scatter) over slabs of entries;
+// UnionScratch is the layer's workspace for them: blk [kUnionMaxBlocks x E]
+// per-slab counts, counter (zero at rest) and rank [max_tokens * k].
+constexpr int kUnionMaxBlocks = 64;
+struct UnionScratch {
+    int32_t *blk;
+    int32_t *counter;
+    int32_t *rank;
+};
+struct UnionSplit {
+    int nb;    // workgroups (slabs)
+    int slab;  // entries per slab, a multiple of 256
+};
+UnionSplit union_split(int n_tok, int k);
+hipError_t launch_union_rank(const int32_t *idx, int n_tok, int k, int n_experts, UnionScratch ws,
+                             int32_t *n_union, int32_t *union_ids, int32_t *counts, int32_t *offsets,
+                             int32_t *err, hipStream_t s);
+hipError_t launch_union_scatter(const int32_t *idx, int n_tok, int k, int n_experts, UnionScratch ws,
+                                const int32_t *offsets, int32_t *gather, hipStream_t s);
 hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
                        hipStream_t s);
 // gemv.hip.  gate/up covers units [u_begin, u_begin + u_count) (u_count < 0:

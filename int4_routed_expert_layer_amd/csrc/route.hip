@@ -113,52 +113,64 @@ __global__ __launch_bounds__(64) void router_logits_kernel(
     }
 }
 
-// Top-k by rank counting: the rank of expert e is the number of experts
-// whose key (logit desc, id asc) comes first; e is selected iff rank < k and
-// lands in slot `rank`.  Keys are distinct, so ranks are a permutation.  One
-// 1024-thread block per token: thread (part, e) counts over one slice of the
-// experts, then the parts are summed.  -0 and +0 compare equal.
-__global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ logits,
-                                                    int n_tok, int n_experts, int k,
-                                                    int32_t *__restrict__ idx,
-                                                    float *__restrict__ w) {
-    __shared__ float s_l[kMaxExperts];
-    __shared__ int s_rank[kMaxExperts];
-    __shared__ float s_sig[kMaxTopK];
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int epad = (n_experts + 63) & ~63;
-    const int parts = 1024 / epad;           // >= 1 since n_experts <= 1024
-    const int span = (n_experts + parts - 1) / parts;
-    for (int e = tid; e < n_experts; e += 1024) {
-        s_l[e] = logits[static_cast<size_t>(t) * n_experts + e];
-        s_rank[e] = 0;
+// Top-k by repeated selection, one wave per token: lane l holds the keys of
+// experts l, l+64, ...; each of k rounds takes the largest remaining key
+// (logit descending, then expert id ascending) by a wave max and removes it,
+// so round r yields the expert of rank r.  A key is the order-preserving
+// unsigned image of the logit (-0 and +0 equal) in the high word and the
+// complemented id in the low word; 0 marks a removed or absent expert.  The
+// weights are sigmoid(logit) divided by the sum of the k sigmoids, added in
+// rank order.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+    const uint32_t b = __float_as_uint(f + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
+                                                   int n_tok, int n_experts, int k,
+                                                   int32_t *__restrict__ idx,
+                                                   float *__restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tok) return;  // uniform per wave
+    const float *row = logits + static_cast<size_t>(t) * n_experts;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        key[j] = e < n_experts
+                     ? (static_cast<uint64_t>(logit_key(row[e])) << 32) | (0xffffffffu - static_cast<uint32_t>(e))
+                     : 0ull;
     }
-    __syncthreads();
-    const int e = tid % epad, part = tid / epad;
-    if (e < n_experts && part < parts) {
-        const float v = s_l[e];
-        const int j0 = part * span, j1 = min(n_experts, j0 + span);
-        int r = 0;
-        for (int j = j0; j < j1; ++j) {
-            const float o = s_l[j];
-            r += (o > v || (o == v && j < e)) ? 1 : 0;
+    int my_e = 0;
+    float my_sig = 0.0f, sum = 0.0f;
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint64_t other = __shfl_xor(best, o, 64);
+            best = other > best ? other : best;
         }
-        atomicAdd(&s_rank[e], r);
-    }
-    __syncthreads();
-    if (tid < n_experts) {
-        const int r = s_rank[tid];
-        if (r < k) {
-            idx[static_cast<size_t>(t) * k + r] = tid;
-            s_sig[r] = 1.0f / (1.0f + expf(-s_l[tid]));
+        const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j == e) key[j] = 0ull;
+        const float sg = 1.0f / (1.0f + expf(-key_logit(static_cast<uint32_t>(best >> 32))));
+        sum = sum + sg;
+        if (lane == r) {
+            my_e = e;
+            my_sig = sg;
         }
     }
-    __syncthreads();
-    if (tid < k) {
-        float sum = 0.0f;
-        for (int j = 0; j < k; ++j) sum = sum + s_sig[j];
-        w[static_cast<size_t>(t) * k + tid] = s_sig[tid] / sum;
+    if (lane < k) {
+        idx[static_cast<size_t>(t) * k + lane] = my_e;
+        w[static_cast<size_t>(t) * k + lane] = my_sig / sum;
     }
 }
 
@@ -195,7 +207,17 @@ hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
 hipError_t launch_topk(const float *logits, int n_tok, int n_experts, int k,
                        int32_t *idx, float *w, hipStream_t s) {
     if (n_tok <= 0) return hipSuccess;
-    launch(topk_kernel, n_tok, 1024, 0, s, logits, n_tok, n_experts, k, idx, w);
+    const int blocks = (n_tok + 3) / 4;
+    if (n_experts <= 64)
+        launch(topk_kernel<1>, blocks, 256, 0, s, logits, n_tok, n_experts, k, idx, w);
+    else if (n_experts <= 128)
+        launch(topk_kernel<2>, blocks, 256, 0, s, logits, n_tok, n_experts, k, idx, w);
+    else if (n_experts <= 256)
+        launch(topk_kernel<4>, blocks, 256, 0, s, logits, n_tok, n_experts, k, idx, w);
+    else if (n_experts <= 512)
+        launch(topk_kernel<8>, blocks, 256, 0, s, logits, n_tok, n_experts, k, idx, w);
+    else
+        launch(topk_kernel<16>, blocks, 256, 0, s, logits, n_tok, n_experts, k, idx, w);
     return hipGetLastError();
 }
 

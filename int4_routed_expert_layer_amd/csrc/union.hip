@@ -8,13 +8,19 @@
 // (expert, token) -- a stable counting sort -- so each expert's tokens form
 // one contiguous run of rows for the expert FFNs.
 //
-// One block (256 threads for up to 256 experts, else 1024) does the whole
-// batch: an LDS histogram (integer atomics, order-free), two block scans
-// (offsets, compaction of the union), then the gather in chunks of one entry
-// per thread, where each entry's rank among
-// equal experts comes from wave ballots (match-any over the id bits) plus
-// per-wave counts in LDS.  Everything is integer, so results are exact and
-// independent of scheduling.
+// The batch's n = n_tok*k entries are cut into slabs of whole 256-entry
+// chunks, one workgroup per slab, in two launches:
+//  * rank: each workgroup gives every entry of its slab its stable rank among
+//    the slab's entries of the same expert (chunk by chunk: wave ballots
+//    matching the id bits give the rank inside a wave, per-wave counts in LDS
+//    the waves before it, a per-expert running base the chunks before it) and
+//    publishes its per-expert counts.  The last workgroup to finish sums the
+//    counts over slabs in slab order, which gives counts, offsets, the union
+//    and each slab's per-expert base.
+//  * scatter: entry i of expert e in slab b goes to
+//    gather[offsets[e] + base[b][e] + rank[i]].
+// Everything is integer and every sum has a fixed order or is order-free, so
+// the results are exact and independent of scheduling.
 #include "dev_common.h"
 
 namespace coli {
@@ -22,88 +28,113 @@ namespace {
 
 constexpr int kThreads = 1024;
 
-// NT threads handle up to NT experts.
-template <int NT>
-__global__ __launch_bounds__(NT) void union_kernel(
-    const int32_t *__restrict__ idx, int n_ent, int n_experts,
+constexpr int kUT = 256;                 // threads per union workgroup
+constexpr int kUWaves = kUT / 64;
+
+__global__ __launch_bounds__(kUT) void union_rank_kernel(
+    const int32_t *__restrict__ idx, int n_ent, int slab, int n_experts,
+    int32_t *__restrict__ rank_out, int32_t *__restrict__ blk, int32_t *__restrict__ counter,
     int32_t *__restrict__ n_union, int32_t *__restrict__ union_ids,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ gather, int32_t *__restrict__ err) {
-    constexpr int kThreads = NT;
-    constexpr int kWaves = NT / 64;
-    __shared__ int s_cnt[NT];
-    __shared__ int s_off[NT];
-    __shared__ int s_base[NT];
-    __shared__ unsigned short s_wc[kWaves][NT];
-    __shared__ int s_tmp[kWaves + 1];
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ err) {
+    __shared__ int s_base[kMaxExperts];
+    __shared__ unsigned short s_wc[kUWaves][kMaxExperts];
+    __shared__ int s_tmp[kUWaves + 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int E = n_experts, b = blockIdx.x, nb = gridDim.x;
 
-    s_cnt[tid] = 0;
-    s_base[tid] = 0;
+    for (int e = tid; e < E; e += kUT) {
+        s_base[e] = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s_wc[w][tid] = 0;
-    __syncthreads();
-
-    bool bad = false;
-    for (int i = tid; i < n_ent; i += kThreads) {
-        const int e = idx[i];
-        if (e >= 0 && e < n_experts)
-            atomicAdd(&s_cnt[e], 1);
-        else
-            bad = true;
+        for (int w = 0; w < kUWaves; ++w) s_wc[w][e] = 0;
     }
-    if (bad) atomicOr(err, 1);
     __syncthreads();
 
-    const int c = tid < n_experts ? s_cnt[tid] : 0;
-    int total = 0;
-    const int excl = dev::block_exclusive_scan<NT>(c, s_tmp, &total);
-    if (tid < n_experts) {
-        counts[tid] = c;
-        offsets[tid] = excl;
-        s_off[tid] = excl;
-    }
-    if (tid == 0) offsets[n_experts] = total;
-    const int flag = (tid < n_experts && c > 0) ? 1 : 0;
-    int nu = 0;
-    const int pos = dev::block_exclusive_scan<NT>(flag, s_tmp, &nu);
-    if (flag) union_ids[pos] = tid;
-    if (tid == 0) *n_union = nu;
-    __syncthreads();
-
+    const int i0 = b * slab, i1 = min(n_ent, i0 + slab);
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int c0 = 0; c0 < n_ent; c0 += kThreads) {
+    bool bad = false;
+    int nxt = i0 + tid < i1 ? idx[i0 + tid] : -1;
+    for (int c0 = i0; c0 < i1; c0 += kUT) {
         const int i = c0 + tid;
-        int e = i < n_ent ? idx[i] : -1;
-        if (e >= n_experts) e = -1;
+        int e = nxt;
+        nxt = i + kUT < i1 ? idx[i + kUT] : -1;
+        if (i < i1 && (e < 0 || e >= E)) bad = true;
+        if (e >= E) e = -1;
         uint64_t peers = __ballot(e >= 0);
 #pragma unroll
-        for (int b = 0; b < 10; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
+        for (int bit = 0; bit < 10; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
         }
-        const int rank = __popcll(peers & lt_mask);
-        if (e >= 0 && rank == 0) s_wc[wave][e] = static_cast<unsigned short>(__popcll(peers));
+        const int r = __popcll(peers & lt_mask);
+        const bool leader = e >= 0 && r == 0;
+        const int cnt = __popcll(peers);
+        if (leader) s_wc[wave][e] = static_cast<unsigned short>(cnt);
         __syncthreads();
         if (e >= 0) {
             int before = 0;
             for (int w = 0; w < wave; ++w) before += s_wc[w][e];
-            gather[s_off[e] + s_base[e] + before + rank] = i;
+            rank_out[i] = s_base[e] + before + r;
         }
         __syncthreads();
-        if (tid < n_experts) {
-            int tot = 0;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                tot += s_wc[w][tid];
-                s_wc[w][tid] = 0;
-            }
-            s_base[tid] += tot;
+        if (leader) {
+            atomicAdd(&s_base[e], cnt);  // integer adds: order-free
+            s_wc[wave][e] = 0;
         }
         __syncthreads();
     }
+    if (bad) atomicOr(err, 1);
+    for (int e = tid; e < E; e += kUT) dev::store_coherent(&blk[b * E + e], s_base[e]);
+    if (!dev::arrive_last(counter, nb)) return;
+
+    // Last workgroup: per-expert sums over slabs in slab order (blk becomes
+    // each slab's exclusive base), then offsets and the union over experts.
+    int carry_off = 0, carry_u = 0;
+    for (int e0 = 0; e0 < E; e0 += kUT) {
+        const int e = e0 + tid;
+        int c = 0;
+        if (e < E) {
+            for (int q0 = 0; q0 < nb; q0 += 16) {
+                int v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    v[j] = q0 + j < nb ? dev::load_coherent(&blk[(q0 + j) * E + e]) : 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (q0 + j < nb) blk[(q0 + j) * E + e] = c;
+                    c += v[j];
+                }
+            }
+        }
+        int tot = 0;
+        const int ex = dev::block_exclusive_scan<kUT>(c, s_tmp, &tot);
+        if (e < E) {
+            counts[e] = c;
+            offsets[e] = carry_off + ex;
+        }
+        carry_off += tot;
+        const int f = (e < E && c > 0) ? 1 : 0;
+        int nu = 0;
+        const int pos = dev::block_exclusive_scan<kUT>(f, s_tmp, &nu);
+        if (f) union_ids[carry_u + pos] = e;
+        carry_u += nu;
+    }
+    if (tid == 0) {
+        offsets[E] = carry_off;
+        *n_union = carry_u;
+    }
+}
+
+__global__ __launch_bounds__(kUT) void union_scatter_kernel(
+    const int32_t *__restrict__ idx, int n_ent, int slab, int n_experts,
+    const int32_t *__restrict__ rank, const int32_t *__restrict__ blk,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ gather) {
+    const int i = blockIdx.x * kUT + threadIdx.x;
+    if (i >= n_ent) return;
+    const int e = idx[i];
+    if (e < 0 || e >= n_experts) return;
+    gather[offsets[e] + blk[(i / slab) * n_experts + e] + rank[i]] = i;
 }
 
 // Work chunks for the grouped GEMMs: each union expert (and the shared
@@ -140,16 +171,32 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(FwdArgs a,
 
 }  // namespace
 
-hipError_t launch_union(const int32_t *idx, int n_tok, int k, int n_experts,
-                        int32_t *n_union, int32_t *union_ids, int32_t *counts,
-                        int32_t *offsets, int32_t *gather, int32_t *err,
-                        hipStream_t s) {
-    if (n_experts <= 256)
-        launch(union_kernel<256>, 1, 256, 0, s, idx, n_tok * k, n_experts, n_union, union_ids,
-                                            counts, offsets, gather, err);
-    else
-        launch(union_kernel<1024>, 1, 1024, 0, s, idx, n_tok * k, n_experts, n_union, union_ids,
-                                              counts, offsets, gather, err);
+UnionSplit union_split(int n_tok, int k) {
+    const int n = n_tok * k;
+    const int per = (n + kUnionMaxBlocks - 1) / kUnionMaxBlocks;
+    UnionSplit u;
+    u.slab = ((per + kUT - 1) / kUT) * kUT;
+    if (u.slab < kUT) u.slab = kUT;
+    u.nb = n > 0 ? (n + u.slab - 1) / u.slab : 1;
+    return u;
+}
+
+hipError_t launch_union_rank(const int32_t *idx, int n_tok, int k, int n_experts, UnionScratch ws,
+                             int32_t *n_union, int32_t *union_ids, int32_t *counts, int32_t *offsets,
+                             int32_t *err, hipStream_t s) {
+    const UnionSplit u = union_split(n_tok, k);
+    launch(union_rank_kernel, u.nb, kUT, 0, s, idx, n_tok * k, u.slab, n_experts, ws.rank, ws.blk,
+           ws.counter, n_union, union_ids, counts, offsets, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_union_scatter(const int32_t *idx, int n_tok, int k, int n_experts, UnionScratch ws,
+                                const int32_t *offsets, int32_t *gather, hipStream_t s) {
+    const int n = n_tok * k;
+    if (n == 0) return hipSuccess;
+    const UnionSplit u = union_split(n_tok, k);
+    launch(union_scatter_kernel, (n + kUT - 1) / kUT, kUT, 0, s, idx, n, u.slab, n_experts, ws.rank,
+           ws.blk, offsets, gather);
     return hipGetLastError();
 }
 
