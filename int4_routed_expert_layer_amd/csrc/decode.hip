@@ -103,7 +103,10 @@ __device__ void select_and_union(const FwdArgs &a, const FrontArgs &f) {
             for (int j = 0; j < 4 * k; ++j) R += s_fin[j] > fk ? 1 : 0;
             if (R < k) {
                 const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(fk));
-                const float l = dev::load_coherent(f.logits + static_cast<size_t>(t) * E + e);
+                // The key's high word is the order-preserving image of the
+                // logit (-0 folded to +0, which has the same sigmoid).
+                const uint32_t kh = static_cast<uint32_t>(fk >> 32);
+                const float l = __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
                 s_idx[t * k + R] = e;
                 f.topk_idx[static_cast<size_t>(t) * k + R] = e;
                 s_sig[R] = 1.0f / (1.0f + expf(-l));

@@ -169,14 +169,6 @@ __device__ __forceinline__ void store_coherent(_Float16 *p, _Float16 v) {
     __hip_atomic_store(reinterpret_cast<uint16_t *>(p), __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16 bytes as two coherent 8-byte loads.
-__device__ __forceinline__ uint4 load_coherent_16B(const void *p) {
-    uint64_t *q = const_cast<uint64_t *>(static_cast<const uint64_t *>(p));
-    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_uint4(static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32), static_cast<uint32_t>(hi),
-                      static_cast<uint32_t>(hi >> 32));
-}
 
 // Returns true in exactly one workgroup: the last of `expected` workgroups
 // to arrive at `counter` (which it resets to 0 for the next launch).  The

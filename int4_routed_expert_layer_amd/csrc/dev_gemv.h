@@ -295,8 +295,8 @@ __device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, c
 // hidden rows r0..r0+M-1.  Wave w takes panel 2pg + (w & 1) and reduction
 // half (w >> 1); the halves are summed through LDS in a fixed order.  Writes
 // ys row rows.entry(row) scaled by rows.weight(row) (the routing weight of a
-// routed row, 1 for a shared row).  With COHERENT, h is read and ys written
-// device-coherently (producer and consumer in the same launch); before_h()
+// routed row, 1 for a shared row).  With COHERENT, ys is written
+// device-coherently (a consumer in the same launch reads it); before_h()
 // runs, by all threads, after the first weight loads are issued and before h
 // is read (a wait for h's producers).  All 256 threads must call it.
 template <int MAXM, bool COHERENT = false, class Rows, class BeforeH>
@@ -331,7 +331,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
         for (int i = tid; i < mc * (I / 8); i += 256) {
             const int m = i / (I / 8), q = i % (I / 8);
             const _Float16 *src = a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q;
-            const uint4 raw = COHERENT ? load_coherent_16B(src) : gload<uint4>(src);
+            const uint4 raw = gload<uint4>(src);     // h comes from an earlier launch
             const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
             float v[8];
 #pragma unroll
@@ -374,16 +374,44 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
 
 // y rows for output panels 2pg, 2pg+1: per token, its k routed rows in slot
 // order, then the shared row.  Same order as the standalone combine kernel.
-// The rows were written by other workgroups with store_coherent.
-__device__ __forceinline__ void combine_panelgroup(const FwdArgs &a, int pg) {
-    const int H = a.hidden;
-    const int n = a.n_tok * 2 * kPanel;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int t = i / (2 * kPanel), col = 2 * kPanel * pg + i % (2 * kPanel);
-        float acc = load_coherent(a.ys + static_cast<size_t>(t * a.k) * H + col);
-        for (int j = 1; j < a.k; ++j) acc = acc + load_coherent(a.ys + static_cast<size_t>(t * a.k + j) * H + col);
-        if (a.has_shared) acc = acc + load_coherent(a.ys + static_cast<size_t>(a.n_tok * a.k + t) * H + col);
-        a.y[static_cast<size_t>(t) * H + col] = acc;
+// The rows were written by other workgroups with store_coherent.  All rows
+// of as many tokens as fit in `cap` floats of LDS are loaded at once (two
+// loads in flight per thread), so the tail costs about one memory round trip
+// per pass instead of one per row.  All threads of the workgroup must call it.
+__device__ __forceinline__ void combine_panelgroup(const FwdArgs &a, int pg, float *lds, int cap) {
+    const int H = a.hidden, k = a.k;
+    const int nrows = k + (a.has_shared ? 1 : 0);
+    const int per_tok = 2 * kPanel * nrows;
+    const int tpp = cap / per_tok > 0 ? cap / per_tok : 1;
+    const int col0 = 2 * kPanel * pg;
+    const int tid = threadIdx.x;
+    auto src = [&](int t0, int i) {
+        // item i of a pass: token t0 + i / per_tok, row j, column c
+        const int tt = i / per_tok, rem = i % per_tok;
+        const int j = rem / (2 * kPanel), c = rem % (2 * kPanel);
+        const int t = t0 + tt;
+        const int row = j < k ? t * k + j : a.n_tok * k + t;
+        return a.ys + static_cast<size_t>(row) * H + col0 + c;
+    };
+    for (int t0 = 0; t0 < a.n_tok; t0 += tpp) {
+        const int nt = min(tpp, a.n_tok - t0);
+        const int n = nt * per_tok;
+        for (int i = tid; i < n; i += 2 * blockDim.x) {
+            const int i2 = i + static_cast<int>(blockDim.x);
+            const float v0 = load_coherent(src(t0, i));
+            const float v1 = i2 < n ? load_coherent(src(t0, i2)) : 0.0f;
+            lds[i] = v0;
+            if (i2 < n) lds[i2] = v1;
+        }
+        __syncthreads();
+        for (int i = tid; i < nt * 2 * kPanel; i += blockDim.x) {
+            const int tt = i / (2 * kPanel), c = i % (2 * kPanel);
+            const float *r = lds + tt * per_tok + c;
+            float acc = r[0];
+            for (int j = 1; j < nrows; ++j) acc = acc + r[j * 2 * kPanel];
+            a.y[static_cast<size_t>(t0 + tt) * H + col0 + c] = acc;
+        }
+        __syncthreads();
     }
 }
 

@@ -36,7 +36,10 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
         dev::down_panelgroup<MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::NoWait{});
     if (FUSED_COMBINE) {
         const int units = *a.n_union + (a.has_shared ? 1 : 0);
-        if (dev::arrive_last(counters + pg, units)) dev::combine_panelgroup(a, pg);
+        // The last workgroup of the panel pair reuses its (now idle) LDS.
+        if (dev::arrive_last(counters + pg, units))
+            dev::combine_panelgroup(a, pg, reinterpret_cast<float *>(lds),
+                                    static_cast<int>(dev::down_lds_bytes(MAXM, a.inter) / sizeof(float)));
     }
 }
 
