@@ -7,16 +7,18 @@
 // with N-blocks; a persistent grid walks that list (consecutive items, which
 // share the same activation rows, land on the same XCD and its L2).
 //
-// Per item a 256-thread workgroup copies the chunk's fp16 activation rows for
-// 128 reduction columns at a time straight from global memory into LDS
-// (global_load_lds, double-buffered: the next 128 columns are in flight while
-// the current ones are multiplied; XOR-swizzled 16-byte units, conflict-free
-// for the fragment reads), while each wave streams its own int4 weight
-// panels from HBM (prefetched one step ahead): one 16-byte load per lane per
-// 1 KB chunk, already in B-fragment order of v_mfma_f32_16x16x32_f16.  Each
-// dword is turned into eight fp16 weights in registers: q = (1024 + u) -
-// 1032 (exact) times the group's fp16 scale (one rounding), so a fragment
-// covers exactly one 32-wide scale group and the MFMA accumulates in fp32.
+// Per item a 256-thread workgroup (two per CU) walks the reduction axis in
+// 64-column steps through a ring of four LDS stages: the chunk's fp16
+// activation rows of step c + 3 are copied straight from global memory into
+// LDS (global_load_lds; XOR-swizzled 16-byte units, conflict-free for the
+// fragment reads) and each wave's int4 weight fragments of step c + 3 are
+// loaded into registers (buffer loads, already in B-fragment order of
+// v_mfma_f32_32x32x16_f16) while step c is multiplied.  Inside a step the LDS
+// reads and the dequantisation of the next 16-column slice are interleaved
+// between the MFMAs of the current one.  Each weight dword becomes eight fp16
+// weights: q = (1024 + u) - 1032 (exact) times the group's fp16 scale (one
+// rounding), so a fragment covers exactly one 32-wide scale group and the
+// MFMA accumulates in fp32.
 //   gate/up: A = gathered token rows (fp16 copy of x); each wave owns
 //            32 intermediate rows of both gate and up, so SwiGLU is applied
 //            in registers and h is stored as fp16.
@@ -36,7 +38,14 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRowBytes = kChunkK * 2;     // one staged row: 128 fp16
+// The K loop advances 64 reduction columns per step through a ring of eight
+// LDS stages (one workgroup per CU): the activation copy and the weight loads
+// of step c + 6 are issued while step c is multiplied.
+constexpr int kStepK = 64;
+constexpr int kStageRowBytes = kStepK * 2;                  // one staged row: 64 fp16
+constexpr int kStages = 4;
+constexpr int kAhead = 3;                                   // steps issued ahead
+constexpr int kStageBytes = kChunkRows * kStageRowBytes;   // 16 KB
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
@@ -76,75 +85,96 @@ __device__ __forceinline__ half2v scale_pair(uint2 sc, int s) {
     return half2v{f, f};
 }
 
+// Byte offset of logical 16-byte unit q (0..7) of staged row m.  A fragment
+// read has 16 consecutive lanes read 16 bytes each from rows m..m+15 at the
+// same logical unit; with 64 four-byte banks a 128-byte row spans half of
+// them, so the physical unit is q ^ ((m >> 1) & 7): the 16 rows then cover
+// all 64 banks once.
+__device__ __forceinline__ int lds_swz(int m) { return (m >> 1) & 7; }
 __device__ __forceinline__ int lds_unit(int m, int q) {
-    return m * kRowBytes + ((q ^ (m & 15)) << 4);
+    return m * kStageRowBytes + ((q ^ lds_swz(m)) << 4);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at
-// lds_base + 16 L (lds_base must be wave-uniform).
-__device__ __forceinline__ void copy16_to_lds(const void *src, uint8_t *lds_base) {
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(src),
-                                     (void __attribute__((address_space(3))) *)(lds_base), 16, 0, 0);
+// LDS byte address lds_addr + 16 L (lds_addr wave-uniform; it goes to M0).
+// Written as inline asm so that the compiler's wait insertion does not see an
+// LDS write in flight: it would otherwise make every LDS read wait for all
+// copies, including the lookahead stages.  The caller waits for a stage's
+// copies explicitly (s_waitcnt vmcnt) before reading it; the copy has no
+// output register, and its address operands are consumed at issue.
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
 }
 
-struct BFrag {
-    uint4 q[4];
-    uint2 s[4];
-};
+// Scheduling groups for one slice: N times (one MFMA, on odd turns one LDS
+// read, V VALU instructions), so the reads and dequantisation of the next
+// slice issue between the MFMAs of this one.
+template <int I, int N, int V>
+__device__ __forceinline__ void interleave() {
+    if constexpr (I < N) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (I & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+        interleave<I + 1, N, V>();
+    }
+}
 
 // State of one work item (chunk x N-block) shared by its K loop and
 // epilogue.
 struct ItemState {
     const _Float16 *asrc;
-    uint32_t src_off[2][4];      // A rows staged by this wave (fp16 elements, column 0)
-    int my_groups;
+    uint32_t src_off[4];         // this wave's copy j (< MT): lane's source (fp16 elements, column 0)
     dev::rsrc_t brs;             // weight blob
     uint32_t qv_even, qv_odd, sv; // per-lane byte offsets of the B slots and scales
     uint32_t qoff[2], soff[2];   // this wave's two 32-row B tiles (uniform)
     bool bvalid[2];
-    int row0, rows, nb, C;
+    int row0, rows, nb, C2;      // C2 = K / kStepK steps
 };
 
 // K loop and epilogue of one item on v_mfma_f32_32x32x16_f16 with MT 32-row
 // tiles of the chunk (rows past `rows` are padding, computed and discarded).
 //
 // B tile nt covers 32 weight rows = two 16-row panels.  For the 16-wide K
-// slice t of a 128-wide chunk, lane L needs rows n = L % 32, columns
-// 16t + 8(L / 32) + 0..7: in the device layout those are dword t / 2 of the
-// 16-byte slot (n % 16) + 16 (L / 32) (t even) or (n % 16) + 16 (2 + L / 32)
-// (t odd) of panel n / 16, so each lane loads two 16-byte slots per tile and
-// step and every byte is used once.  The A fragment of slice t is the 16-byte
-// unit 2t + L / 32 of row L % 32 in the staged tile.
+// slice T of a 128-wide chunk, lane L needs rows n = L % 32, columns
+// 16T + 8(L / 32) + 0..7: in the device layout those are dword T / 2 of the
+// 16-byte slot (n % 16) + 16 (L / 32) (T even) or (n % 16) + 16 (2 + L / 32)
+// (T odd) of panel n / 16, so a 64-column step (half h of a chunk) takes the
+// 8 bytes at 8h of each of the two slots, plus the dword of its two scales.
+// The A fragment of slice t of a step is the 16-byte unit 2t + L / 32 of row
+// L % 32 of the staged tile.
+//
+// Step c waits for its own copies with an explicit count: after them this
+// wave has issued exactly the B loads of step c (6) and the copies (MT) and B
+// loads (6) of steps c + 1 .. c + kAhead - 1.  Lookahead past the last step repeats
+// the last step's addresses (never used), so that count holds at every step;
+// the loop ends with a full wait before the stages are reused.
 template <bool GATEUP, int MT>
-__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, uint8_t (*s_a)[kChunkRows * kRowBytes],
-                                         const int *s_ent, const float *s_w) {
+__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, uint8_t (*s_a)[kStageBytes],
+                                         uint32_t sa_lds, const int *s_ent, const float *s_w) {
     const int H = a.hidden, I = a.inter;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = dev::wave_id(), lane = threadIdx.x & 63;
     const int l31 = lane & 31, lh = lane >> 5;
-    const int routed = a.n_tok * a.k;
-    auto stage = [&](int c, int buf) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            if (g < st.my_groups) {
-                const int grp = wave + 4 * g;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    copy16_to_lds(st.asrc + st.src_off[g][i] + c * kChunkK, &s_a[buf][(grp * 16 + i * 4) * kRowBytes]);
-            }
-        }
+    struct B64 {
+        uint2 qe[2], qo[2];
+        uint32_t sc[2];
     };
-    struct B32 {
-        uint4 qe[2], qo[2];
-        uint2 sc[2];
-    };
-    auto load_b = [&](int c, B32 &f) {
+    auto issue = [&](int c, B64 &f) {
+        const int cc = min(c, st.C2 - 1);
+        const uint32_t dst = sa_lds + static_cast<uint32_t>(c & (kStages - 1)) * kStageBytes;
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            copy16_to_lds(st.asrc + st.src_off[j] + cc * kStepK,
+                          dst + static_cast<uint32_t>(8 * (wave + 4 * j) * kStageRowBytes));
+        asm volatile("" ::: "memory");
+        const uint32_t ch = static_cast<uint32_t>(cc >> 1), h = static_cast<uint32_t>(cc & 1);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const uint32_t cq = st.qoff[nt] + static_cast<uint32_t>(c) * kChunkBytes;
-            f.qe[nt] = dev::bload<uint4>(st.brs, st.qv_even, cq);
-            f.qo[nt] = dev::bload<uint4>(st.brs, st.qv_odd, cq);
-            f.sc[nt] = dev::bload<uint2>(st.brs, st.sv, st.soff[nt] + static_cast<uint32_t>(c) * kScaleChunkBytes);
+            const uint32_t cq = st.qoff[nt] + ch * kChunkBytes + 8 * h;
+            f.qe[nt] = dev::bload<uint2>(st.brs, st.qv_even, cq);
+            f.qo[nt] = dev::bload<uint2>(st.brs, st.qv_odd, cq);
+            f.sc[nt] = dev::bload<uint32_t>(st.brs, st.sv, st.soff[nt] + ch * kScaleChunkBytes + 4 * h);
         }
+        asm volatile("" ::: "memory");
     };
 
     floatx16 acc[MT][2];
@@ -157,51 +187,74 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
 
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
 
-    B32 bn, bc;
-    stage(0, 0);
-    load_b(0, bn);
-    for (int c = 0; c < st.C; ++c) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        bc = bn;
-        if (c + 1 < st.C) {
-            stage(c + 1, (c + 1) & 1);
-            load_b(c + 1, bn);
-        }
-        const uint8_t *tile = s_a[c & 1];
-        // A fragments are read one slice ahead so LDS latency overlaps the
-        // MFMAs of the current slice.
-        half8 av[MT];
+    // B fragment of slice t (0..3) of a step: dword t / 2 of the even or odd
+    // slot half, times the scale of group t / 2.
+    auto bfrag = [&](const B64 &f, int t, int nt) {
+        const uint2 &q = (t & 1) ? f.qo[nt] : f.qe[nt];
+        const uint32_t w = (t >> 1) ? q.y : q.x;
+        const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(f.sc[nt] >> (16 * (t >> 1))));
+        return dequant8(w, half2v{sh, sh}, M0, M1, G);
+    };
+    // Software pipeline over the four slices of a step: the A fragments and
+    // dequantised B fragments of slice t + 1 are produced before the MFMAs of
+    // slice t are issued (the scheduling barriers keep that order), so LDS
+    // latency and dequantisation overlap the matrix pipe.
+    auto compute = [&](int c, const B64 &f) {
+        if (c >= st.C2) return;
+        const uint8_t *tile = s_a[c & (kStages - 1)];
+        half8 av[MT], bc[2];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             av[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, lh));
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            half8 an[MT];
-            if (t + 1 < 8) {
+        for (int nt = 0; nt < 2; ++nt) bc[nt] = bfrag(f, 0, nt);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            half8 an[MT], bn[2];
+            if (t + 1 < 4) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     an[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, 2 * (t + 1) + lh));
-            }
-            half8 bf[2];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const uint4 &q = (t & 1) ? bc.qo[nt] : bc.qe[nt];
-                const int s2 = t >> 1;
-                const uint32_t w = s2 == 0 ? q.x : s2 == 1 ? q.y : s2 == 2 ? q.z : q.w;
-                bf[nt] = dequant8(w, scale_pair(bc.sc[nt], s2), M0, M1, G);
+                for (int nt = 0; nt < 2; ++nt) bn[nt] = bfrag(f, t + 1, nt);
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bf[nt], acc[mt][nt], 0, 0, 0);
-            if (t + 1 < 8) {
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bc[nt], acc[mt][nt], 0, 0, 0);
+            // Interleave: after each MFMA of slice t, a share of the LDS reads
+            // and dequantisation of slice t + 1, which then execute while the
+            // MFMA occupies the matrix pipe.
+            interleave<0, 2 * MT, 26 / (2 * MT) + 1>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < 4) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) av[mt] = an[mt];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) bc[nt] = bn[nt];
             }
         }
+    };
+    auto step = [&](int c, const B64 &cur, B64 &ahead) {
+        // A plain barrier, not __syncthreads: its release fence would wait
+        // for every load in flight, which is the lookahead itself.  LDS reads
+        // of the previous step are complete (lgkmcnt) before any wave passes.
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(6 + (kAhead - 1) * (MT + 6)) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(c + kAhead, ahead);
+        compute(c, cur);
+    };
+
+    B64 b[kStages];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) issue(i, b[i]);
+    for (int c = 0; c < st.C2; c += kStages) {
+#pragma unroll
+        for (int i = 0; i < kStages; ++i) step(c + i, b[i], b[(i + kAhead) & (kStages - 1)]);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue.  Lane holds D[m = 8(i / 4) + 4(L / 32) + i % 4][n = L % 32]
     // of each 32x32 tile.
@@ -234,16 +287,18 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
-    // Two A tiles (double buffer): kChunkRows rows x 128 fp16 each.
-    __shared__ __align__(16) uint8_t s_a[2][kChunkRows * kRowBytes];
+    // Ring of A stages: kChunkRows rows x kStepK fp16 each.
+    __shared__ __align__(16) uint8_t s_a[kStages][kStageBytes];
+    // LDS byte address of s_a (for the copies' M0).
+    const uint32_t sa_lds = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)(&s_a[0][0])));
     __shared__ int s_tok[kChunkRows];
     __shared__ int s_ent[GATEUP ? 1 : kChunkRows];     // down: output entry and routing weight per row
     __shared__ float s_w[GATEUP ? 1 : kChunkRows];
     const int H = a.hidden, I = a.inter;
     const int K = GATEUP ? H : I;
     const int NB = GATEUP ? I / 128 : (H + 255) / 256;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int l15 = lane & 15, l4 = lane >> 4;
+    const int tid = threadIdx.x, wave = dev::wave_id(), lane = tid & 63;
     const int l31 = lane & 31, lh = lane >> 5;
     const int routed = a.n_tok * a.k;
 
@@ -264,30 +319,43 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         __syncthreads();       // every thread has read the previous s_item
         if (tid == 0) s_item = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        const int j = s_item;
+        // Uniform across the workgroup: everything derived from it (chunk,
+        // blob, descriptor, offsets) then lives in scalar registers.
+        const int j = __builtin_amdgcn_readfirstlane(s_item);
         if (j >= q_items) break;
         const int item = (q + nq * (j / NB)) * NB + j % NB;
         const int chunk = item / NB, nb = item % NB;
-        const ChunkDesc d = a.chunks[chunk];
-        const uint8_t *blob = a.table[d.expert];
+        // The chunk descriptor and the blob pointer are read by every lane
+        // from one address; readfirstlane makes them scalar, so the weight
+        // descriptor built from them is known to be uniform (a per-lane
+        // descriptor would turn every buffer load into a loop over lanes).
+        ChunkDesc d = a.chunks[chunk];
+        d.expert = __builtin_amdgcn_readfirstlane(d.expert);
+        d.row0 = __builtin_amdgcn_readfirstlane(d.row0);
+        d.rows = __builtin_amdgcn_readfirstlane(d.rows);
+        const uint64_t braw = reinterpret_cast<uint64_t>(a.table[d.expert]);
+        const uint64_t bl = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(braw)));
+        const uint64_t bh = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(braw >> 32)));
+        const uint8_t *blob = reinterpret_cast<const uint8_t *>(bl | (bh << 32));
         if (!blob) continue;
         ItemState st;
         st.asrc = GATEUP ? a.xh : a.h;
         st.row0 = d.row0;
         st.rows = d.rows;
         st.nb = nb;
-        st.C = K / kChunkK;
+        st.C2 = K / kStepK;
+        const int C = K / kChunkK;
         // 32-row tiles: 1, 2 or 4 (padding rows are computed and discarded).
         const int mt = d.rows > 64 ? 4 : (d.rows > 32 ? 2 : 1);
 
         // This wave's two 32-row B tiles (two 16-row panels each), as
         // uniform offsets, and the per-lane slot offsets inside them.
         st.brs = dev::make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
-        const uint32_t pstep = static_cast<uint32_t>(st.C) * kChunkBytes;   // bytes per panel
+        const uint32_t pstep = static_cast<uint32_t>(C) * kChunkBytes;   // bytes per panel
         const uint32_t r16 = static_cast<uint32_t>(l31 & 15), hi = static_cast<uint32_t>(l31 >> 4);
         st.qv_even = hi * pstep + 16 * (r16 + 16 * static_cast<uint32_t>(lh));
         st.qv_odd = hi * pstep + 16 * (r16 + 16 * (2 + static_cast<uint32_t>(lh)));
-        st.sv = hi * static_cast<uint32_t>(st.C) * kScaleChunkBytes + r16 * 8;
+        st.sv = hi * static_cast<uint32_t>(C) * kScaleChunkBytes + r16 * 8;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             int panel;
@@ -304,8 +372,8 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
                 st.bvalid[nt] = panel + 1 < H / kPanel;
                 if (!st.bvalid[nt]) panel = 0;
             }
-            st.qoff[nt] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * st.C * kChunkBytes);
-            st.soff[nt] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * st.C * kScaleChunkBytes);
+            st.qoff[nt] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * C * kChunkBytes);
+            st.soff[nt] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * C * kScaleChunkBytes);
         }
 
         __syncthreads();   // previous item is done with s_tok and the A tiles
@@ -321,23 +389,19 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
             }
         }
         __syncthreads();
-        // This wave stages 16-row groups wave, wave+4 of the first mt*32
-        // rows: one copy16 per 4 rows, swizzled on the source side so that
-        // lane L fills slot (L & 15) of row (L >> 4).
+        // Copy j of this wave stages rows 8 (wave + 4j) .. +7 (MT copies per
+        // wave cover the first mt*32 rows): lane L fills LDS unit L & 7 of row
+        // m = 8 (wave + 4j) + L / 8 with logical unit (L & 7) ^ lds_swz(m).
         const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
-        const int ng = 2 * mt;
-        st.my_groups = ng > wave ? (ng - wave + 3) / 4 : 0;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = (wave + 4 * g) * 16 + i * 4 + l4;
-                const int q = l15 ^ (m & 15);
-                st.src_off[g][i] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
-            }
-        if (mt == 4) run_item<GATEUP, 4>(a, st, s_a, s_ent, s_w);
-        else if (mt == 2) run_item<GATEUP, 2>(a, st, s_a, s_ent, s_w);
-        else run_item<GATEUP, 1>(a, st, s_a, s_ent, s_w);
+        for (int j = 0; j < 4; ++j) {
+            const int m = 8 * (wave + 4 * j) + (lane >> 3);
+            const int q = (lane & 7) ^ lds_swz(m);
+            st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
+        }
+        if (mt == 4) run_item<GATEUP, 4>(a, st, s_a, sa_lds, s_ent, s_w);
+        else if (mt == 2) run_item<GATEUP, 2>(a, st, s_a, sa_lds, s_ent, s_w);
+        else run_item<GATEUP, 1>(a, st, s_a, sa_lds, s_ent, s_w);
     }
     // The last workgroup out clears the queue counters for the next launch.
     if (dev::arrive_last(a.queues + kGroupedQueues * kQueueStride, gridDim.x) && tid < kGroupedQueues)
