@@ -38,14 +38,14 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// The K loop advances 64 reduction columns per step through a ring of eight
-// LDS stages (one workgroup per CU): the activation copy and the weight loads
-// of step c + 6 are issued while step c is multiplied.
+// The K loop advances 64 reduction columns per step through a ring of three
+// LDS stages of kChunkRows rows (two workgroups per CU): the activation copy
+// and the weight loads of step c + 2 are issued while step c is multiplied.
 constexpr int kStepK = 64;
 constexpr int kStageRowBytes = kStepK * 2;                  // one staged row: 64 fp16
-constexpr int kStages = 4;
-constexpr int kAhead = 3;                                   // steps issued ahead
-constexpr int kStageBytes = kChunkRows * kStageRowBytes;   // 16 KB
+constexpr int kStages = 3;
+constexpr int kAhead = 2;                                   // steps issued ahead
+constexpr int kStageBytes = kChunkRows * kStageRowBytes;   // 20 KB
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
@@ -123,7 +123,7 @@ __device__ __forceinline__ void interleave() {
 // epilogue.
 struct ItemState {
     const _Float16 *asrc;
-    uint32_t src_off[4];         // this wave's copy j (< MT): lane's source (fp16 elements, column 0)
+    uint32_t src_off[5];         // this wave's copy j (< MT): lane's source (fp16 elements, column 0)
     dev::rsrc_t brs;             // weight blob
     uint32_t qv_even, qv_odd, sv; // per-lane byte offsets of the B slots and scales
     uint32_t qoff[2], soff[2];   // this wave's two 32-row B tiles (uniform)
@@ -145,11 +145,12 @@ struct ItemState {
 //
 // Step c waits for its own copies with an explicit count: after them this
 // wave has issued exactly the B loads of step c (6) and the copies (MT) and B
-// loads (6) of steps c + 1 .. c + kAhead - 1.  Lookahead past the last step repeats
-// the last step's addresses (never used), so that count holds at every step;
-// the loop ends with a full wait before the stages are reused.
+// loads (6) of steps c + 1 .. c + kAhead - 1 (other memory operations only
+// make that wait stricter).  Lookahead past the last step repeats the last
+// step's addresses (never used), so that count holds at every step; the loop
+// ends with a full wait before the stages are reused.
 template <bool GATEUP, int MT>
-__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, uint8_t (*s_a)[kStageBytes],
+__device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, const uint8_t *s_a,
                                          uint32_t sa_lds, const int *s_ent, const float *s_w) {
     const int H = a.hidden, I = a.inter;
     const int wave = dev::wave_id(), lane = threadIdx.x & 63;
@@ -160,7 +161,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     };
     auto issue = [&](int c, B64 &f) {
         const int cc = min(c, st.C2 - 1);
-        const uint32_t dst = sa_lds + static_cast<uint32_t>(c & (kStages - 1)) * kStageBytes;
+        const uint32_t dst = sa_lds + static_cast<uint32_t>(c % kStages) * kStageBytes;
 #pragma unroll
         for (int j = 0; j < MT; ++j)
             copy16_to_lds(st.asrc + st.src_off[j] + cc * kStepK,
@@ -201,7 +202,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     // latency and dequantisation overlap the matrix pipe.
     auto compute = [&](int c, const B64 &f) {
         if (c >= st.C2) return;
-        const uint8_t *tile = s_a[c & (kStages - 1)];
+        const uint8_t *tile = s_a + (c % kStages) * kStageBytes;
         half8 av[MT], bc[2];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -252,7 +253,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     for (int i = 0; i < kAhead; ++i) issue(i, b[i]);
     for (int c = 0; c < st.C2; c += kStages) {
 #pragma unroll
-        for (int i = 0; i < kStages; ++i) step(c + i, b[i], b[(i + kAhead) & (kStages - 1)]);
+        for (int i = 0; i < kStages; ++i) step(c + i, b[i], b[(i + kAhead) % kStages]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -287,11 +288,11 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
-    // Ring of A stages: kChunkRows rows x kStepK fp16 each.
-    __shared__ __align__(16) uint8_t s_a[kStages][kStageBytes];
+    // Ring of A stages, kChunkRows rows x kStepK fp16 each.
+    __shared__ __align__(16) uint8_t s_a[kStages * kStageBytes];
     // LDS byte address of s_a (for the copies' M0).
     const uint32_t sa_lds = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)(&s_a[0][0])));
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)(&s_a[0])));
     __shared__ int s_tok[kChunkRows];
     __shared__ int s_ent[GATEUP ? 1 : kChunkRows];     // down: output entry and routing weight per row
     __shared__ float s_w[GATEUP ? 1 : kChunkRows];
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         st.C2 = K / kStepK;
         const int C = K / kChunkK;
         // 32-row tiles: 1, 2 or 4 (padding rows are computed and discarded).
-        const int mt = d.rows > 64 ? 4 : (d.rows > 32 ? 2 : 1);
+        const int mt = (d.rows + 31) / 32;
 
         // This wave's two 32-row B tiles (two 16-row panels each), as
         // uniform offsets, and the per-lane slot offsets inside them.
@@ -394,14 +395,18 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         // m = 8 (wave + 4j) + L / 8 with logical unit (L & 7) ^ lds_swz(m).
         const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 5; ++j) {
             const int m = 8 * (wave + 4 * j) + (lane >> 3);
             const int q = (lane & 7) ^ lds_swz(m);
             st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
         }
-        if (mt == 4) run_item<GATEUP, 4>(a, st, s_a, sa_lds, s_ent, s_w);
-        else if (mt == 2) run_item<GATEUP, 2>(a, st, s_a, sa_lds, s_ent, s_w);
-        else run_item<GATEUP, 1>(a, st, s_a, sa_lds, s_ent, s_w);
+        switch (mt) {
+            case 5: run_item<GATEUP, 5>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 4: run_item<GATEUP, 4>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 3: run_item<GATEUP, 3>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 2: run_item<GATEUP, 2>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            default: run_item<GATEUP, 1>(a, st, s_a, sa_lds, s_ent, s_w); break;
+        }
     }
     // The last workgroup out clears the queue counters for the next launch.
     if (dev::arrive_last(a.queues + kGroupedQueues * kQueueStride, gridDim.x) && tid < kGroupedQueues)

@@ -36,8 +36,7 @@ constexpr int kChunkBytes = 1024;
 constexpr int kScaleChunkBytes = 128;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
-constexpr int kMaxFrags = 8;        // 16-row MFMA tiles per grouped work chunk
-constexpr int kChunkRows = kMaxFrags * 16;
+constexpr int kChunkRows = 160;     // rows per grouped work chunk: five 32-row MFMA tiles
 
 struct BlobLayout {
     size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
