@@ -79,11 +79,12 @@ __host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
            static_cast<size_t>(4) * maxm * 16 * 4;
 }
 
-constexpr int kPipeGroup = 2;   // chunks per register buffer
+constexpr int kGateUpGroup = 2;   // gate/up chunks per register buffer
+constexpr int kPipeGroup = 2;   // down chunks per register buffer
 
 struct GateUpBuf {
-    uint4 gw[kPipeGroup], uw[kPipeGroup];
-    uint2 gs[kPipeGroup], us[kPipeGroup];
+    uint4 gw[kGateUpGroup], uw[kGateUpGroup];
+    uint2 gs[kGateUpGroup], us[kGateUpGroup];
 };
 
 // Sources of one gate/up panel: the blob descriptor, the lane offsets of a
@@ -96,7 +97,7 @@ struct GateUpSrc {
 
 __device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpSrc &S, int first, int step, int C) {
 #pragma unroll
-    for (int g = 0; g < kPipeGroup; ++g) {
+    for (int g = 0; g < kGateUpGroup; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + step * g, C - 1));
         b.gw[g] = bload<uint4>(S.r, S.vq, S.gq + c * kChunkBytes);
         b.uw[g] = bload<uint4>(S.r, S.vq, S.uq + c * kChunkBytes);
@@ -111,7 +112,7 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf &b, const uint8_t *x
                                             uint32_t M0, uint32_t M1, uint32_t G, float *gacc,
                                             float *vacc) {
 #pragma unroll
-    for (int g = 0; g < kPipeGroup; ++g) {
+    for (int g = 0; g < kGateUpGroup; ++g) {
         if (g >= count) continue;
         const int c = first + step * g;
         const uint32_t gws[4] = {b.gw[g].x, b.gw[g].y, b.gw[g].z, b.gw[g].w};
@@ -196,14 +197,14 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
         }
         __syncthreads();
         // i indexes this wave's chunk list; buffers alternate A, B.
-        for (int i = 0; i < nper; i += 2 * kPipeGroup) {
-            if (i + kPipeGroup < nper) gateup_load(B, P, wave + 4 * (i + kPipeGroup), 4, C);
-            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(kPipeGroup, nper - i), kq, mc, M0, M1, G,
+        for (int i = 0; i < nper; i += 2 * kGateUpGroup) {
+            if (i + kGateUpGroup < nper) gateup_load(B, P, wave + 4 * (i + kGateUpGroup), 4, C);
+            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(kGateUpGroup, nper - i), kq, mc, M0, M1, G,
                               gacc, vacc);
-            if (i + 2 * kPipeGroup < nper) gateup_load(A, P, wave + 4 * (i + 2 * kPipeGroup), 4, C);
-            if (i + kPipeGroup < nper)
-                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + kPipeGroup), 4,
-                                  min(kPipeGroup, nper - i - kPipeGroup), kq, mc, M0, M1, G, gacc, vacc);
+            if (i + 2 * kGateUpGroup < nper) gateup_load(A, P, wave + 4 * (i + 2 * kGateUpGroup), 4, C);
+            if (i + kGateUpGroup < nper)
+                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + kGateUpGroup), 4,
+                                  min(kGateUpGroup, nper - i - kGateUpGroup), kq, mc, M0, M1, G, gacc, vacc);
         }
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
