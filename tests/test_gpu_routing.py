@@ -96,3 +96,24 @@ def test_route_matches_oracle(E, k):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
     L.close()
+
+
+@pytest.mark.parametrize("E,act", [(256, "bf16"), (300, "f32"), (37, "bf16")])
+def test_router_logits_large_batch_matches_oracle(E, act):
+    """Logits of a large batch (the 8-token x 8-expert tile kernel, ragged
+    in both tokens and experts here), bit for bit."""
+    spec = configs.TINY.with_(hidden=512, inter=128, n_experts=E, top_k=4, n_tok=1000,
+                              has_shared=False, act=act, routing="gauss")
+    data = Data(spec)
+    log(f"case router E={E} act={act} n_tok={spec.n_tok}")
+    L = B.MoELayer.from_spec(spec)
+    L.set_router(data.w, data.b)
+    x = B.activations_to_device(data.x)
+    logits = L.router_logits(x)
+    idx, w = L.route(x)
+    torch.cuda.synchronize()
+    ref_logits = orc.router_logits(data.x, data.w, data.b)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_logits.view(np.uint32))
+    ref_idx, _ = orc.topk(ref_logits, spec.top_k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    L.close()
