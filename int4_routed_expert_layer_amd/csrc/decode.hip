@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
     extern __shared__ __align__(16) uint8_t lds[];
     if (static_cast<int>(blockIdx.x) >= router_blocks) {
         const int p = blockIdx.x - router_blocks;
-        dev::gateup_panel<NT>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k, a.n_tok, p, lds);
+        dev::gateup_panel<NT>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k, a.n_tok, p, lds,
+                              dev::lds_address(lds));
         return;
     }
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);

@@ -105,6 +105,7 @@ __device__ __forceinline__ bool resolve(const FwdArgs &a, int u, int &e, int &r0
 // Token of hidden-buffer row `row`: routed rows are in gather order, shared
 // rows follow at n_tok*k + t.
 __device__ __forceinline__ int token_of_row(const FwdArgs &a, int row) {
+    if (a.n_tok == 1) return 0;   // one token: no lookup
     const int routed = a.n_tok * a.k;
     return row < routed ? a.gather[row] / a.k : row - routed;
 }
@@ -114,6 +115,25 @@ __device__ __forceinline__ int token_of_row(const FwdArgs &a, int row) {
 __device__ __forceinline__ uint32_t float_key(float f) {
     const uint32_t b = __float_as_uint(f + 0.0f);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// LDS byte address of a __shared__ array (pass the array itself, not a
+// pointer computed at run time, so the conversion folds to a constant).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_address(T *shared_array) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T *)(shared_array))));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at
+// LDS byte address lds_addr + 16 L (lds_addr wave-uniform; it goes to M0).
+// Written as inline asm so that the compiler's wait insertion does not see an
+// LDS write in flight: it would otherwise make every LDS read wait for all
+// copies, including the lookahead stages.  The caller waits for a stage's
+// copies explicitly (s_waitcnt vmcnt) before reading it; the copy has no
+// output register, and its address operands are consumed at issue.
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
 }
 
 // Exclusive scan of one int per thread over a block of NT threads; *total

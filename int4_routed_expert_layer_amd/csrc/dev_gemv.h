@@ -144,7 +144,7 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf &b, const uint8_t *x
 // synchronises the workgroup).
 template <int MAXM, bool COHERENT = false, class Rows>
 __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int p,
-                             uint8_t *lds) {
+                             uint8_t *lds, uint32_t lds_addr) {
     const int H = a.hidden, I = a.inter;
     const int C = H / kChunkK;
     const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
@@ -173,6 +173,48 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
         for (int m = 0; m < MAXM; ++m) gacc[m] = vacc[m] = 0.0f;
 
         GateUpBuf A, B;
+        if (a.act_bf16 && (H * 2) % 1024 == 0) {
+            // bf16 rows are copied straight into the staging area (1 KB per
+            // wave instruction) before the weight loads are issued; the wait
+            // below then covers only those copies (memory returns are counted
+            // in issue order), not the first weight burst.  Each thread then
+            // turns its own 16 bytes into the staged fp16 form in place.
+            __syncthreads();                    // the previous row block is done with xs
+            const int per_row = H / 512;
+            int toks[MAXM];                     // token lookups first: none sits between the copies
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) toks[m] = m < mc ? rows.token(r0 + mb + m) : 0;
+            for (int ci = wave; ci < mc * per_row; ci += 4) {
+                const int m = ci / per_row, part = ci % per_row;
+                int t = toks[0];
+#pragma unroll
+                for (int mm = 1; mm < MAXM; ++mm) t = m == mm ? toks[mm] : t;
+                copy16_to_lds(static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * H + part * 512 + 8 * lane,
+                              lds_addr + static_cast<uint32_t>((m * H + part * 512) * 2));
+            }
+            gateup_load(A, P, wave, 4, C);      // weights do not depend on x
+            // Plain barriers here: __syncthreads' fence would also wait for
+            // the weight loads just issued.
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kGateUpGroup) : "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            for (int i = tid; i < mc * (H / 8); i += 256) {
+                const int m = i / (H / 8), q = i % (H / 8);
+                uint8_t *dst = xs + (static_cast<size_t>(m) * H + 8 * q) * 2;
+                const uint4 raw = *reinterpret_cast<const uint4 *>(dst);
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = bf16_bits_to_f32(w4[j] & 0xFFFFu);
+                    v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
+                }
+                stage8(v, dst, cs + m * (H / 8) + q);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        } else {
         gateup_load(A, P, wave, 4, C);          // weights do not depend on x
         __syncthreads();
         for (int i = tid; i < mc * (H / 8); i += 256) {
@@ -196,6 +238,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
             stage8(v, xs + (static_cast<size_t>(m) * H + 8 * q) * 2, cs + m * (H / 8) + q);
         }
         __syncthreads();
+        }
         // i indexes this wave's chunk list; buffers alternate A, B.
         for (int i = 0; i < nper; i += 2 * kGateUpGroup) {
             if (i + kGateUpGroup < nper) gateup_load(B, P, wave + 4 * (i + kGateUpGroup), 4, C);
@@ -302,7 +345,7 @@ __device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, c
 // is read (a wait for h's producers).  All 256 threads must call it.
 template <int MAXM, bool COHERENT = false, class Rows, class BeforeH>
 __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int pg,
-                                uint8_t *lds, const BeforeH &before_h) {
+                                uint8_t *lds, uint32_t lds_addr, const BeforeH &before_h) {
     const int H = a.hidden, I = a.inter;
     const int C = I / kChunkK;
     const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
@@ -326,20 +369,49 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
         DownBuf A, B;
-        down_load(A, rs, vq, vs, sq, ss, c_begin, C);
         if (mb == 0) before_h();
-        __syncthreads();
-        for (int i = tid; i < mc * (I / 8); i += 256) {
-            const int m = i / (I / 8), q = i % (I / 8);
-            const _Float16 *src = a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q;
-            const uint4 raw = gload<uint4>(src);     // h comes from an earlier launch
-            const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
-            float v[8];
+        __syncthreads();                        // the previous row block is done with hs
+        if ((I * 2) % 1024 == 0) {
+            // h rows (fp16, from an earlier launch) are copied straight into
+            // the staging area before the weight loads, and converted in
+            // place once the copies alone have landed (as in gateup_panel).
+            const int per_row = I / 512;
+            for (int ci = wave; ci < mc * per_row; ci += 4) {
+                const int m = ci / per_row, part = ci % per_row;
+                copy16_to_lds(a.h + static_cast<size_t>(r0 + mb + m) * I + part * 512 + 8 * lane,
+                              lds_addr + static_cast<uint32_t>((m * I + part * 512) * 2));
+            }
+            down_load(A, rs, vq, vs, sq, ss, c_begin, C);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPipeGroup) : "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            for (int i = tid; i < mc * (I / 8); i += 256) {
+                const int m = i / (I / 8), q = i % (I / 8);
+                uint8_t *dst = hs + (static_cast<size_t>(m) * I + 8 * q) * 2;
+                const uint4 raw = *reinterpret_cast<const uint4 *>(dst);
+                const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
+                float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
-            stage8(v, hs + (static_cast<size_t>(m) * I + 8 * q) * 2, cs + m * (I / 8) + q);
+                for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
+                stage8(v, dst, cs + m * (I / 8) + q);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        } else {
+            down_load(A, rs, vq, vs, sq, ss, c_begin, C);
+            for (int i = tid; i < mc * (I / 8); i += 256) {
+                const int m = i / (I / 8), q = i % (I / 8);
+                const _Float16 *src = a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q;
+                const uint4 raw = gload<uint4>(src);     // h comes from an earlier launch
+                const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
+                stage8(v, hs + (static_cast<size_t>(m) * I + 8 * q) * 2, cs + m * (I / 8) + q);
+            }
+            __syncthreads();
         }
-        __syncthreads();
         for (int i = 0; i < nper; i += 2 * kPipeGroup) {
             if (i + kPipeGroup < nper) down_load(B, rs, vq, vs, sq, ss, c_begin + i + kPipeGroup, C);
             down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), kq, mc, M0, M1, G, acc);

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin
     if (a.skip_shared && e == a.n_experts) return;
     const uint8_t *blob = a.table[e];
     if (!blob || M <= 0) return;
-    dev::gateup_panel<MAXM>(a, dev::PlainRows{a}, blob, r0, M, p, lds);
+    dev::gateup_panel<MAXM>(a, dev::PlainRows{a}, blob, r0, M, p, lds, dev::lds_address(lds));
 }
 
 template <int MAXM, bool FUSED_COMBINE>
@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
     if (!dev::resolve(a, u, e, r0, M)) return;
     const uint8_t *blob = a.table[e];
     if (blob && M > 0)
-        dev::down_panelgroup<MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::NoWait{});
+        dev::down_panelgroup<MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::lds_address(lds),
+                                                  dev::NoWait{});
     if (FUSED_COMBINE) {
         const int units = *a.n_union + (a.has_shared ? 1 : 0);
         // The last workgroup of the panel pair reuses its (now idle) LDS.

@@ -95,17 +95,6 @@ __device__ __forceinline__ int lds_unit(int m, int q) {
     return m * kStageRowBytes + ((q ^ lds_swz(m)) << 4);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at
-// LDS byte address lds_addr + 16 L (lds_addr wave-uniform; it goes to M0).
-// Written as inline asm so that the compiler's wait insertion does not see an
-// LDS write in flight: it would otherwise make every LDS read wait for all
-// copies, including the lookahead stages.  The caller waits for a stage's
-// copies explicitly (s_waitcnt vmcnt) before reading it; the copy has no
-// output register, and its address operands are consumed at issue.
-__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds_addr) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
-}
-
 // Scheduling groups for one slice: N times (one MFMA, on odd turns one LDS
 // read, V VALU instructions), so the reads and dequantisation of the next
 // slice issue between the MFMAs of this one.
@@ -164,7 +153,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
         const uint32_t dst = sa_lds + static_cast<uint32_t>(c % kStages) * kStageBytes;
 #pragma unroll
         for (int j = 0; j < MT; ++j)
-            copy16_to_lds(st.asrc + st.src_off[j] + cc * kStepK,
+            dev::copy16_to_lds(st.asrc + st.src_off[j] + cc * kStepK,
                           dst + static_cast<uint32_t>(8 * (wave + 4 * j) * kStageRowBytes));
         asm volatile("" ::: "memory");
         const uint32_t ch = static_cast<uint32_t>(cc >> 1), h = static_cast<uint32_t>(cc & 1);
