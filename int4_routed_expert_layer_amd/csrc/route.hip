@@ -200,7 +200,7 @@ hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
     if (n_tok <= 32)
         return launch_logits_t<4, 2, 8>(x, act_bf16, wt, bias, n_tok, hidden,
                                         n_experts, logits, s);
-    return launch_logits_t<8, 8, 2>(x, act_bf16, wt, bias, n_tok, hidden,
+    return launch_logits_t<8, 8, 4>(x, act_bf16, wt, bias, n_tok, hidden,
                                     n_experts, logits, s);
 }
 
