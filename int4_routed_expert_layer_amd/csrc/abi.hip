@@ -165,9 +165,9 @@ struct coli_layer {
     const uint8_t **table_dev = nullptr;      // [E + 1]; NULL for non-VRAM experts
 
     float *logits = nullptr;    // [max_tokens x E]
-    _Float16 *h = nullptr;      // [(max_tokens*k + max_tokens) x I]
+    _Float16 *h = nullptr;      // [(max_tokens*k + max_tokens + 1) x I]; the last row takes discarded stores
     _Float16 *xh = nullptr;     // [max_tokens x H]
-    float *ys = nullptr;        // [(max_tokens*k + max_tokens) x H]
+    float *ys = nullptr;        // [(max_tokens*k + max_tokens + 1) x H]; the last row takes discarded stores
     ChunkDesc *chunks = nullptr;
     int32_t *n_chunks = nullptr;
     int max_chunks = 0;
@@ -347,6 +347,7 @@ FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, 
     a.h = L->h;
     a.xh = L->xh;
     a.ys = L->ys;
+    a.discard_row = static_cast<int>(L->d.max_tokens) * (L->d.top_k + 1);
     a.y = y;
     a.chunks = L->chunks;
     a.n_chunks = L->n_chunks;
@@ -497,9 +498,9 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->bias), sizeof(float) * E, "router bias"},
         {reinterpret_cast<void **>(&L->table_dev), sizeof(void *) * (E + 1), "expert table"},
         {reinterpret_cast<void **>(&L->logits), sizeof(float) * T * E, "logits scratch"},
-        {reinterpret_cast<void **>(&L->h), sizeof(_Float16) * rows * I, "hidden scratch"},
+        {reinterpret_cast<void **>(&L->h), sizeof(_Float16) * (rows + 1) * I, "hidden scratch"},
         {reinterpret_cast<void **>(&L->xh), sizeof(_Float16) * T * H, "fp16 activation scratch"},
-        {reinterpret_cast<void **>(&L->ys), sizeof(float) * rows * H, "per-entry output scratch"},
+        {reinterpret_cast<void **>(&L->ys), sizeof(float) * (rows + 1) * H, "per-entry output scratch"},
         {reinterpret_cast<void **>(&L->chunks), sizeof(ChunkDesc) * L->max_chunks, "work list"},
         {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
         {reinterpret_cast<void **>(&L->err), sizeof(int32_t), "error flags"},

@@ -53,6 +53,16 @@ __device__ __forceinline__ T bload(rsrc_t r, uint32_t voff, uint32_t soff) {
     }
 }
 
+// SwiGLU of one gate/up pair, silu(g) * v = g * v / (1 + e^-g), with e^-g as
+// 2^(-g log2 e) on the hardware base-2 exponential and the quotient through
+// the hardware reciprocal (each about one ulp in fp32; h is then rounded to
+// fp16, whose step is 2^11 ulp of fp32).  Large negative g gives e^-g = inf,
+// reciprocal 0 and h = -0 or 0, the limit of the exact function.
+__device__ __forceinline__ float swiglu(float g, float v) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * v;
+}
+
 // Wave index as a scalar (uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
 

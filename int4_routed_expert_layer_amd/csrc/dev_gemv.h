@@ -272,7 +272,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                 g = g + red[((w * MAXM + m) * 16 + r) * 2 + 0];
                 v = v + red[((w * MAXM + m) * 16 + r) * 2 + 1];
             }
-            const float hval = g / (1.0f + expf(-g)) * v;
+            const float hval = swiglu(g, v);
             _Float16 *dst = a.h + static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r;
             if (COHERENT) store_coherent(dst, static_cast<_Float16>(hval));
             else *dst = static_cast<_Float16>(hval);

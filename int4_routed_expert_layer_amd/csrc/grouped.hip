@@ -247,28 +247,39 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue.  Lane holds D[m = 8(i / 4) + 4(L / 32) + i % 4][n = L % 32]
-    // of each 32x32 tile.
+    // of each 32x32 tile.  Padding rows (m >= rows) store into the discard
+    // row, so no store is predicated.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+        if (GATEUP) {
+            const int col = st.nb * 128 + wave * 32 + l31;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = mt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-            if (m < st.rows) {
-                if (GATEUP) {
-                    const float g = acc[mt][0][i], v = acc[mt][1][i];
-                    const float hval = g / (1.0f + expf(-g)) * v;
-                    const int col = st.nb * 128 + wave * 32 + l31;
-                    a.h[static_cast<size_t>(st.row0 + m) * I + col] = static_cast<_Float16>(hval);
-                } else {
-                    const int entry = s_ent[m];
-                    const float wgt = s_w[m];
+            for (int i = 0; i < 16; ++i) {
+                const int m = mt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                const int r = m < st.rows ? st.row0 + m : a.discard_row;
+                a.h[static_cast<size_t>(r) * I + col] =
+                    static_cast<_Float16>(dev::swiglu(acc[mt][0][i], acc[mt][1][i]));
+            }
+        } else {
+            // The tile's output entries (the discard row for padding) and
+            // routing weights, read from LDS in one batch ahead of the stores.
+            const int col = st.nb * 256 + wave * 64 + l31;
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        if (st.bvalid[nt]) {
-                            const int col = st.nb * 256 + wave * 64 + nt * 32 + l31;
-                            a.ys[static_cast<size_t>(entry) * H + col] = wgt * acc[mt][nt][i];
-                        }
-                    }
+            for (int i0 = 0; i0 < 16; i0 += 8) {
+                int ent[8];
+                float wgt[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int m = mt * 32 + 8 * ((i0 + i) >> 2) + 4 * lh + (i & 3);
+                    ent[i] = s_ent[m];
+                    wgt[i] = s_w[m];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float *yrow = a.ys + static_cast<size_t>(ent[i]) * H + col;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        if (st.bvalid[nt]) yrow[nt * 32] = wgt[i] * acc[mt][nt][i0 + i];
                 }
             }
         }
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
             s_tok[m] = GATEUP ? (r < routed ? a.gather[r] / a.k : r - routed) : r;
             if (!GATEUP) {
                 const int entry = r < routed ? a.gather[r] : r;
-                s_ent[m] = entry;
+                s_ent[m] = m < d.rows ? entry : a.discard_row;
                 s_w[m] = r < routed ? a.topk_w[entry] : 1.0f;
             }
         }

@@ -66,9 +66,10 @@ struct FwdArgs {
     const float *topk_w;
     int n_tok, k, hidden, inter, n_experts, has_shared;
     BlobLayout lay;
-    _Float16 *h;                    // [(n_tok*k + n_tok) x I]
+    _Float16 *h;                    // [(n_tok*k + n_tok) x I], plus the discard row
     _Float16 *xh;                   // [n_tok x H] fp16 copy of x (grouped path)
-    float *ys;                      // [(n_tok*k + n_tok) x H]
+    float *ys;                      // [(n_tok*k + n_tok) x H], plus the discard row
+    int discard_row;                // row of h and ys that takes the padding rows' stores
     float *y;                       // [n_tok x H]
     const ChunkDesc *chunks;        // grouped path work list
     const int32_t *n_chunks;
