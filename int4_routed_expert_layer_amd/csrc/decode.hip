@@ -20,11 +20,13 @@ namespace {
 
 constexpr int kFrontThreads = 256;
 constexpr int kFrontMaxExperts = 256;
+constexpr int kFrontGateUpGroup = 4;   // shared gate/up chunks per register buffer
 
 template <int NT, bool BF16>
 __device__ __forceinline__ void wave_router(const FwdArgs &a, const FrontArgs &f, int e) {
     const int lane = threadIdx.x & 63;
     const int H = a.hidden, E = a.n_experts;
+    const float b = f.bias ? f.bias[e] : 0.0f;   // scalar load, in flight during the row
     const float *wrow = f.wt + static_cast<size_t>(e) * H + lane;
     float acc[NT];
 #pragma unroll
@@ -66,7 +68,6 @@ __device__ __forceinline__ void wave_router(const FwdArgs &a, const FrontArgs &f
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = acc[t] + __shfl_down(acc[t], s, 64);
     if (lane == 0) {
-        const float b = f.bias ? f.bias[e] : 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             if (t < a.n_tok) dev::store_coherent(f.logits + static_cast<size_t>(t) * E + e, acc[t] + b);
@@ -149,18 +150,80 @@ __device__ void select_and_union(const FwdArgs &a, const FrontArgs &f) {
     }
 }
 
+// One token: the same top-k and weights; its union needs no scans, as the k
+// selected experts are distinct: expert e has count 1 if selected, offset =
+// number of selected experts below e, and its single entry is the slot that
+// chose it.
+__device__ void select_one_token(const FwdArgs &a, const FrontArgs &f) {
+    __shared__ uint64_t s_key[kFrontMaxExperts];
+    __shared__ uint64_t s_fin[4 * kMaxTopK];
+    __shared__ float s_sig[kMaxTopK];
+    __shared__ int s_sel[kMaxTopK];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int E = a.n_experts, k = a.k;
+    const uint32_t low = 0xFFFFFFFFu - static_cast<uint32_t>(tid);
+    uint64_t key = low;
+    if (tid < E) key |= static_cast<uint64_t>(dev::float_key(dev::load_coherent(f.logits + tid))) << 32;
+    s_key[tid] = key;
+    __syncthreads();
+    int r = 0;
+    for (int j = 0; j < 64; ++j) r += s_key[64 * wave + j] > key ? 1 : 0;
+    if (r < k) s_fin[wave * k + r] = key;
+    __syncthreads();
+    if (tid < 4 * k) {
+        const uint64_t fk = s_fin[tid];
+        int R = 0;
+        for (int j = 0; j < 4 * k; ++j) R += s_fin[j] > fk ? 1 : 0;
+        if (R < k) {
+            const uint32_t kh = static_cast<uint32_t>(fk >> 32);
+            const float l = __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
+            s_sel[R] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(fk));
+            s_sig[R] = 1.0f / (1.0f + expf(-l));
+        }
+    }
+    __syncthreads();
+    if (tid < k) {
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum = sum + s_sig[j];
+        f.topk_idx[tid] = s_sel[tid];
+        f.topk_w[tid] = s_sig[tid] / sum;
+    }
+    if (tid < E) {
+        int below = 0, slot = -1;
+        for (int j = 0; j < k; ++j) {
+            const int id = s_sel[j];
+            below += id < tid ? 1 : 0;
+            slot = id == tid ? j : slot;
+        }
+        f.counts[tid] = slot >= 0 ? 1 : 0;
+        f.offsets[tid] = below;
+        if (slot >= 0) {
+            f.union_ids[below] = tid;
+            f.gather[below] = slot;
+        }
+    }
+    if (tid == 0) {
+        f.offsets[E] = k;
+        *f.n_union = k;
+    }
+}
+
 template <int NT, bool BF16>
 __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, FrontArgs f, int router_blocks) {
     extern __shared__ __align__(16) uint8_t lds[];
     if (static_cast<int>(blockIdx.x) >= router_blocks) {
         const int p = blockIdx.x - router_blocks;
-        dev::gateup_panel<NT>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k, a.n_tok, p, lds,
-                              dev::lds_address(lds));
+        // One block per CU here: a deeper load pipeline than the routed kernel.
+        dev::gateup_panel<NT, false, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
+                                                        a.n_tok, p, lds, dev::lds_address(lds));
         return;
     }
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int e = static_cast<int>(blockIdx.x) * 4 + dev::wave_id();   // uniform per wave
     if (e < a.n_experts) wave_router<NT, BF16>(a, f, e);
-    if (dev::arrive_last(f.counter, router_blocks)) select_and_union(a, f);
+    if (dev::arrive_last(f.counter, router_blocks)) {
+        if (a.n_tok == 1) select_one_token(a, f);
+        else select_and_union(a, f);
+    }
 }
 
 template <int NT>

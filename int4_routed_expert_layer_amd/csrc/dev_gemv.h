@@ -82,9 +82,10 @@ __host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
 constexpr int kGateUpGroup = 2;   // gate/up chunks per register buffer
 constexpr int kPipeGroup = 2;   // down chunks per register buffer
 
+template <int NG>
 struct GateUpBuf {
-    uint4 gw[kGateUpGroup], uw[kGateUpGroup];
-    uint2 gs[kGateUpGroup], us[kGateUpGroup];
+    uint4 gw[NG], uw[NG];
+    uint2 gs[NG], us[NG];
 };
 
 // Sources of one gate/up panel: the blob descriptor, the lane offsets of a
@@ -95,9 +96,10 @@ struct GateUpSrc {
     uint32_t gq, uq, gs, us;  // uniform
 };
 
-__device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpSrc &S, int first, int step, int C) {
+template <int NG>
+__device__ __forceinline__ void gateup_load(GateUpBuf<NG> &b, const GateUpSrc &S, int first, int step, int C) {
 #pragma unroll
-    for (int g = 0; g < kGateUpGroup; ++g) {
+    for (int g = 0; g < NG; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + step * g, C - 1));
         b.gw[g] = bload<uint4>(S.r, S.vq, S.gq + c * kChunkBytes);
         b.uw[g] = bload<uint4>(S.r, S.vq, S.uq + c * kChunkBytes);
@@ -106,13 +108,13 @@ __device__ __forceinline__ void gateup_load(GateUpBuf &b, const GateUpSrc &S, in
     }
 }
 
-template <int MAXM>
-__device__ __forceinline__ void gateup_math(const GateUpBuf &b, const uint8_t *xs, const float *cs, int H,
+template <int MAXM, int NG>
+__device__ __forceinline__ void gateup_math(const GateUpBuf<NG> &b, const uint8_t *xs, const float *cs, int H,
                                             int first, int step, int count, int kq, int mc,
                                             uint32_t M0, uint32_t M1, uint32_t G, float *gacc,
                                             float *vacc) {
 #pragma unroll
-    for (int g = 0; g < kGateUpGroup; ++g) {
+    for (int g = 0; g < NG; ++g) {
         if (g >= count) continue;
         const int c = first + step * g;
         const uint32_t gws[4] = {b.gw[g].x, b.gw[g].y, b.gw[g].z, b.gw[g].w};
@@ -141,8 +143,9 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf &b, const uint8_t *x
 // tokens of hidden-buffer rows r0..r0+M-1 (rows.token(row) names the token of
 // a row).  Writes h rows (fp16; device-coherent stores when COHERENT, for a
 // consumer in the same launch).  All 256 threads must call it (it
-// synchronises the workgroup).
-template <int MAXM, bool COHERENT = false, class Rows>
+// synchronises the workgroup).  NG chunks per register buffer (two buffers in
+// flight): more for few workgroups per CU.
+template <int MAXM, bool COHERENT = false, int NG = kGateUpGroup, class Rows>
 __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int p,
                              uint8_t *lds, uint32_t lds_addr) {
     const int H = a.hidden, I = a.inter;
@@ -172,7 +175,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) gacc[m] = vacc[m] = 0.0f;
 
-        GateUpBuf A, B;
+        GateUpBuf<NG> A, B;
         if (a.act_bf16 && (H * 2) % 1024 == 0) {
             // bf16 rows are copied straight into the staging area (1 KB per
             // wave instruction) before the weight loads are issued; the wait
@@ -195,7 +198,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
             gateup_load(A, P, wave, 4, C);      // weights do not depend on x
             // Plain barriers here: __syncthreads' fence would also wait for
             // the weight loads just issued.
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kGateUpGroup) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NG) : "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             for (int i = tid; i < mc * (H / 8); i += 256) {
@@ -240,14 +243,14 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
         __syncthreads();
         }
         // i indexes this wave's chunk list; buffers alternate A, B.
-        for (int i = 0; i < nper; i += 2 * kGateUpGroup) {
-            if (i + kGateUpGroup < nper) gateup_load(B, P, wave + 4 * (i + kGateUpGroup), 4, C);
-            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(kGateUpGroup, nper - i), kq, mc, M0, M1, G,
+        for (int i = 0; i < nper; i += 2 * NG) {
+            if (i + NG < nper) gateup_load(B, P, wave + 4 * (i + NG), 4, C);
+            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(NG, nper - i), kq, mc, M0, M1, G,
                               gacc, vacc);
-            if (i + 2 * kGateUpGroup < nper) gateup_load(A, P, wave + 4 * (i + 2 * kGateUpGroup), 4, C);
-            if (i + kGateUpGroup < nper)
-                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + kGateUpGroup), 4,
-                                  min(kGateUpGroup, nper - i - kGateUpGroup), kq, mc, M0, M1, G, gacc, vacc);
+            if (i + 2 * NG < nper) gateup_load(A, P, wave + 4 * (i + 2 * NG), 4, C);
+            if (i + NG < nper)
+                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + NG), 4, min(NG, nper - i - NG), kq, mc, M0, M1, G,
+                                  gacc, vacc);
         }
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
