@@ -3,15 +3,15 @@
 //
 // When the union gives experts many tokens (large decode batches, prefill)
 // the expert matmuls become dense contractions, [M_u x K] x [K x N] per
-// union expert.  Work is a list of chunks (one expert, <= 128 rows) crossed
-// with N-blocks; a persistent grid walks that list (consecutive items, which
-// share the same activation rows, land on the same XCD and its L2).
+// union expert.  Work is a list of chunks (one expert, <= 160 rows) crossed
+// with N-blocks; a persistent grid walks that list (the N-blocks of a chunk,
+// which share its activation rows, are queued on one XCD and its L2).
 //
 // Per item a 256-thread workgroup (two per CU) walks the reduction axis in
-// 64-column steps through a ring of four LDS stages: the chunk's fp16
-// activation rows of step c + 3 are copied straight from global memory into
+// 64-column steps through a ring of three LDS stages: the chunk's fp16
+// activation rows of step c + 2 are copied straight from global memory into
 // LDS (global_load_lds; XOR-swizzled 16-byte units, conflict-free for the
-// fragment reads) and each wave's int4 weight fragments of step c + 3 are
+// fragment reads) and each wave's int4 weight fragments of step c + 2 are
 // loaded into registers (buffer loads, already in B-fragment order of
 // v_mfma_f32_32x32x16_f16) while step c is multiplied.  Inside a step the LDS
 // reads and the dequantisation of the next 16-column slice are interleaved
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     // chunk (chunk c to queue c mod 8) and taken dynamically: workgroup b
     // draws from queue b mod 8, which on an 8-XCD part is the queue of its
     // XCD, so the N-blocks of a chunk (same activation rows) share an L2.
-    // Items differ in cost (chunks of 1 to 128 rows); dynamic claiming keeps
+    // Items differ in cost (chunks of 1 to 160 rows); dynamic claiming keeps
     // every workgroup busy until its queue is empty.
     const int nq = gridDim.x >= kGroupedQueues ? kGroupedQueues : 1;
     const int q = blockIdx.x % nq;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         st.nb = nb;
         st.C2 = K / kStepK;
         const int C = K / kChunkK;
-        // 32-row tiles: 1, 2 or 4 (padding rows are computed and discarded).
+        // 32-row tiles: 1 to 5 (padding rows are computed and discarded).
         const int mt = (d.rows + 31) / 32;
 
         // This wave's two 32-row B tiles (two 16-row panels each), as
