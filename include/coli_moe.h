@@ -211,6 +211,20 @@ coli_status coli_layer_set_path(coli_layer *layer, int32_t path);
 coli_status coli_layer_stream_stats(const coli_layer *layer,
                                     int32_t *n_streamed, int64_t *bytes);
 
+/* Keep up to n_slots pinned-host experts in VRAM between tiered forward
+ * calls (the pages' placement step: a copy that a later call finds in VRAM
+ * needs no PCIe transfer).  Each slot is one expert blob of device memory,
+ * allocated at the next tiered call; the least recently used slot is
+ * replaced on a miss.  0 (the default) copies every host-tier expert on
+ * every call.  Results are bit-identical with or without the cache.
+ * Re-placing an expert drops its cached copy; changing n_slots drops all.
+ * COLI_E_INVALID unless n_slots is 0 or between 4 and n_experts. */
+coli_status coli_layer_set_stream_cache(coli_layer *layer, int32_t n_slots);
+
+/* Host-tier experts of the last tiered forward call that were found in the
+ * stream cache (host pointer). */
+coli_status coli_layer_stream_hits(const coli_layer *layer, int32_t *hits);
+
 /* Read and clear the device error flags (synchronises the device):
  * bit 0 = an out-of-range expert id reached coli_moe_union. */
 coli_status coli_layer_device_errors(coli_layer *layer, int32_t *flags);

@@ -40,6 +40,8 @@ SIGNATURES = {
     "coli_layer_set_path": (C.c_int, [_p, _i32]),
     "coli_moe_layer": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "coli_layer_stream_stats": (C.c_int, [_p, _p, _p]),
+    "coli_layer_set_stream_cache": (C.c_int, [_p, _i32]),
+    "coli_layer_stream_hits": (C.c_int, [_p, _p]),
     "coli_layer_device_errors": (C.c_int, [_p, _p]),
     "coli_layer_set_timing": (C.c_int, [_p, _i32]),
     "coli_layer_kernel_times": (C.c_int, [_p, _p, _p]),
@@ -225,6 +227,14 @@ class MoELayer:
         idx, w = self.route(x)
         u = self.union(idx)
         return self.forward(x, idx, w, u), idx, w, u
+
+    def set_stream_cache(self, n_slots: int):
+        _check(lib.coli_layer_set_stream_cache(self.handle, n_slots), self.handle)
+
+    def stream_hits(self) -> int:
+        h = C.c_int32()
+        _check(lib.coli_layer_stream_hits(self.handle, C.byref(h)), self.handle)
+        return h.value
 
     def stream_stats(self):
         n = C.c_int32()

@@ -188,6 +188,13 @@ struct coli_layer {
     int32_t *pin_union = nullptr;    // [1 + E]
     int32_t last_streamed = 0;
     int64_t last_bytes = 0;
+    int32_t last_hits = 0;
+    // Stream cache: slots keep host-tier experts between calls (LRU).
+    int cache_slots = 0;
+    std::vector<int> slot_expert;    // expert held by each slot, -1 none
+    std::vector<int64_t> slot_stamp; // last call that used the slot
+    std::vector<int> expert_slot;    // [E] slot holding the expert, -1 none
+    int64_t call_no = 0;
 
     // kernel timing
     bool timing = false;
@@ -407,10 +414,13 @@ void free_layer(coli_layer *L) {
 coli_status ensure_stream_resources(coli_layer *L, int n_batches) {
     const size_t bytes = L->lay.total;
     if (!L->side) HIP_TRY(L, hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking), "side stream");
-    while (static_cast<int>(L->slots.size()) < kSlotCount) {
+    const int n_slots = std::max(kSlotCount, L->cache_slots);
+    while (static_cast<int>(L->slots.size()) < n_slots) {
         uint8_t *p = nullptr;
         HIP_TRY(L, hipMalloc(&p, bytes), "staging slot");
         L->slots.push_back(p);
+        L->slot_expert.push_back(-1);
+        L->slot_stamp.push_back(0);
         hipEvent_t ev;
         HIP_TRY(L, hipEventCreateWithFlags(&ev, hipEventDisableTiming), "slot event");
         L->slot_free.push_back(ev);
@@ -491,6 +501,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     const size_t rows = T * dims->top_k + T;
     L->max_chunks = max_work_chunks(dims->max_tokens, dims->top_k, E, dims->has_shared);
     L->experts.resize(E + 1);
+    L->expert_slot.assign(E, -1);
     L->table_host.assign(E + 1, nullptr);
 
     struct A { void **p; size_t n; const char *what; } allocs[] = {
@@ -596,6 +607,10 @@ coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_ho
         L->table_host[idx] = nullptr;
     }
     x.tier = tier;
+    if (idx < L->d.n_experts && L->expert_slot[idx] >= 0) {   // a cached copy is stale now
+        L->slot_expert[L->expert_slot[idx]] = -1;
+        L->expert_slot[idx] = -1;
+    }
     HIP_TRY(L, hipMemcpy(L->table_dev + idx, &L->table_host[idx], sizeof(void *), hipMemcpyHostToDevice), "table update");
     if (tier == COLI_TIER_HOST && x.dev) {
         HIP_TRY(L, hipDeviceSynchronize(), "sync before free");
@@ -690,6 +705,7 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
 
     L->last_streamed = 0;
     L->last_bytes = 0;
+    L->last_hits = 0;
     std::vector<int> streamed;
     if (!all_routed_resident(L)) {
         // Read the union back to find the experts that are not in VRAM.
@@ -720,38 +736,83 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
     if ((st = launch_experts(L, a, path, s)) != COLI_OK) return st;
 
     if (!streamed.empty()) {
-        const int n_batches = (static_cast<int>(streamed.size()) + kBatchExperts - 1) / kBatchExperts;
+        // Host-tier experts already in the stream cache form the first batch
+        // (no copy); the others are copied into slots in batches of
+        // kBatchExperts, each batch computed once its copies have landed.
+        // Every earlier call ended with a stream synchronisation, so only
+        // slots read earlier in this call can still be in use.
+        const bool cache = L->cache_slots > 0;
+        const int64_t call = ++L->call_no;
+        std::vector<int> hits, misses;
+        for (int e : streamed) (cache && L->expert_slot[e] >= 0 ? hits : misses).push_back(e);
+        const int n_hit_batches = hits.empty() ? 0 : 1;
+        const int n_batches = n_hit_batches + (static_cast<int>(misses.size()) + kBatchExperts - 1) / kBatchExperts;
         if ((st = ensure_stream_resources(L, n_batches)) != COLI_OK) return st;
+        const int n_slots = cache ? L->cache_slots : kSlotCount;
         const size_t bytes = L->lay.total;
         const size_t tbytes = sizeof(uint8_t *) * (L->d.n_experts + 1);
-        std::vector<bool> slot_used(L->slots.size(), false);
+        // Batch of this call that last read each slot (-1: none yet).
+        std::vector<int> slot_batch(L->slots.size(), -1);
+        // A slot for a copy in batch b: a slot not read yet in this call (the
+        // least recently used one with the cache); when every slot was, the
+        // one read earliest, never one of batch b itself (n_slots >=
+        // kBatchExperts, so such a slot exists), after its kernels.
+        auto pick_slot = [&](int b) {
+            int best = -1;
+            for (int q = 0; q < n_slots; ++q)
+                if (slot_batch[q] < 0 && (best < 0 || (cache && L->slot_stamp[q] < L->slot_stamp[best]))) best = q;
+            if (best >= 0) return best;
+            for (int q = 0; q < n_slots; ++q)
+                if (slot_batch[q] < b && (best < 0 || slot_batch[q] < slot_batch[best])) best = q;
+            return best;
+        };
         for (int b = 0; b < n_batches; ++b) {
             const uint8_t **pt = L->pin_tables[b];
             std::memset(pt, 0, tbytes);
-            const int first = b * kBatchExperts;
-            const int last = std::min<int>(static_cast<int>(streamed.size()), first + kBatchExperts);
-            for (int i = first; i < last; ++i) {
-                const int slot = i % kSlotCount;
-                if (slot_used[slot]) HIP_TRY(L, hipStreamWaitEvent(L->side, L->slot_free[slot], 0), "slot wait");
-                const int e = streamed[i];
-                HIP_TRY(L, hipMemcpyAsync(L->slots[slot], L->experts[e].host, bytes, hipMemcpyHostToDevice, L->side),
-                        "expert H2D");
-                pt[e] = L->slots[slot];
-                L->last_bytes += static_cast<int64_t>(bytes);
+            std::vector<int> batch_slots;
+            if (b < n_hit_batches) {
+                for (int e : hits) {
+                    const int slot = L->expert_slot[e];
+                    pt[e] = L->slots[slot];
+                    slot_batch[slot] = b;
+                    batch_slots.push_back(slot);
+                }
+            } else {
+                const int first = (b - n_hit_batches) * kBatchExperts;
+                const int last = std::min<int>(static_cast<int>(misses.size()), first + kBatchExperts);
+                for (int i = first; i < last; ++i) {
+                    const int e = misses[i];
+                    const int slot = pick_slot(b);
+                    if (slot_batch[slot] >= 0)       // read earlier in this call: after those kernels
+                        HIP_TRY(L, hipStreamWaitEvent(L->side, L->slot_free[slot], 0), "slot wait");
+                    if (L->slot_expert[slot] >= 0) L->expert_slot[L->slot_expert[slot]] = -1;
+                    L->slot_expert[slot] = -1;
+                    HIP_TRY(L, hipMemcpyAsync(L->slots[slot], L->experts[e].host, bytes, hipMemcpyHostToDevice,
+                                              L->side),
+                            "expert H2D");
+                    if (cache) {
+                        L->slot_expert[slot] = e;
+                        L->expert_slot[e] = slot;
+                    }
+                    pt[e] = L->slots[slot];
+                    slot_batch[slot] = b;
+                    batch_slots.push_back(slot);
+                    L->last_bytes += static_cast<int64_t>(bytes);
+                }
+                HIP_TRY(L, hipEventRecord(L->batch_ready[b], L->side), "batch event");
+                HIP_TRY(L, hipStreamWaitEvent(s, L->batch_ready[b], 0), "batch wait");
             }
-            HIP_TRY(L, hipEventRecord(L->batch_ready[b], L->side), "batch event");
-            HIP_TRY(L, hipStreamWaitEvent(s, L->batch_ready[b], 0), "batch wait");
             HIP_TRY(L, hipMemcpyAsync(L->dev_tables[b], pt, tbytes, hipMemcpyHostToDevice, s), "batch table");
             FwdArgs ab = a;
             ab.table = L->dev_tables[b];
             if ((st = launch_experts(L, ab, path, s)) != COLI_OK) return st;
-            for (int i = first; i < last; ++i) {
-                const int slot = i % kSlotCount;
+            for (int slot : batch_slots) {
                 HIP_TRY(L, hipEventRecord(L->slot_free[slot], s), "slot event");
-                slot_used[slot] = true;
+                L->slot_stamp[slot] = call;
             }
         }
-        L->last_streamed = static_cast<int32_t>(streamed.size());
+        L->last_streamed = static_cast<int32_t>(misses.size());
+        L->last_hits = static_cast<int32_t>(hits.size());
     }
     {
         KernelMark m(L, COLI_K_COMBINE, s);
@@ -846,6 +907,24 @@ coli_status coli_layer_stream_stats(const coli_layer *L, int32_t *n_streamed, in
     if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
     if (n_streamed) *n_streamed = L->last_streamed;
     if (bytes) *bytes = L->last_bytes;
+    return COLI_OK;
+}
+
+coli_status coli_layer_set_stream_cache(coli_layer *L, int32_t n_slots) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (n_slots != 0 && (n_slots < kBatchExperts || n_slots > L->d.n_experts))
+        return fail(L, COLI_E_INVALID, "n_slots %d: 0 or %d..%d", n_slots, kBatchExperts, L->d.n_experts);
+    L->cache_slots = n_slots;
+    for (auto &x : L->slot_expert) x = -1;
+    for (auto &x : L->slot_stamp) x = 0;
+    for (auto &x : L->expert_slot) x = -1;
+    return COLI_OK;
+}
+
+coli_status coli_layer_stream_hits(const coli_layer *L, int32_t *hits) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (!hits) return fail(const_cast<coli_layer *>(L), COLI_E_INVALID, "hits is NULL");
+    *hits = L->last_hits;
     return COLI_OK;
 }
 
