@@ -75,7 +75,7 @@ typedef enum {
 typedef enum { COLI_ACT_F32 = 0, COLI_ACT_BF16 = 1 } coli_act;
 typedef enum { COLI_TIER_VRAM = 0, COLI_TIER_HOST = 1 } coli_tier;
 
-/* Forward strategy.  AUTO picks the VALU GEMV path for n_tok <= 2 and the
+/* Forward strategy.  AUTO picks the VALU GEMV path for n_tok <= 4 and the
  * grouped MFMA path otherwise.  Both give results within tolerance of the
  * definition; for a given strategy results are deterministic. */
 typedef enum {

@@ -83,6 +83,9 @@ TINY = Spec("tiny_h256_i128_e16_k4_b8", 256, 128, 16, 4, 8, "f32", False,
             "gauss", seed=20261203 + 0)
 DECODE_B1 = Spec("decode_b1_h6144_i2048_e256_k8", n_tok=1, routing="gauss",
                  seed=20261203 + 1, **_BIG)
+# Four tokens of one sequence per call: the speculative-verify batch.
+DECODE_B4 = Spec("decode_b4_h6144_i2048_e256_k8", n_tok=4, routing="gauss",
+                 seed=20261203 + 1, **_BIG)
 DECODE_B64 = Spec("decode_b64_zipf_h6144_i2048_e256_k8", n_tok=64,
                   routing="zipf", seed=20261203 + 2, **_BIG)
 PREFILL_B4096 = Spec("prefill_b4096_h6144_i2048_e256_k8", n_tok=4096,

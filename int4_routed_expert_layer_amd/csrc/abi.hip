@@ -328,7 +328,7 @@ bool all_routed_resident(const coli_layer *L) {
 
 int choose_path(const coli_layer *L, int n_tok) {
     if (L->path != COLI_PATH_AUTO) return L->path;
-    return n_tok <= 2 ? COLI_PATH_GEMV : COLI_PATH_GROUPED;
+    return n_tok <= 4 ? COLI_PATH_GEMV : COLI_PATH_GROUPED;   // B=4: 183 us GEMV, 203 us grouped
 }
 
 FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, const int32_t *n_union,

@@ -197,7 +197,9 @@ hipError_t launch_router_logits(const void *x, int act_bf16, const float *wt,
     if (n_tok <= 2)
         return launch_logits_t<1, 1, 32>(x, act_bf16, wt, bias, n_tok, hidden,
                                          n_experts, logits, s);
-    if (n_tok <= 32)
+    // Up to 128 tokens, small tiles: more waves, each with a shorter load chain
+    // (at 64 tokens 21 us instead of 38 us with the 8 x 8 tiles).
+    if (n_tok <= 128)
         return launch_logits_t<4, 2, 8>(x, act_bf16, wt, bias, n_tok, hidden,
                                         n_experts, logits, s);
     return launch_logits_t<8, 8, 4>(x, act_bf16, wt, bias, n_tok, hidden,
