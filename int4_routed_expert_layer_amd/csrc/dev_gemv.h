@@ -176,6 +176,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
         for (int m = 0; m < MAXM; ++m) gacc[m] = vacc[m] = 0.0f;
 
         GateUpBuf<NG> A, B;
+        bool b_issued = false;
         if (a.act_bf16 && (H * 2) % 1024 == 0) {
             // bf16 rows are copied straight into the staging area (1 KB per
             // wave instruction) before the weight loads are issued; the wait
@@ -195,10 +196,16 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                 copy16_to_lds(static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * H + part * 512 + 8 * lane,
                               lds_addr + static_cast<uint32_t>((m * H + part * 512) * 2));
             }
-            gateup_load(A, P, wave, 4, C);      // weights do not depend on x
+            // Both weight buffers go out before the wait (weights do not
+            // depend on x): twice the bytes in flight while x lands.  Lookahead
+            // past the last chunk repeats it (never used), so the count of
+            // loads behind the copies is always 8 NG.
+            gateup_load(A, P, wave, 4, C);
+            gateup_load(B, P, wave + 4 * NG, 4, C);
+            b_issued = true;
             // Plain barriers here: __syncthreads' fence would also wait for
             // the weight loads just issued.
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NG) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * NG) : "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             for (int i = tid; i < mc * (H / 8); i += 256) {
@@ -244,7 +251,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
         }
         // i indexes this wave's chunk list; buffers alternate A, B.
         for (int i = 0; i < nper; i += 2 * NG) {
-            if (i + NG < nper) gateup_load(B, P, wave + 4 * (i + NG), 4, C);
+            if (i + NG < nper && (i > 0 || !b_issued)) gateup_load(B, P, wave + 4 * (i + NG), 4, C);
             gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(NG, nper - i), kq, mc, M0, M1, G,
                               gacc, vacc);
             if (i + 2 * NG < nper) gateup_load(A, P, wave + 4 * (i + 2 * NG), 4, C);
@@ -372,6 +379,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
         DownBuf A, B;
+        bool b_issued = false;
         if (mb == 0) before_h();
         __syncthreads();                        // the previous row block is done with hs
         if ((I * 2) % 1024 == 0) {
@@ -384,8 +392,12 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
                 copy16_to_lds(a.h + static_cast<size_t>(r0 + mb + m) * I + part * 512 + 8 * lane,
                               lds_addr + static_cast<uint32_t>((m * I + part * 512) * 2));
             }
+            // Both weight buffers go out before the wait, as in gateup_panel
+            // (lookahead past the half's last chunk is clamped and unused).
             down_load(A, rs, vq, vs, sq, ss, c_begin, C);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPipeGroup) : "memory");
+            down_load(B, rs, vq, vs, sq, ss, c_begin + kPipeGroup, C);
+            b_issued = true;
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kPipeGroup) : "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             for (int i = tid; i < mc * (I / 8); i += 256) {
@@ -416,7 +428,8 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
             __syncthreads();
         }
         for (int i = 0; i < nper; i += 2 * kPipeGroup) {
-            if (i + kPipeGroup < nper) down_load(B, rs, vq, vs, sq, ss, c_begin + i + kPipeGroup, C);
+            if (i + kPipeGroup < nper && (i > 0 || !b_issued))
+                down_load(B, rs, vq, vs, sq, ss, c_begin + i + kPipeGroup, C);
             down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), kq, mc, M0, M1, G, acc);
             if (i + 2 * kPipeGroup < nper) down_load(A, rs, vq, vs, sq, ss, c_begin + i + 2 * kPipeGroup, C);
             if (i + kPipeGroup < nper)
