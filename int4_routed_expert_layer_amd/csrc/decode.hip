@@ -7,10 +7,12 @@
 //   * the last router block to finish (arrival counter) selects the top-k of
 //     every token and builds the union, so the routed gate/up kernel can
 //     start right after this launch.
-// Top-k: each wave ranks its 64 candidates locally (keys are unique:
-// (logit desc, id asc)), the k best of each wave are the only possible
-// winners, and ranking those 4k finalists gives the global slots.  Union:
-// LDS histogram, block scans, and an in-order rank for the gather.
+// Top-k, keys (logit desc, id asc), unique per expert: one token -- each
+// wave ranks its 64 candidates, the k best of each wave are the only
+// possible winners, and ranking those 4k finalists gives the slots; two to
+// four tokens -- one wave per token takes k rounds of a wave-wide max.
+// Union: an LDS histogram, one block scan, and an in-order rank for the
+// gather (one token needs no scan at all).
 #include "dev_gemv.h"
 
 #pragma clang fp contract(off)
@@ -74,86 +76,10 @@ __device__ __forceinline__ void wave_router(const FwdArgs &a, const FrontArgs &f
     }
 }
 
-// Top-k of every token and the union, by the last router block.
-__device__ void select_and_union(const FwdArgs &a, const FrontArgs &f) {
-    __shared__ uint64_t s_key[kFrontMaxExperts];
-    __shared__ uint64_t s_fin[4 * kMaxTopK];
-    __shared__ float s_sig[kMaxTopK];
-    __shared__ int s_idx[kFrontMaxTok * kMaxTopK];
-    __shared__ int s_cnt[kFrontMaxExperts];
-    __shared__ int s_off[kFrontMaxExperts];
-    __shared__ int s_tmp[kFrontThreads / 64 + 1];
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int E = a.n_experts, k = a.k, n_tok = a.n_tok;
-    for (int t = 0; t < n_tok; ++t) {
-        // key = (logit order, then lower id first); unique per expert.
-        const uint32_t low = 0xFFFFFFFFu - static_cast<uint32_t>(tid);
-        uint64_t key = low;
-        if (tid < E)
-            key |= static_cast<uint64_t>(dev::float_key(dev::load_coherent(f.logits + static_cast<size_t>(t) * E + tid)))
-                   << 32;
-        s_key[tid] = key;
-        __syncthreads();
-        int r = 0;
-        for (int j = 0; j < 64; ++j) r += s_key[64 * wave + j] > key ? 1 : 0;
-        if (r < k) s_fin[wave * k + r] = key;
-        __syncthreads();
-        if (tid < 4 * k) {
-            const uint64_t fk = s_fin[tid];
-            int R = 0;
-            for (int j = 0; j < 4 * k; ++j) R += s_fin[j] > fk ? 1 : 0;
-            if (R < k) {
-                const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(fk));
-                // The key's high word is the order-preserving image of the
-                // logit (-0 folded to +0, which has the same sigmoid).
-                const uint32_t kh = static_cast<uint32_t>(fk >> 32);
-                const float l = __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
-                s_idx[t * k + R] = e;
-                f.topk_idx[static_cast<size_t>(t) * k + R] = e;
-                s_sig[R] = 1.0f / (1.0f + expf(-l));
-            }
-        }
-        __syncthreads();
-        if (tid < k) {
-            float sum = 0.0f;
-            for (int j = 0; j < k; ++j) sum = sum + s_sig[j];
-            f.topk_w[static_cast<size_t>(t) * k + tid] = s_sig[tid] / sum;
-        }
-        __syncthreads();
-    }
-    // Union of the n_tok * k selections.
-    const int n_ent = n_tok * k;
-    s_cnt[tid] = 0;
-    __syncthreads();
-    if (tid < n_ent) atomicAdd(&s_cnt[s_idx[tid]], 1);
-    __syncthreads();
-    const int c = tid < E ? s_cnt[tid] : 0;
-    int total = 0;
-    const int excl = dev::block_exclusive_scan<kFrontThreads>(c, s_tmp, &total);
-    if (tid < E) {
-        f.counts[tid] = c;
-        f.offsets[tid] = excl;
-        s_off[tid] = excl;
-    }
-    if (tid == 0) f.offsets[E] = total;
-    const int flag = (tid < E && c > 0) ? 1 : 0;
-    int nu = 0;
-    const int pos = dev::block_exclusive_scan<kFrontThreads>(flag, s_tmp, &nu);
-    if (flag) f.union_ids[pos] = tid;
-    if (tid == 0) *f.n_union = nu;
-    __syncthreads();
-    if (tid < n_ent) {
-        const int e = s_idx[tid];
-        int before = 0;
-        for (int i = 0; i < tid; ++i) before += s_idx[i] == e ? 1 : 0;
-        f.gather[s_off[e] + before] = tid;
-    }
-}
-
-// One token: the same top-k and weights; its union needs no scans, as the k
-// selected experts are distinct: expert e has count 1 if selected, offset =
-// number of selected experts below e, and its single entry is the slot that
-// chose it.
+// One token: top-k by ranks within waves and among the finalists, weights in
+// rank order; its union needs no scans, as the k selected experts are
+// distinct: expert e has count 1 if selected, offset = number of selected
+// experts below e, and its single entry is the slot that chose it.
 __device__ void select_one_token(const FwdArgs &a, const FrontArgs &f) {
     __shared__ uint64_t s_key[kFrontMaxExperts];
     __shared__ uint64_t s_fin[4 * kMaxTopK];
@@ -208,6 +134,87 @@ __device__ void select_one_token(const FwdArgs &a, const FrontArgs &f) {
     }
 }
 
+// Two to kFrontMaxTok tokens: wave t selects token t's experts (lane l holds
+// the keys of experts l, l + 64, ...; k rounds of a wave-wide max, the same
+// selection and weights as the standalone top-k), then the union with one
+// block scan of counts and union flags packed together.
+__device__ void select_few_tokens(const FwdArgs &a, const FrontArgs &f) {
+    __shared__ int s_idx[kFrontMaxTok * kMaxTopK];
+    __shared__ int s_cnt[kFrontMaxExperts];
+    __shared__ int s_off[kFrontMaxExperts];
+    __shared__ int s_tmp[kFrontThreads / 64 + 1];
+    constexpr int kEpl = kFrontMaxExperts / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.n_experts, k = a.k, n_tok = a.n_tok;
+    if (wave < n_tok) {
+        const int t = wave;
+        uint64_t key[kEpl];
+#pragma unroll
+        for (int j = 0; j < kEpl; ++j) {
+            const int e = lane + 64 * j;
+            key[j] = e < E ? (static_cast<uint64_t>(dev::float_key(dev::load_coherent(f.logits + t * E + e))) << 32) |
+                                 (0xFFFFFFFFu - static_cast<uint32_t>(e))
+                           : 0ull;
+        }
+        int my_e = 0;
+        float my_sig = 0.0f, sum = 0.0f;
+        for (int r = 0; r < k; ++r) {
+            uint64_t best = key[0];
+#pragma unroll
+            for (int j = 1; j < kEpl; ++j) best = key[j] > best ? key[j] : best;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint64_t other = __shfl_xor(best, o, 64);
+                best = other > best ? other : best;
+            }
+            const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+#pragma unroll
+            for (int j = 0; j < kEpl; ++j)
+                if (lane + 64 * j == e) key[j] = 0ull;
+            const uint32_t kh = static_cast<uint32_t>(best >> 32);
+            const float l = __uint_as_float((kh & 0x80000000u) ? (kh & 0x7fffffffu) : ~kh);
+            const float sg = 1.0f / (1.0f + expf(-l));
+            sum = sum + sg;
+            if (lane == r) {
+                my_e = e;
+                my_sig = sg;
+            }
+        }
+        if (lane < k) {
+            s_idx[t * k + lane] = my_e;
+            f.topk_idx[t * k + lane] = my_e;
+            f.topk_w[t * k + lane] = my_sig / sum;
+        }
+    }
+    s_cnt[tid] = 0;
+    __syncthreads();
+    const int n_ent = n_tok * k;
+    if (tid < n_ent) atomicAdd(&s_cnt[s_idx[tid]], 1);
+    __syncthreads();
+    // counts (< 2^16) in the low half, union flags in the high half: one scan
+    // gives both the offsets and the union positions.
+    const int c = tid < E ? s_cnt[tid] : 0;
+    int total = 0;
+    const int excl = dev::block_exclusive_scan<kFrontThreads>(c | ((c > 0 ? 1 : 0) << 16), s_tmp, &total);
+    if (tid < E) {
+        f.counts[tid] = c;
+        f.offsets[tid] = excl & 0xFFFF;
+        s_off[tid] = excl & 0xFFFF;
+        if (c > 0) f.union_ids[excl >> 16] = tid;
+    }
+    if (tid == 0) {
+        f.offsets[E] = total & 0xFFFF;
+        *f.n_union = total >> 16;
+    }
+    __syncthreads();
+    if (tid < n_ent) {
+        const int e = s_idx[tid];
+        int before = 0;
+        for (int i = 0; i < tid; ++i) before += s_idx[i] == e ? 1 : 0;
+        f.gather[s_off[e] + before] = tid;
+    }
+}
+
 template <int NT, bool BF16>
 __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, FrontArgs f, int router_blocks) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
     if (e < a.n_experts) wave_router<NT, BF16>(a, f, e);
     if (dev::arrive_last(f.counter, router_blocks)) {
         if (a.n_tok == 1) select_one_token(a, f);
-        else select_and_union(a, f);
+        else select_few_tokens(a, f);
     }
 }
 
