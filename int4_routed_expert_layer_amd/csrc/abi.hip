@@ -914,7 +914,19 @@ coli_status coli_layer_set_stream_cache(coli_layer *L, int32_t n_slots) {
     if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
     if (n_slots != 0 && (n_slots < kBatchExperts || n_slots > L->d.n_experts))
         return fail(L, COLI_E_INVALID, "n_slots %d: 0 or %d..%d", n_slots, kBatchExperts, L->d.n_experts);
+    DeviceGuard guard(L->device);
     L->cache_slots = n_slots;
+    // Slots past the new need are released (every tiered call ended with a
+    // synchronisation, so none is in use).
+    const size_t keep = static_cast<size_t>(std::max(kSlotCount, n_slots));
+    while (L->slots.size() > keep) {
+        (void)hipFree(L->slots.back());
+        (void)hipEventDestroy(L->slot_free.back());
+        L->slots.pop_back();
+        L->slot_free.pop_back();
+        L->slot_expert.pop_back();
+        L->slot_stamp.pop_back();
+    }
     for (auto &x : L->slot_expert) x = -1;
     for (auto &x : L->slot_stamp) x = 0;
     for (auto &x : L->expert_slot) x = -1;

@@ -93,4 +93,25 @@ def test_stream_cache_size_is_checked():
             L.set_stream_cache(bad)
     L.set_stream_cache(0)
     L.set_stream_cache(SPEC.n_experts)
+    L.set_stream_cache(4)          # shrinking releases the slots past the need
+    L.close()
+
+
+def test_stream_cache_survives_resizing():
+    """A large cache, then a small one, then none: every call still gives the
+    all-VRAM bits (slots released on shrinking are never used again)."""
+    data = Data(SPEC, n_tok=SPEC.n_tok * 3)
+    mask = inputs.resident_mask(SPEC, 0)
+    tiers = [B.TIER_VRAM if mask[e] else B.TIER_HOST for e in range(SPEC.n_experts)]
+    ref = make_layer(B, data, max_tokens=SPEC.n_tok)
+    L = make_layer(B, data, tiers=tiers, max_tokens=SPEC.n_tok)
+    for c, slots in enumerate((32, 4, 0)):
+        L.set_stream_cache(slots)
+        x = B.activations_to_device(data.x[c * SPEC.n_tok:(c + 1) * SPEC.n_tok])
+        for _ in range(2):
+            y_ref, _ = run(ref, x)
+            y, _ = run(L, x)
+            assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32)), slots
+    assert L.device_errors() == 0
+    ref.close()
     L.close()
