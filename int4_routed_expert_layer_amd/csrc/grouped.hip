@@ -307,24 +307,30 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     // chunk (chunk c to queue c mod 8) and taken dynamically: workgroup b
     // draws from queue b mod 8, which on an 8-XCD part is the queue of its
     // XCD, so the N-blocks of a chunk (same activation rows) share an L2.
-    // Items differ in cost (chunks of 1 to 160 rows); dynamic claiming keeps
-    // every workgroup busy until its queue is empty.
+    // Items differ in cost (chunks of 1 to 160 rows) and the queues in total
+    // work; dynamic claiming keeps every workgroup busy until its queue is
+    // empty, and then it takes items from the other queues in turn.
     const int nq = gridDim.x >= kGroupedQueues ? kGroupedQueues : 1;
-    const int q = blockIdx.x % nq;
     const int n_chunks = *a.n_chunks;
-    const int q_items = (n_chunks > q ? (n_chunks - q + nq - 1) / nq : 0) * NB;
-    int32_t *ticket = a.queues + q * kQueueStride;
+    int qq = static_cast<int>(blockIdx.x) % nq, tried = 0;
     __shared__ int s_item;
 
     for (;;) {
         __syncthreads();       // every thread has read the previous s_item
-        if (tid == 0) s_item = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0)
+            s_item = __hip_atomic_fetch_add(a.queues + qq * kQueueStride, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         // Uniform across the workgroup: everything derived from it (chunk,
         // blob, descriptor, offsets) then lives in scalar registers.
         const int j = __builtin_amdgcn_readfirstlane(s_item);
-        if (j >= q_items) break;
-        const int item = (q + nq * (j / NB)) * NB + j % NB;
+        const int q_items = (n_chunks > qq ? (n_chunks - qq + nq - 1) / nq : 0) * NB;
+        if (j >= q_items) {
+            if (++tried >= nq) break;
+            qq = qq + 1 < nq ? qq + 1 : 0;   // this queue is empty: the next one
+            continue;
+        }
+        const int item = (qq + nq * (j / NB)) * NB + j % NB;
         const int chunk = item / NB, nb = item % NB;
         // The chunk descriptor and the blob pointer are read by every lane
         // from one address; readfirstlane makes them scalar, so the weight
