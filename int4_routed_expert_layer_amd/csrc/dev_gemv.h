@@ -74,6 +74,13 @@ __host__ __device__ inline size_t gateup_lds_bytes(int maxm, int hidden) {
     return static_cast<size_t>(maxm) * hidden * 2 + static_cast<size_t>(maxm) * (hidden / 8) * 4 +
            static_cast<size_t>(4) * maxm * 16 * 2 * 4;
 }
+// LDS floats the fused combine gets: the down item's LDS, and at least one
+// token's rows (k routed + shared) of a 32-column panel pair.
+__host__ __device__ inline size_t combine_lds_floats(size_t down_bytes, int k, int has_shared) {
+    const size_t one_token = static_cast<size_t>(2 * kPanel) * (k + (has_shared ? 1 : 0));
+    return down_bytes / sizeof(float) > one_token ? down_bytes / sizeof(float) : one_token;
+}
+
 __host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
     return static_cast<size_t>(maxm) * inter * 2 + static_cast<size_t>(maxm) * (inter / 8) * 4 +
            static_cast<size_t>(4) * maxm * 16 * 4;

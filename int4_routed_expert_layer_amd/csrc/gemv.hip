@@ -39,8 +39,9 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
         const int units = *a.n_union + (a.has_shared ? 1 : 0);
         // The last workgroup of the panel pair reuses its (now idle) LDS.
         if (dev::arrive_last(counters + pg, units))
-            dev::combine_panelgroup(a, pg, reinterpret_cast<float *>(lds),
-                                    static_cast<int>(dev::down_lds_bytes(MAXM, a.inter) / sizeof(float)));
+            dev::combine_panelgroup(
+                a, pg, reinterpret_cast<float *>(lds),
+                static_cast<int>(dev::combine_lds_floats(dev::down_lds_bytes(MAXM, a.inter), a.k, a.has_shared)));
     }
 }
 
@@ -70,7 +71,8 @@ hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, i
 hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s, int32_t *combine_counters) {
     int maxm = pick_maxm(a.n_tok);
     while (maxm > 1 && dev::down_lds_bytes(maxm, a.inter) > max_lds) maxm >>= 1;
-    const size_t lds = dev::down_lds_bytes(maxm, a.inter);
+    size_t lds = dev::down_lds_bytes(maxm, a.inter);
+    if (combine_counters) lds = sizeof(float) * dev::combine_lds_floats(lds, a.k, a.has_shared);
     if (lds > max_lds) return hipErrorInvalidValue;
     const int grid = units_bound(a) * (a.hidden / (2 * kPanel));
     if (combine_counters) {

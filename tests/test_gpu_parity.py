@@ -127,6 +127,36 @@ def test_fused_layer_small_batches(n_tok, act):
     L.close()
 
 
+@pytest.mark.parametrize("E,k", [(37, 5), (100, 32), (256, 32), (256, 1)])
+@pytest.mark.parametrize("n_tok", [1, 3, 4])
+def test_fused_layer_odd_shapes(E, k, n_tok):
+    """The one-launch front with expert counts that are not a multiple of the
+    64-wide waves (partly empty router blocks and selection lanes) and with
+    the largest k: bit-identical to the three separate calls, and routing and
+    output against the oracle."""
+    spec = MEDIUM.with_(name=f"fused_e{E}_k{k}", n_experts=E, top_k=k, routing="gauss")
+    data = Data(spec, n_tok=n_tok)
+    log(f"case fused odd shape E={E} k={k} n_tok={n_tok}")
+    L = make_layer(B, data)
+    x = B.activations_to_device(data.x)
+    y, idx, w, u = L.layer(x)
+    torch.cuda.synchronize()
+    assert L.device_errors() == 0
+    three = gpu_run(B, L, data, with_logits=False)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), three["y"].view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), three["idx"])
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), three["weight"].view(np.uint32))
+    nu = int(u["n_union"].cpu()[0])
+    assert nu == three["n_union"]
+    np.testing.assert_array_equal(u["gather"].cpu().numpy(), three["gather"])
+    np.testing.assert_array_equal(u["offsets"].cpu().numpy(), three["offsets"])
+    np.testing.assert_array_equal(u["counts"].cpu().numpy(), three["counts"])
+    ref = oracle_route(data)
+    check_routing(three, ref, check_logits=False)
+    check_outputs(y.cpu().numpy(), oracle_y(data, ref, range(n_tok)), f"fused E={E} k={k} n={n_tok}")
+    L.close()
+
+
 def test_fused_layer_alternating_sizes():
     """One layer, fused calls of changing batch size back to back: the launch
     counters must be clean after every call."""
