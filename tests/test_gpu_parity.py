@@ -54,6 +54,17 @@ def test_medium_single_token(path):
     full_check(MEDIUM, path, n_tok=1)
 
 
+@pytest.mark.parametrize("path", ["gemv", "grouped", None])
+@pytest.mark.parametrize("hidden,inter,n_tok", [(384, 384, 3), (640, 128, 29), (384, 640, 45)])
+def test_hidden_not_multiple_of_256(path, hidden, inter, n_tok):
+    # A hidden width of 128 mod 256 leaves the grouped down pass a last
+    # 256-column block that is half empty; odd multiples of 128 for the
+    # intermediate width give gate/up an odd block count.
+    spec = MEDIUM.with_(name=f"h{hidden}_i{inter}_e24_k6_b{n_tok}", hidden=hidden, inter=inter,
+                        n_experts=24, top_k=6, n_tok=n_tok, has_shared=True, act="bf16")
+    full_check(spec, path)
+
+
 def test_special_case_e1_k1():
     full_check(configs.TINY.with_(n_experts=1, top_k=1, has_shared=True, act="bf16"), "gemv")
     full_check(configs.TINY.with_(n_experts=1, top_k=1, has_shared=True, act="bf16"), "grouped")
