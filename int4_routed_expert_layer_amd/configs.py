@@ -15,8 +15,11 @@ from __future__ import annotations
 
 from dataclasses import dataclass, replace
 
-# Int4 weights carry one fp16 scale per 32 consecutive reduction elements.
+# Int4 weights carry one fp16 scale per GROUP consecutive reduction elements
+# (32 in the fixed workloads; the container the README's "Scarica il modello"
+# section ships uses 64, which GROUPS also allows).
 GROUP = 32
+GROUPS = (32, 64)
 # Every section of an expert blob starts on a 256-byte boundary.
 BLOB_ALIGN = 256
 
@@ -37,6 +40,7 @@ class Spec:
     seed: int = 20261203
     zipf_s: float = 1.1
     zipf_gamma: float = 0.648
+    group: int = GROUP           # reduction elements per fp16 weight scale
 
     @property
     def act_bytes(self) -> int:
@@ -50,19 +54,19 @@ def _align(n: int) -> int:
     return (n + BLOB_ALIGN - 1) // BLOB_ALIGN * BLOB_ALIGN
 
 
-def blob_sections(hidden: int, inter: int) -> dict:
+def blob_sections(hidden: int, inter: int, group: int = GROUP) -> dict:
     """Byte offset and size of each section of one expert blob.
 
     Order: gate nibbles, up nibbles, down nibbles, gate scales, up scales,
     down scales.  Gate and up are [I x H] (output rows x reduction), down is
     [H x I]; nibbles are row-major along the reduction axis, two per byte,
-    element 2j in the low nibble; scales are fp16 [rows x K/32].
+    element 2j in the low nibble; scales are fp16 [rows x K/group].
     """
     h, i = hidden, inter
     sizes = [
         ("gate_q", i * h // 2), ("up_q", i * h // 2), ("down_q", h * i // 2),
-        ("gate_s", i * (h // GROUP) * 2), ("up_s", i * (h // GROUP) * 2),
-        ("down_s", h * (i // GROUP) * 2),
+        ("gate_s", i * (h // group) * 2), ("up_s", i * (h // group) * 2),
+        ("down_s", h * (i // group) * 2),
     ]
     out, off = {}, 0
     for name, size in sizes:
@@ -72,8 +76,8 @@ def blob_sections(hidden: int, inter: int) -> dict:
     return out
 
 
-def blob_bytes(hidden: int, inter: int) -> int:
-    return blob_sections(hidden, inter)["total"][1]
+def blob_bytes(hidden: int, inter: int, group: int = GROUP) -> int:
+    return blob_sections(hidden, inter, group)["total"][1]
 
 
 _BIG = dict(hidden=6144, inter=2048, n_experts=256, top_k=8, act="bf16",

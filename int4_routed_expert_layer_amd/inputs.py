@@ -105,7 +105,7 @@ def expert_blob(spec: Spec, layer: int, expert: int) -> np.ndarray:
         raise ValueError(f"expert {expert} out of range")
     if expert == SHARED and not spec.has_shared:
         raise ValueError("spec has no shared expert")
-    sec = blob_sections(spec.hidden, spec.inter)
+    sec = blob_sections(spec.hidden, spec.inter, spec.group)
     blob = np.zeros(sec["total"][1], dtype=np.uint8)
     g = rng(spec, layer, stream)
     for name in ("gate_q", "up_q", "down_q"):

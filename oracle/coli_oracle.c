@@ -29,8 +29,10 @@
  *           prefix sum of counts; gather = entries t*k+j ordered by
  *           (expert asc, token asc).  The shared expert is not in the union.
  *  Experts  int4 two's-complement nibbles (element 2j low nibble, 2j+1 high
- *           nibble), one fp16 scale per 32 consecutive reduction elements,
- *           w = q * s exactly in fp64.  SwiGLU: h = silu(Wg x) * (Wu x),
+ *           nibble), one fp16 scale per `group` consecutive reduction
+ *           elements (32 in the fixed configurations; 64 in the container the
+ *           README's "Scarica il modello" section ships), w = q * s exactly
+ *           in fp64.  The scale sections hold [rows x K/group] fp16.  SwiGLU: h = silu(Wg x) * (Wu x),
  *           silu(z) = z * sigmoid(z), y_e = Wd h, all fp64.
  *  Combine  y_t = sum_j w_j * y_{e_j}(x_t) + y_shared(x_t), fp64, where the
  *           shared expert (one always-on expert of the same shape) has
@@ -43,8 +45,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 1
-#define GROUP 32
+#define ORACLE_ABI_VERSION 2
 #define ALIGN 256
 
 int coli_oracle_version(void) { return ORACLE_ABI_VERSION; }
@@ -210,13 +211,13 @@ static size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 /* Section offsets of a canonical blob: gate_q, up_q, down_q, gate_s, up_s,
  * down_s, total. */
-static void blob_offsets(int hidden, int inter, size_t off[7])
+static void blob_offsets(int hidden, int inter, int group, size_t off[7])
 {
     size_t sz[6] = {
         (size_t)inter * hidden / 2, (size_t)inter * hidden / 2,
         (size_t)hidden * inter / 2,
-        (size_t)inter * (hidden / GROUP) * 2, (size_t)inter * (hidden / GROUP) * 2,
-        (size_t)hidden * (inter / GROUP) * 2,
+        (size_t)inter * (hidden / group) * 2, (size_t)inter * (hidden / group) * 2,
+        (size_t)hidden * (inter / group) * 2,
     };
     size_t o = 0;
     for (int i = 0; i < 6; ++i) {
@@ -226,34 +227,42 @@ static void blob_offsets(int hidden, int inter, size_t off[7])
     off[6] = o;
 }
 
-size_t coli_oracle_blob_bytes(int hidden, int inter)
+/* A group size the layout supports: positive and dividing both widths. */
+static int group_ok(int hidden, int inter, int group)
+{
+    return group > 0 && hidden > 0 && inter > 0 && hidden % group == 0 && inter % group == 0;
+}
+
+size_t coli_oracle_blob_bytes(int hidden, int inter, int group)
 {
     size_t off[7];
-    blob_offsets(hidden, inter, off);
+    if (!group_ok(hidden, inter, group))
+        return 0;
+    blob_offsets(hidden, inter, group, off);
     return off[6];
 }
 
 /* Row r of a [rows x K] int4 matrix with fp16 group scales, dequantised to
- * fp64: out[k] = q[r][k] * s[r][k / 32]. */
-static void dequant_row(const uint8_t *q, const uint16_t *s, int K, int r,
+ * fp64: out[k] = q[r][k] * s[r][k / group]. */
+static void dequant_row(const uint8_t *q, const uint16_t *s, int K, int group, int r,
                         double *out)
 {
     const uint8_t *row = q + (size_t)r * (K / 2);
-    const uint16_t *srow = s + (size_t)r * (K / GROUP);
-    for (int g = 0; g < K / GROUP; ++g) {
+    const uint16_t *srow = s + (size_t)r * (K / group);
+    for (int g = 0; g < K / group; ++g) {
         double scale = half_bits_to_double(srow[g]);
-        for (int k = g * GROUP; k < (g + 1) * GROUP; ++k)
+        for (int k = g * group; k < (g + 1) * group; ++k)
             out[k] = (double)nibble_at(row, k) * scale;
     }
 }
 
 /* y[H] = SwiGLU expert applied to x[H], all fp64.  scratch >= I + 2*H
  * doubles. */
-static void expert_ffn(const uint8_t *blob, int hidden, int inter,
+static void expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
                        const double *x, double *y, double *scratch)
 {
     size_t off[7];
-    blob_offsets(hidden, inter, off);
+    blob_offsets(hidden, inter, group, off);
     const uint8_t *gq = blob + off[0], *uq = blob + off[1], *dq = blob + off[2];
     const uint16_t *gs = (const uint16_t *)(blob + off[3]);
     const uint16_t *us = (const uint16_t *)(blob + off[4]);
@@ -262,8 +271,8 @@ static void expert_ffn(const uint8_t *blob, int hidden, int inter,
     double *wa = scratch + inter;
     double *wb = wa + hidden;
     for (int r = 0; r < inter; ++r) {
-        dequant_row(gq, gs, hidden, r, wa);
-        dequant_row(uq, us, hidden, r, wb);
+        dequant_row(gq, gs, hidden, group, r, wa);
+        dequant_row(uq, us, hidden, group, r, wb);
         double g = 0.0, v = 0.0;
         for (int k = 0; k < hidden; ++k) {
             g += wa[k] * x[k];
@@ -272,7 +281,7 @@ static void expert_ffn(const uint8_t *blob, int hidden, int inter,
         h[r] = g * sigmoid(g) * v;
     }
     for (int n = 0; n < hidden; ++n) {
-        dequant_row(dq, ds, inter, n, wa);
+        dequant_row(dq, ds, inter, group, n, wa);
         double acc = 0.0;
         for (int r = 0; r < inter; ++r)
             acc += wa[r] * h[r];
@@ -280,34 +289,34 @@ static void expert_ffn(const uint8_t *blob, int hidden, int inter,
     }
 }
 
-int coli_oracle_expert_ffn(const uint8_t *blob, int hidden, int inter,
+int coli_oracle_expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
                            const double *x, double *y)
 {
-    if (hidden % GROUP || inter % GROUP)
+    if (!group_ok(hidden, inter, group))
         return -1;
     double *scratch = (double *)malloc(sizeof(double) * ((size_t)inter + 2 * (size_t)hidden));
     if (!scratch)
         return -2;
-    expert_ffn(blob, hidden, inter, x, y, scratch);
+    expert_ffn(blob, hidden, inter, group, x, y, scratch);
     free(scratch);
     return 0;
 }
 
 /* Dequantise one [rows x K] matrix of a blob to fp64 (row-major). which:
  * 0 gate, 1 up, 2 down. */
-int coli_oracle_dequant(const uint8_t *blob, int hidden, int inter, int which,
+int coli_oracle_dequant(const uint8_t *blob, int hidden, int inter, int group, int which,
                         double *out)
 {
     size_t off[7];
-    blob_offsets(hidden, inter, off);
-    if (which < 0 || which > 2)
+    if (which < 0 || which > 2 || !group_ok(hidden, inter, group))
         return -1;
+    blob_offsets(hidden, inter, group, off);
     int rows = which == 2 ? hidden : inter;
     int K = which == 2 ? inter : hidden;
     const uint8_t *q = blob + off[which];
     const uint16_t *s = (const uint16_t *)(blob + off[3 + which]);
     for (int r = 0; r < rows; ++r)
-        dequant_row(q, s, K, r, out + (size_t)r * K);
+        dequant_row(q, s, K, group, r, out + (size_t)r * K);
     return 0;
 }
 
@@ -317,11 +326,13 @@ int coli_oracle_dequant(const uint8_t *blob, int hidden, int inter, int which,
  * (idx, weight) of the whole batch.  blobs[e] must be non-NULL for every
  * expert some selected token routes to; shared may be NULL (no shared
  * expert). */
-int coli_oracle_layer_tokens(const void *x, int x_bf16, int hidden, int inter,
+int coli_oracle_layer_tokens(const void *x, int x_bf16, int hidden, int inter, int group,
                              int top_k, const int32_t *idx, const double *weight,
                              const uint8_t *const *blobs, const uint8_t *shared,
                              const int32_t *sel, int n_sel, double *y)
 {
+    if (!group_ok(hidden, inter, group))
+        return -1;
     double *xt = (double *)malloc(sizeof(double) * (size_t)hidden);
     double *ye = (double *)malloc(sizeof(double) * (size_t)hidden);
     double *scratch = (double *)malloc(sizeof(double) * ((size_t)inter + 2 * (size_t)hidden));
@@ -346,12 +357,12 @@ int coli_oracle_layer_tokens(const void *x, int x_bf16, int hidden, int inter,
                 return -1;
             }
             double w = weight[(size_t)t * top_k + j];
-            expert_ffn(blobs[e], hidden, inter, xt, ye, scratch);
+            expert_ffn(blobs[e], hidden, inter, group, xt, ye, scratch);
             for (int n = 0; n < hidden; ++n)
                 yt[n] += w * ye[n];
         }
         if (shared) {
-            expert_ffn(shared, hidden, inter, xt, ye, scratch);
+            expert_ffn(shared, hidden, inter, group, xt, ye, scratch);
             for (int n = 0; n < hidden; ++n)
                 yt[n] += ye[n];
         }

@@ -224,8 +224,8 @@ def test_union_matches_brute_force(seed, B, E, k):
 
 # ------------------------------------------------------------------ experts
 
-def numpy_dequant(blob, H, I, which):
-    sec = configs.blob_sections(H, I)
+def numpy_dequant(blob, H, I, which, group=32):
+    sec = configs.blob_sections(H, I, group)
     rows, K = (H, I) if which == "down" else (I, H)
     off, size = sec[which + "_q"]
     b = blob[off:off + size].reshape(rows, K // 2)
@@ -235,8 +235,8 @@ def numpy_dequant(blob, H, I, which):
     q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
     q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
     soff, ssize = sec[which + "_s"]
-    s = blob[soff:soff + ssize].view(np.float16).reshape(rows, K // 32).astype(np.float64)
-    return q * np.repeat(s, 32, axis=1)
+    s = blob[soff:soff + ssize].view(np.float16).reshape(rows, K // group).astype(np.float64)
+    return q * np.repeat(s, group, axis=1)
 
 
 def test_blob_size_matches_pages_scale():
@@ -245,35 +245,47 @@ def test_blob_size_matches_pages_scale():
     assert orc.blob_bytes(256, 128) == configs.blob_bytes(256, 128)
 
 
+def test_group64_blob_size():
+    # Group 64 halves the scale sections: 3*H*I/2 nibble bytes plus
+    # 3*H*I/64 fp16 scales (every section already 256-byte aligned here).
+    H, I = 6144, 2048
+    assert orc.blob_bytes(H, I, 64) == configs.blob_bytes(H, I, 64) == 3 * H * I // 2 + 3 * H * I // 64 * 2
+    assert orc.blob_bytes(384, 640, 64) == configs.blob_bytes(384, 640, 64)
+    with pytest.raises(ValueError):
+        orc.blob_bytes(6144, 2048, 48)      # 48 does not divide 2048
+
+
+@pytest.mark.parametrize("group", [32, 64])
 @pytest.mark.parametrize("which", ["gate", "up", "down"])
-def test_dequant_matches_numpy(which):
-    spec = configs.TINY
+def test_dequant_matches_numpy(which, group):
+    spec = configs.TINY.with_(group=group)
     blob = inputs.expert_blob(spec, 0, 3)
-    np.testing.assert_array_equal(orc.dequant(blob, spec.hidden, spec.inter, which),
-                                  numpy_dequant(blob, spec.hidden, spec.inter, which))
+    np.testing.assert_array_equal(orc.dequant(blob, spec.hidden, spec.inter, which, group),
+                                  numpy_dequant(blob, spec.hidden, spec.inter, which, group))
 
 
-def numpy_ffn(blob, H, I, x):
-    g = numpy_dequant(blob, H, I, "gate") @ x
-    v = numpy_dequant(blob, H, I, "up") @ x
+def numpy_ffn(blob, H, I, x, group=32):
+    g = numpy_dequant(blob, H, I, "gate", group) @ x
+    v = numpy_dequant(blob, H, I, "up", group) @ x
     h = g * expit(g) * v
-    return numpy_dequant(blob, H, I, "down") @ h
+    return numpy_dequant(blob, H, I, "down", group) @ h
 
 
-def test_expert_ffn_matches_numpy_matmul():
-    spec = configs.TINY
+@pytest.mark.parametrize("group", [32, 64])
+def test_expert_ffn_matches_numpy_matmul(group):
+    spec = configs.TINY.with_(group=group)
     rng = np.random.default_rng(11)
     for e in (0, 5):
         blob = inputs.expert_blob(spec, 0, e)
         x = rng.standard_normal(spec.hidden)
-        got = orc.expert_ffn(blob, spec.hidden, spec.inter, x)
-        ref = numpy_ffn(blob, spec.hidden, spec.inter, x)
+        got = orc.expert_ffn(blob, spec.hidden, spec.inter, x, group)
+        ref = numpy_ffn(blob, spec.hidden, spec.inter, x, group)
         assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
-def make_blob(H, I, gate_q, up_q, down_q, gate_s, up_s, down_s):
+def make_blob(H, I, gate_q, up_q, down_q, gate_s, up_s, down_s, group=32):
     """Canonical blob from explicit int4 matrices and fp16 scales."""
-    sec = configs.blob_sections(H, I)
+    sec = configs.blob_sections(H, I, group)
     blob = np.zeros(sec["total"][1], np.uint8)
     for name, q in (("gate_q", gate_q), ("up_q", up_q), ("down_q", down_q)):
         q = np.asarray(q, np.int64)
@@ -303,6 +315,42 @@ def test_swiglu_closed_form_with_permutation_weights():
     z = x[pi] * 2.0 ** (pi // 32)
     ref = z * expit(z) * x
     np.testing.assert_allclose(orc.expert_ffn(blob, H, I, x), ref, rtol=1e-15, atol=1e-300)
+
+
+def test_swiglu_closed_form_group64():
+    # As above with one scale per 64 columns: gate scales 1, 2, 4, 8 over
+    # the four 64-column groups of a 256-wide row, so
+    #   y[n] = silu(x[pi(n)] * 2^(pi(n)//64)) * x[n].
+    H = I = 256
+    rng = np.random.default_rng(13)
+    pi = rng.permutation(H)
+    gq = np.zeros((I, H), np.int64)
+    gq[np.arange(I), pi] = 1
+    eye = np.eye(H, dtype=np.int64)
+    gs = np.tile(np.array([1.0, 2.0, 4.0, 8.0]), (I, 1))
+    ones = np.ones((I, H // 64))
+    blob = make_blob(H, I, gq, eye, eye, gs, ones, np.ones((H, I // 64)), group=64)
+    x = rng.standard_normal(H)
+    z = x[pi] * 2.0 ** (pi // 64)
+    ref = z * expit(z) * x
+    np.testing.assert_allclose(orc.expert_ffn(blob, H, I, x, 64), ref, rtol=1e-15, atol=1e-300)
+
+
+def test_group64_is_group32_with_each_scale_repeated():
+    # A group-64 matrix is the group-32 matrix whose scale pairs are equal:
+    # same nibbles, each 64-group scale written twice, gives the same
+    # dequantised weights and the same FFN output, bit for bit.
+    H, I = 256, 128
+    rng = np.random.default_rng(14)
+    q = {n: rng.integers(-8, 8, size=sh) for n, sh in (("g", (I, H)), ("u", (I, H)), ("d", (H, I)))}
+    s64 = {n: rng.uniform(0.005, 0.02, size=(sh[0], sh[1] // 64)).astype(np.float16)
+           for n, sh in (("g", (I, H)), ("u", (I, H)), ("d", (H, I)))}
+    b64 = make_blob(H, I, q["g"], q["u"], q["d"], s64["g"], s64["u"], s64["d"], group=64)
+    b32 = make_blob(H, I, q["g"], q["u"], q["d"], *(np.repeat(s64[n], 2, axis=1) for n in "gud"))
+    for which in ("gate", "up", "down"):
+        np.testing.assert_array_equal(orc.dequant(b64, H, I, which, 64), orc.dequant(b32, H, I, which, 32))
+    x = rng.standard_normal(H)
+    np.testing.assert_array_equal(orc.expert_ffn(b64, H, I, x, 64), orc.expert_ffn(b32, H, I, x, 32))
 
 
 def test_int4_extremes_and_scale_product_are_exact():
@@ -401,13 +449,14 @@ def test_layer_expert_relabelling_is_invariant():
     np.testing.assert_array_equal(r2["y"], r1["y"])
 
 
-def test_layer_matches_numpy_composition_on_tiny():
-    spec = configs.TINY
+@pytest.mark.parametrize("group", [32, 64])
+def test_layer_matches_numpy_composition_on_tiny(group):
+    spec = configs.TINY.with_(group=group)
     x, w, b, blobs, _ = layer_inputs(spec)
-    r = orc.run_layer(x, w, b, spec.top_k, blobs, None, spec.hidden, spec.inter)
+    r = orc.run_layer(x, w, b, spec.top_k, blobs, None, spec.hidden, spec.inter, group=group)
     xf = x64(x)
     for t in range(spec.n_tok):
-        ref = sum(r["weight"][t, j] * numpy_ffn(blobs[int(e)], spec.hidden, spec.inter, xf[t])
+        ref = sum(r["weight"][t, j] * numpy_ffn(blobs[int(e)], spec.hidden, spec.inter, xf[t], group)
                   for j, e in enumerate(r["idx"][t]))
         assert np.max(np.abs(r["y"][t] - ref)) <= 1e-12 * np.max(np.abs(ref))
 
