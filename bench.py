@@ -43,12 +43,12 @@ def algorithmic_bytes(spec, n_union, n_tok):
     once, the shared expert's blob, the router weight, activations in, output
     out; and the share of them each expert kernel streams."""
     from int4_routed_expert_layer_amd import configs
-    blob = configs.blob_bytes(spec.hidden, spec.inter)
+    blob = configs.blob_bytes(spec.hidden, spec.inter, spec.group)
     experts = n_union + (1 if spec.has_shared else 0)
-    h, i = spec.hidden, spec.inter
+    h, i, g = spec.hidden, spec.inter, spec.group
     gu_experts = n_union if (fused_decode(spec) and spec.has_shared) else experts
-    gateup = gu_experts * (2 * i * h // 2 + 2 * i * (h // 32) * 2)
-    down = experts * (h * i // 2 + h * (i // 32) * 2)
+    gateup = gu_experts * (2 * i * h // 2 + 2 * i * (h // g) * 2)
+    down = experts * (h * i // 2 + h * (i // g) * 2)
     router = h * spec.n_experts * 4
     act = n_tok * h * spec.act_bytes + n_tok * h * 4
     return dict(total=experts * blob + router + act, gateup=gateup, down=down, router=router)
@@ -327,7 +327,8 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--instances", type=int, default=8, help="layer copies rotated per step")
-    ap.add_argument("--workloads", default="decode_b1,decode_b4,decode_b64,prefill_b4096,tiered_b16")
+    ap.add_argument("--workloads", default="decode_b1,decode_b4,decode_b64,prefill_b4096,tiered_b16,"
+                                           "decode_b1_g64,prefill_b4096_g64")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -363,6 +364,8 @@ def main():
         del src, dst
 
     results = {}
+    specs = {"decode_b1": spec1, "decode_b4": configs.DECODE_B4, "decode_b64": configs.DECODE_B64,
+             "prefill_b4096": configs.PREFILL_B4096}
     decode_layers = []
     if "decode_b1" in wanted or "decode_b4" in wanted or "decode_b64" in wanted:
         log(f"placing {args.instances} decode layer instances")
@@ -414,11 +417,42 @@ def main():
         tiered = run_tiered(B, torch, blobs, shared)
         torch.cuda.empty_cache()
 
+    # The same layer with one scale per 64 reduction elements (the group
+    # size of the README's shipped int4 container): 5.6% fewer bytes.
+    if "decode_b1_g64" in wanted or "prefill_b4096_g64" in wanted:
+        spec1g = spec1.with_(name="decode_b1_g64_h6144_i2048_e256_k8", group=64)
+        log(f"generating experts of {spec1g.name}")
+        blobs_g = inputs.expert_blobs(spec1g, 0, range(spec1g.n_experts), threads=8)
+        shared_g = inputs.expert_blob(spec1g, 0, inputs.SHARED)
+        if "decode_b1_g64" in wanted:
+            specs["decode_b1_g64"] = spec1g
+            log(f"placing {args.instances} g64 decode layer instances")
+            layers_g = make_layers(B, spec1g, blobs_g, shared_g, args.instances, 64, w1, b1)
+            x = B.activations_to_device(inputs.activations(spec1g, 0, 256))
+            wl = Workload("decode_b1_g64", spec1g, layers_g, args.steps, args.warmup, graph_steps=64)
+            log("timing decode_b1_g64")
+            results["decode_b1_g64"] = run_workload(B, torch, wl, x, use_graph=not args.no_graph)
+            for L in layers_g:
+                L.close()
+            del layers_g
+            torch.cuda.empty_cache()
+        if "prefill_b4096_g64" in wanted:
+            spec3g = configs.PREFILL_B4096.with_(name="prefill_b4096_g64_h6144_i2048_e256_k8", group=64)
+            specs["prefill_b4096_g64"] = spec3g
+            log("placing the g64 prefill layer")
+            (L3,) = make_layers(B, spec3g, blobs_g, shared_g, 1, spec3g.n_tok, inputs.router_weight(spec3g),
+                                inputs.router_bias(spec3g))
+            x = B.activations_to_device(inputs.activations(spec3g, 0))
+            wl = Workload("prefill_b4096_g64", spec3g, [L3], max(4, args.steps // 32), 2, graph_steps=1)
+            log("timing prefill_b4096_g64")
+            results["prefill_b4096_g64"] = run_workload(B, torch, wl, x, use_graph=False)
+            L3.close()
+        del blobs_g, shared_g
+
     # ---- report
     out_also = {}
     for name, r in results.items():
-        spec = {"decode_b1": spec1, "decode_b4": configs.DECODE_B4, "decode_b64": configs.DECODE_B64,
-                "prefill_b4096": configs.PREFILL_B4096}[name]
+        spec = specs[name]
         ms = r.get("graph_ms_per_step", r["eager_ms_per_step"])
         nb = algorithmic_bytes(spec, r["union_mean"], spec.n_tok)
         entry = dict(tokens_per_s=spec.n_tok / (ms / 1e3), ms_per_step=ms,
@@ -432,7 +466,7 @@ def main():
             entry["gateup_GBs"] = nb["gateup"] / (kg / 1e3) / 1e9
         if kd:
             entry["down_GBs"] = nb["down"] / (kd / 1e3) / 1e9
-        if name == "prefill_b4096" and kg and kd:
+        if name.startswith("prefill") and kg and kd:
             fl = expert_flops(spec, spec.n_tok)
             entry["expert_gemm_TFLOPs"] = fl / ((kg + kd) / 1e3) / 1e12
             entry["expert_gemm_frac_mfma"] = entry["expert_gemm_TFLOPs"] / MFMA_F16_PEAK_TFLOPS
@@ -440,7 +474,8 @@ def main():
     if tiered is not None:
         out_also["tiered_b16"] = tiered
 
-    kernel_names = [n for n in ("decode_b1", "decode_b4", "decode_b64", "prefill_b4096") if n in out_also]
+    kernel_names = [n for n in ("decode_b1", "decode_b4", "decode_b64", "prefill_b4096", "decode_b1_g64",
+                                "prefill_b4096_g64") if n in out_also]
     if not kernel_names:        # the tiered measurement alone
         print(json.dumps({"metric": METRIC, "value": tiered["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
                           "steps": tiered["calls_per_layer"], "warmup": 2, "ms_per_step": tiered["ms_per_call"],
@@ -450,8 +485,7 @@ def main():
         return
     head_name = kernel_names[0]
     head = out_also[head_name]
-    head_spec = {"decode_b1": spec1, "decode_b4": configs.DECODE_B4, "decode_b64": configs.DECODE_B64,
-                 "prefill_b4096": configs.PREFILL_B4096}[head_name]
+    head_spec = specs[head_name]
     r = results[head_name]
     nb = algorithmic_bytes(head_spec, r["union_mean"], head_spec.n_tok)
     kname = ("gemv_gateup_kernel (routed gate/up + SwiGLU)" if fused_decode(head_spec)

@@ -34,10 +34,10 @@
  *   output y_t   = sum_j weight_j * expert_{e_j}(x_t) + shared(x_t).
  *
  * Expert weights are int4 (two's complement, element 2j in the low nibble of
- * byte j, 2j+1 in the high nibble) with one fp16 scale per 32 consecutive
- * reduction elements (w = q * s).  The int4 container and its group scales
- * follow the README "Scarica il modello" (group-scaled int4); the group size
- * is 32 here.
+ * byte j, 2j+1 in the high nibble) with one fp16 scale per `group`
+ * consecutive reduction elements (w = q * s), group 32 or 64.  The int4
+ * container and its group scales follow the README "Scarica il modello"
+ * (group-scaled int4, 64 elements per scale in the shipped files).
  *
  * Conventions for every entry point:
  *  - Return codes only; nothing aborts or throws across the ABI.  On error
@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define COLI_ABI_VERSION 1
+#define COLI_ABI_VERSION 2
 
 typedef enum {
     COLI_OK = 0,
@@ -95,16 +95,18 @@ typedef struct {
     int32_t has_shared;  /* 0 or 1: one always-on shared expert */
     int32_t max_tokens;  /* largest n_tok any call will pass (>= 1) */
     int32_t act;         /* coli_act: dtype of x */
+    int32_t group;       /* reduction elements per fp16 weight scale: 32 or 64 */
 } coli_moe_dims;
 
 typedef struct coli_layer coli_layer;   /* opaque, library-owned */
 
-/* Bytes of one expert blob for H, I: gate_q, up_q ([I x H/2] bytes each),
- * down_q ([H x I/2]), gate_s, up_s (fp16 [I x H/32]), down_s (fp16
- * [H x I/32]), in that order, each section starting on a 256-byte boundary.
- * The README stores an expert's three matrices contiguously so one read
- * fetches all of them; this blob is that unit.  Returns 0 for invalid sizes. */
-size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter);
+/* Bytes of one expert blob for H, I and scale group G: gate_q, up_q
+ * ([I x H/2] bytes each), down_q ([H x I/2]), gate_s, up_s (fp16
+ * [I x H/G]), down_s (fp16 [H x I/G]), in that order, each section starting
+ * on a 256-byte boundary.  The README stores an expert's three matrices
+ * contiguously so one read fetches all of them; this blob is that unit.
+ * Returns 0 for invalid sizes or a group other than 32 and 64. */
+size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group);
 
 /* Repack a blob (host pointer, layout above) into the library's device
  * layout (host pointer `out`, same size): the bytes coli_expert_place keeps
@@ -112,11 +114,12 @@ size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter);
  * columns ordered so that lane L of a 64-lane wave loads bytes L*16..L*16+15
  * of a tile: row L mod 16, columns 32s + 8(L div 16) + 0..7 in dword s, each
  * stored as q + 8 with columns 2j and 2j+1 in nibbles j and 4+j; each tile's
- * 64 fp16 scales are stored row-major next to it in the scale section.
- * Host-only, no device needed.  COLI_E_INVALID for NULL pointers or sizes
- * that are not multiples of 128. */
+ * 16 x 128/group fp16 scales are stored row-major at the same tile index in
+ * the scale section.  Host-only, no device needed.  COLI_E_INVALID for NULL
+ * pointers, sizes that are not multiples of 128, or a group other than 32
+ * and 64. */
 coli_status coli_expert_repack(const void *blob_host, void *out_host,
-                               int32_t hidden, int32_t inter);
+                               int32_t hidden, int32_t inter, int32_t group);
 
 /* Create a layer on HIP device `device`.  Allocates the router copy, the
  * expert pointer table and scratch sized from dims->max_tokens.

@@ -20,10 +20,10 @@ namespace coli {
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-BlobLayout blob_layout(int hidden, int inter) {
-    const size_t h = static_cast<size_t>(hidden), i = static_cast<size_t>(inter);
+BlobLayout blob_layout(int hidden, int inter, int group) {
+    const size_t h = static_cast<size_t>(hidden), i = static_cast<size_t>(inter), g = static_cast<size_t>(group);
     const size_t sz[6] = {i * h / 2, i * h / 2, h * i / 2,
-                          i * (h / kGroup) * 2, i * (h / kGroup) * 2, h * (i / kGroup) * 2};
+                          i * (h / g) * 2, i * (h / g) * 2, h * (i / g) * 2};
     size_t off[7];
     size_t o = 0;
     for (int k = 0; k < 6; ++k) {
@@ -31,7 +31,7 @@ BlobLayout blob_layout(int hidden, int inter) {
         o = align256(o + sz[k]);
     }
     off[6] = o;
-    return BlobLayout{off[0], off[1], off[2], off[3], off[4], off[5], off[6]};
+    return BlobLayout{off[0], off[1], off[2], off[3], off[4], off[5], off[6], group};
 }
 
 namespace {
@@ -65,17 +65,18 @@ const RepackTables &repack_tables() {
     return *t;
 }
 
-// Repack rows [p_begin, p_end) panels of one [R x K] matrix.
-void repack_panels(const uint8_t *q_src, const uint16_t *s_src, int K, int p_begin,
+// Repack rows [p_begin, p_end) panels of one [R x K] matrix with one scale
+// per `group` columns (the chunk's 128/group scales of each row, row-major).
+void repack_panels(const uint8_t *q_src, const uint16_t *s_src, int K, int group, int p_begin,
                    int p_end, uint8_t *q_dst, uint16_t *s_dst) {
     const RepackTables &T = repack_tables();
     const int C = K / kChunkK;
     const size_t row_bytes = static_cast<size_t>(K) / 2;
-    const int groups = K / kGroup;
+    const int groups = K / group, per_chunk = kChunkK / group;
     for (int p = p_begin; p < p_end; ++p) {
         for (int c = 0; c < C; ++c) {
             uint8_t *qc = q_dst + (static_cast<size_t>(p) * C + c) * kChunkBytes;
-            uint16_t *sc = s_dst + (static_cast<size_t>(p) * C + c) * (kScaleChunkBytes / 2);
+            uint16_t *sc = s_dst + (static_cast<size_t>(p) * C + c) * (kPanel * per_chunk);
             for (int lane = 0; lane < 64; ++lane) {
                 const int r = p * kPanel + (lane & 15);
                 for (int s = 0; s < 4; ++s) {
@@ -87,14 +88,14 @@ void repack_panels(const uint8_t *q_src, const uint16_t *s_src, int K, int p_beg
                 }
             }
             for (int r = 0; r < kPanel; ++r)
-                for (int s = 0; s < 4; ++s)
-                    sc[r * 4 + s] = s_src[static_cast<size_t>(p * kPanel + r) * groups + 4 * c + s];
+                for (int s = 0; s < per_chunk; ++s)
+                    sc[r * per_chunk + s] = s_src[static_cast<size_t>(p * kPanel + r) * groups + per_chunk * c + s];
         }
     }
 }
 
-void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter) {
-    const BlobLayout L = blob_layout(hidden, inter);
+void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter, int group) {
+    const BlobLayout L = blob_layout(hidden, inter, group);
     std::memset(dst, 0, L.total);
     struct Mat { size_t q, s; int rows, K; } mats[3] = {
         {L.gate_q, L.gate_s, inter, hidden},
@@ -106,7 +107,7 @@ void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter) {
     for (const Mat &m : mats) {
         const int P = m.rows / kPanel;
         auto run = [&](int b, int e) {
-            repack_panels(src + m.q, reinterpret_cast<const uint16_t *>(src + m.s), m.K, b, e,
+            repack_panels(src + m.q, reinterpret_cast<const uint16_t *>(src + m.s), m.K, group, b, e,
                           dst + m.q, reinterpret_cast<uint16_t *>(dst + m.s));
         };
         if (nthreads <= 1 || P < 2 * nthreads) {
@@ -292,6 +293,7 @@ bool dims_valid(const coli_moe_dims *d, std::string &why) {
     }
     if (d->has_shared != 0 && d->has_shared != 1) { why = "has_shared must be 0 or 1"; return false; }
     if (d->act != COLI_ACT_F32 && d->act != COLI_ACT_BF16) { why = "act must be COLI_ACT_F32 or COLI_ACT_BF16"; return false; }
+    if (!group_supported(d->group)) { why = "group must be 32 or 64"; return false; }
     if (d->top_k > d->n_experts || d->top_k > kMaxTopK) {
         std::snprintf(buf, sizeof buf, "top_k %d must be <= min(n_experts, %d)", d->top_k, kMaxTopK);
         why = buf;
@@ -461,16 +463,18 @@ const char *coli_last_error(const coli_layer *L) {
     return L ? L->msg.c_str() : g_create_error.c_str();
 }
 
-size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter) {
-    if (hidden <= 0 || inter <= 0 || hidden % kGroup || inter % kGroup) return 0;
-    return blob_layout(hidden, inter).total;
+size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group) {
+    if (!group_supported(group) || hidden <= 0 || inter <= 0 || hidden % group || inter % group) return 0;
+    return blob_layout(hidden, inter, group).total;
 }
 
-coli_status coli_expert_repack(const void *blob_host, void *out_host, int32_t hidden, int32_t inter) {
+coli_status coli_expert_repack(const void *blob_host, void *out_host, int32_t hidden, int32_t inter,
+                               int32_t group) {
     if (!blob_host || !out_host) return fail(nullptr, COLI_E_INVALID, "NULL host pointer");
     if (hidden <= 0 || inter <= 0 || hidden % kChunkK || inter % kChunkK)
         return fail(nullptr, COLI_E_INVALID, "hidden and inter must be positive multiples of %d", kChunkK);
-    repack_blob(static_cast<const uint8_t *>(blob_host), static_cast<uint8_t *>(out_host), hidden, inter);
+    if (!group_supported(group)) return fail(nullptr, COLI_E_INVALID, "group %d must be 32 or 64", group);
+    repack_blob(static_cast<const uint8_t *>(blob_host), static_cast<uint8_t *>(out_host), hidden, inter, group);
     return COLI_OK;
 }
 
@@ -495,7 +499,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     L->device = device;
     L->n_cu = prop.multiProcessorCount;
     L->max_lds = prop.sharedMemPerBlock;
-    L->lay = blob_layout(dims->hidden, dims->inter);
+    L->lay = blob_layout(dims->hidden, dims->inter, dims->group);
     const int E = dims->n_experts, H = dims->hidden, I = dims->inter;
     const size_t T = static_cast<size_t>(dims->max_tokens);
     const size_t rows = T * dims->top_k + T;
@@ -593,7 +597,7 @@ coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_ho
     DeviceGuard guard(L->device);
     const uint8_t *src = static_cast<const uint8_t *>(blob_host);
     if (tier == COLI_TIER_VRAM) {
-        repack_blob(src, L->pin_stage, L->d.hidden, L->d.inter);
+        repack_blob(src, L->pin_stage, L->d.hidden, L->d.inter, L->d.group);
         if (!x.dev) HIP_TRY(L, hipMalloc(&x.dev, L->lay.total), "expert VRAM");
         HIP_TRY(L, hipMemcpy(x.dev, L->pin_stage, L->lay.total, hipMemcpyHostToDevice), "expert upload");
         if (x.host) {
@@ -603,7 +607,7 @@ coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_ho
         L->table_host[idx] = x.dev;
     } else {
         if (!x.host) HIP_TRY(L, hipHostMalloc(reinterpret_cast<void **>(&x.host), L->lay.total, hipHostMallocDefault), "expert pinned host");
-        repack_blob(src, x.host, L->d.hidden, L->d.inter);
+        repack_blob(src, x.host, L->d.hidden, L->d.inter, L->d.group);
         L->table_host[idx] = nullptr;
     }
     x.tier = tier;

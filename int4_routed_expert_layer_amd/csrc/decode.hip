@@ -215,14 +215,14 @@ __device__ void select_few_tokens(const FwdArgs &a, const FrontArgs &f) {
     }
 }
 
-template <int NT, bool BF16>
+template <int GS, int NT, bool BF16>
 __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, FrontArgs f, int router_blocks) {
     extern __shared__ __align__(16) uint8_t lds[];
     if (static_cast<int>(blockIdx.x) >= router_blocks) {
         const int p = blockIdx.x - router_blocks;
         // One block per CU here: a deeper load pipeline than the routed kernel.
-        dev::gateup_panel<NT, false, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
-                                                        a.n_tok, p, lds, dev::lds_address(lds));
+        dev::gateup_panel<GS, NT, false, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
+                                                            a.n_tok, p, lds, dev::lds_address(lds));
         return;
     }
     const int e = static_cast<int>(blockIdx.x) * 4 + dev::wave_id();   // uniform per wave
@@ -233,15 +233,22 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
     }
 }
 
-template <int NT>
+template <int GS, int NT>
 hipError_t launch_t(const FwdArgs &a, const FrontArgs &f, size_t lds, hipStream_t s) {
     const int router_blocks = (a.n_experts + 3) / 4;
     const int grid = router_blocks + (a.has_shared ? a.inter / kPanel : 0);
     if (a.act_bf16)
-        launch(decode_front_kernel<NT, true>, grid, kFrontThreads, lds, s, a, f, router_blocks);
+        launch(decode_front_kernel<GS, NT, true>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     else
-        launch(decode_front_kernel<NT, false>, grid, kFrontThreads, lds, s, a, f, router_blocks);
+        launch(decode_front_kernel<GS, NT, false>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     return hipGetLastError();
+}
+
+template <int GS>
+hipError_t launch_nt(const FwdArgs &a, const FrontArgs &f, int nt, size_t lds, hipStream_t s) {
+    if (nt == 1) return launch_t<GS, 1>(a, f, lds, s);
+    if (nt == 2) return launch_t<GS, 2>(a, f, lds, s);
+    return launch_t<GS, 4>(a, f, lds, s);
 }
 
 }  // namespace
@@ -251,9 +258,7 @@ hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_
     const int nt = a.n_tok == 1 ? 1 : (a.n_tok == 2 ? 2 : 4);
     const size_t lds = a.has_shared ? dev::gateup_lds_bytes(nt, a.hidden) : 0;
     if (lds > max_lds) return hipErrorInvalidValue;
-    if (nt == 1) return launch_t<1>(a, f, lds, s);
-    if (nt == 2) return launch_t<2>(a, f, lds, s);
-    return launch_t<4>(a, f, lds, s);
+    return a.lay.group == 64 ? launch_nt<64>(a, f, nt, lds, s) : launch_nt<32>(a, f, nt, lds, s);
 }
 
 }  // namespace coli

@@ -89,10 +89,28 @@ __host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
 constexpr int kGateUpGroup = 2;   // gate/up chunks per register buffer
 constexpr int kPipeGroup = 2;   // down chunks per register buffer
 
-template <int NG>
+// One lane's scales of a chunk: the 128/GS fp16 scales of its row (8 bytes
+// for group size 32, 4 bytes for 64).
+template <int GS> struct ScaleRec { using T = uint2; };
+template <> struct ScaleRec<64> { using T = uint32_t; };
+template <int GS> using scale_rec_t = typename ScaleRec<GS>::T;
+
+// Scale of dword s (chunk columns 32s .. 32s+31) from a lane's record.
+template <int GS>
+__device__ __forceinline__ float slice_scale(scale_rec_t<GS> r, int s) {
+    if constexpr (GS == 32) {
+        const uint32_t d = (s >> 1) ? r.y : r.x;
+        return half_bits_to_f32((d >> (16 * (s & 1))) & 0xFFFFu);
+    } else {
+        static_assert(GS == 64, "group size 32 or 64");
+        return half_bits_to_f32((r >> (16 * (s >> 1))) & 0xFFFFu);
+    }
+}
+
+template <int NG, int GS>
 struct GateUpBuf {
     uint4 gw[NG], uw[NG];
-    uint2 gs[NG], us[NG];
+    scale_rec_t<GS> gs[NG], us[NG];
 };
 
 // Sources of one gate/up panel: the blob descriptor, the lane offsets of a
@@ -103,20 +121,20 @@ struct GateUpSrc {
     uint32_t gq, uq, gs, us;  // uniform
 };
 
-template <int NG>
-__device__ __forceinline__ void gateup_load(GateUpBuf<NG> &b, const GateUpSrc &S, int first, int step, int C) {
+template <int NG, int GS>
+__device__ __forceinline__ void gateup_load(GateUpBuf<NG, GS> &b, const GateUpSrc &S, int first, int step, int C) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + step * g, C - 1));
         b.gw[g] = bload<uint4>(S.r, S.vq, S.gq + c * kChunkBytes);
         b.uw[g] = bload<uint4>(S.r, S.vq, S.uq + c * kChunkBytes);
-        b.gs[g] = bload<uint2>(S.r, S.vs, S.gs + c * kScaleChunkBytes);
-        b.us[g] = bload<uint2>(S.r, S.vs, S.us + c * kScaleChunkBytes);
+        b.gs[g] = bload<scale_rec_t<GS>>(S.r, S.vs, S.gs + c * scale_chunk_bytes<GS>());
+        b.us[g] = bload<scale_rec_t<GS>>(S.r, S.vs, S.us + c * scale_chunk_bytes<GS>());
     }
 }
 
-template <int MAXM, int NG>
-__device__ __forceinline__ void gateup_math(const GateUpBuf<NG> &b, const uint8_t *xs, const float *cs, int H,
+template <int MAXM, int NG, int GS>
+__device__ __forceinline__ void gateup_math(const GateUpBuf<NG, GS> &b, const uint8_t *xs, const float *cs, int H,
                                             int first, int step, int count, int kq, int mc,
                                             uint32_t M0, uint32_t M1, uint32_t G, float *gacc,
                                             float *vacc) {
@@ -126,12 +144,10 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf<NG> &b, const uint8_
         const int c = first + step * g;
         const uint32_t gws[4] = {b.gw[g].x, b.gw[g].y, b.gw[g].z, b.gw[g].w};
         const uint32_t uws[4] = {b.uw[g].x, b.uw[g].y, b.uw[g].z, b.uw[g].w};
-        const uint32_t gss[2] = {b.gs[g].x, b.gs[g].y};
-        const uint32_t uss[2] = {b.us[g].x, b.us[g].y};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float sg = half_bits_to_f32((gss[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
-            const float su = half_bits_to_f32((uss[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+            const float sg = slice_scale<GS>(b.gs[g], s);
+            const float su = slice_scale<GS>(b.us[g], s);
             const int k0 = c * kChunkK + 32 * s + 8 * kq;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
@@ -151,8 +167,8 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf<NG> &b, const uint8_
 // a row).  Writes h rows (fp16; device-coherent stores when COHERENT, for a
 // consumer in the same launch).  All 256 threads must call it (it
 // synchronises the workgroup).  NG chunks per register buffer (two buffers in
-// flight): more for few workgroups per CU.
-template <int MAXM, bool COHERENT = false, int NG = kGateUpGroup, class Rows>
+// flight): more for few workgroups per CU.  GS is the scale group size.
+template <int GS, int MAXM, bool COHERENT = false, int NG = kGateUpGroup, class Rows>
 __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int p,
                              uint8_t *lds, uint32_t lds_addr) {
     const int H = a.hidden, I = a.inter;
@@ -162,11 +178,11 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
     GateUpSrc P;
     P.r = make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
     P.vq = static_cast<uint32_t>(lane) * 16;
-    P.vs = static_cast<uint32_t>(row) * 8;
+    P.vs = static_cast<uint32_t>(row) * scale_row_bytes<GS>();
     P.gq = static_cast<uint32_t>(a.lay.gate_q + static_cast<size_t>(p) * C * kChunkBytes);
     P.uq = static_cast<uint32_t>(a.lay.up_q + static_cast<size_t>(p) * C * kChunkBytes);
-    P.gs = static_cast<uint32_t>(a.lay.gate_s + static_cast<size_t>(p) * C * kScaleChunkBytes);
-    P.us = static_cast<uint32_t>(a.lay.up_s + static_cast<size_t>(p) * C * kScaleChunkBytes);
+    P.gs = static_cast<uint32_t>(a.lay.gate_s + static_cast<size_t>(p) * C * scale_chunk_bytes<GS>());
+    P.us = static_cast<uint32_t>(a.lay.up_s + static_cast<size_t>(p) * C * scale_chunk_bytes<GS>());
     // Chunks of this wave: wave, wave + 4, ...
     const int nper = wave < C ? (C - wave + 3) / 4 : 0;
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
@@ -182,7 +198,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) gacc[m] = vacc[m] = 0.0f;
 
-        GateUpBuf<NG> A, B;
+        GateUpBuf<NG, GS> A, B;
         bool b_issued = false;
         if (a.act_bf16 && (H * 2) % 1024 == 0) {
             // bf16 rows are copied straight into the staging area (1 KB per
@@ -311,23 +327,25 @@ struct PlainRows {
     __device__ float weight(int row) const { return row < a.n_tok * a.k ? a.topk_w[a.gather[row]] : 1.0f; }
 };
 
+template <int GS>
 struct DownBuf {
     uint4 w[kPipeGroup];
-    uint2 s[kPipeGroup];
+    scale_rec_t<GS> s[kPipeGroup];
 };
 
-__device__ __forceinline__ void down_load(DownBuf &b, rsrc_t r, uint32_t vq, uint32_t vs, uint32_t sq, uint32_t ss,
+template <int GS>
+__device__ __forceinline__ void down_load(DownBuf<GS> &b, rsrc_t r, uint32_t vq, uint32_t vs, uint32_t sq, uint32_t ss,
                                           int first, int C) {
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + g, C - 1));
         b.w[g] = bload<uint4>(r, vq, sq + c * kChunkBytes);
-        b.s[g] = bload<uint2>(r, vs, ss + c * kScaleChunkBytes);
+        b.s[g] = bload<scale_rec_t<GS>>(r, vs, ss + c * scale_chunk_bytes<GS>());
     }
 }
 
-template <int MAXM>
-__device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, const float *cs, int I,
+template <int MAXM, int GS>
+__device__ __forceinline__ void down_math(const DownBuf<GS> &b, const uint8_t *hs, const float *cs, int I,
                                           int first, int count, int kq, int mc, uint32_t M0,
                                           uint32_t M1, uint32_t G, float *acc) {
 #pragma unroll
@@ -335,10 +353,9 @@ __device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, c
         if (g >= count) continue;
         const int c = first + g;
         const uint32_t ws[4] = {b.w[g].x, b.w[g].y, b.w[g].z, b.w[g].w};
-        const uint32_t ss[2] = {b.s[g].x, b.s[g].y};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float sf = half_bits_to_f32((ss[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+            const float sf = slice_scale<GS>(b.s[g], s);
             const int k0 = c * kChunkK + 32 * s + 8 * kq;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
@@ -359,8 +376,9 @@ __device__ __forceinline__ void down_math(const DownBuf &b, const uint8_t *hs, c
 // routed row, 1 for a shared row).  With COHERENT, ys is written
 // device-coherently (a consumer in the same launch reads it); before_h()
 // runs, by all threads, after the first weight loads are issued and before h
-// is read (a wait for h's producers).  All 256 threads must call it.
-template <int MAXM, bool COHERENT = false, class Rows, class BeforeH>
+// is read (a wait for h's producers).  All 256 threads must call it.  GS is
+// the scale group size.
+template <int GS, int MAXM, bool COHERENT = false, class Rows, class BeforeH>
 __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int pg,
                                 uint8_t *lds, uint32_t lds_addr, const BeforeH &before_h) {
     const int H = a.hidden, I = a.inter;
@@ -372,9 +390,9 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
     const int c_end = half == 0 ? (C + 1) / 2 : C;
     const int nper = c_end - c_begin;
     const rsrc_t rs = make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
-    const uint32_t vq = static_cast<uint32_t>(lane) * 16, vs = static_cast<uint32_t>(row) * 8;
+    const uint32_t vq = static_cast<uint32_t>(lane) * 16, vs = static_cast<uint32_t>(row) * scale_row_bytes<GS>();
     const uint32_t sq = static_cast<uint32_t>(a.lay.down_q + static_cast<size_t>(p) * C * kChunkBytes);
-    const uint32_t ss = static_cast<uint32_t>(a.lay.down_s + static_cast<size_t>(p) * C * kScaleChunkBytes);
+    const uint32_t ss = static_cast<uint32_t>(a.lay.down_s + static_cast<size_t>(p) * C * scale_chunk_bytes<GS>());
     uint8_t *hs = lds;
     float *cs = reinterpret_cast<float *>(lds + static_cast<size_t>(MAXM) * I * 2);
     float *red = cs + MAXM * (I / 8);
@@ -385,7 +403,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
         float acc[MAXM];
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
-        DownBuf A, B;
+        DownBuf<GS> A, B;
         bool b_issued = false;
         if (mb == 0) before_h();
         __syncthreads();                        // the previous row block is done with hs

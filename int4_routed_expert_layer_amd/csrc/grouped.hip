@@ -17,8 +17,8 @@
 // reads and the dequantisation of the next 16-column slice are interleaved
 // between the MFMAs of the current one.  Each weight dword becomes eight fp16
 // weights: q = (1024 + u) - 1032 (exact) times the group's fp16 scale (one
-// rounding), so a fragment covers exactly one 32-wide scale group and the
-// MFMA accumulates in fp32.
+// rounding), so a fragment lies inside one scale group (32 or 64 wide) and
+// the MFMA accumulates in fp32.
 //   gate/up: A = gathered token rows (fp16 copy of x); each wave owns
 //            32 intermediate rows of both gate and up, so SwiGLU is applied
 //            in registers and h is stored as fp16.
@@ -138,7 +138,7 @@ struct ItemState {
 // make that wait stricter).  Lookahead past the last step repeats the last
 // step's addresses (never used), so that count holds at every step; the loop
 // ends with a full wait before the stages are reused.
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MT, int GS>
 __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, const uint8_t *s_a,
                                          uint32_t sa_lds, const int *s_ent, const float *s_w) {
     const int H = a.hidden, I = a.inter;
@@ -162,7 +162,10 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
             const uint32_t cq = st.qoff[nt] + ch * kChunkBytes + 8 * h;
             f.qe[nt] = dev::bload<uint2>(st.brs, st.qv_even, cq);
             f.qo[nt] = dev::bload<uint2>(st.brs, st.qv_odd, cq);
-            f.sc[nt] = dev::bload<uint32_t>(st.brs, st.sv, st.soff[nt] + ch * kScaleChunkBytes + 4 * h);
+            // Group size 32: the step's two scales (groups 2h, 2h+1 of the
+            // chunk); 64: the chunk's two, of which group h is the step's.
+            f.sc[nt] = dev::bload<uint32_t>(st.brs, st.sv,
+                                            st.soff[nt] + ch * scale_chunk_bytes<GS>() + (GS == 32 ? 4 * h : 0));
         }
         asm volatile("" ::: "memory");
     };
@@ -177,12 +180,14 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
 
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
 
-    // B fragment of slice t (0..3) of a step: dword t / 2 of the even or odd
-    // slot half, times the scale of group t / 2.
-    auto bfrag = [&](const B64 &f, int t, int nt) {
+    // B fragment of slice t (0..3) of step c: dword t / 2 of the even or odd
+    // slot half, times the scale of its group (t / 2 of the step's pair for
+    // group size 32; half c & 1 of the chunk's pair for 64).
+    auto bfrag = [&](const B64 &f, int t, int nt, int c) {
         const uint2 &q = (t & 1) ? f.qo[nt] : f.qe[nt];
         const uint32_t w = (t >> 1) ? q.y : q.x;
-        const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(f.sc[nt] >> (16 * (t >> 1))));
+        const int sel = GS == 32 ? (t >> 1) : (c & 1);
+        const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(f.sc[nt] >> (16 * sel)));
         return dequant8(w, half2v{sh, sh}, M0, M1, G);
     };
     // Software pipeline over the four slices of a step: the A fragments and
@@ -197,7 +202,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
         for (int mt = 0; mt < MT; ++mt)
             av[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, lh));
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) bc[nt] = bfrag(f, 0, nt);
+        for (int nt = 0; nt < 2; ++nt) bc[nt] = bfrag(f, 0, nt, c);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             half8 an[MT], bn[2];
@@ -206,7 +211,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
                 for (int mt = 0; mt < MT; ++mt)
                     an[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, 2 * (t + 1) + lh));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) bn[nt] = bfrag(f, t + 1, nt);
+                for (int nt = 0; nt < 2; ++nt) bn[nt] = bfrag(f, t + 1, nt, c);
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -286,7 +291,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int GS>
 __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
     // Ring of A stages, kChunkRows rows x kStepK fp16 each.
     __shared__ __align__(16) uint8_t s_a[kStages * kStageBytes];
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         const uint32_t r16 = static_cast<uint32_t>(l31 & 15), hi = static_cast<uint32_t>(l31 >> 4);
         st.qv_even = hi * pstep + 16 * (r16 + 16 * static_cast<uint32_t>(lh));
         st.qv_odd = hi * pstep + 16 * (r16 + 16 * (2 + static_cast<uint32_t>(lh)));
-        st.sv = hi * static_cast<uint32_t>(C) * kScaleChunkBytes + r16 * 8;
+        st.sv = hi * static_cast<uint32_t>(C) * scale_chunk_bytes<GS>() + r16 * scale_row_bytes<GS>();
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             int panel;
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
                 if (!st.bvalid[nt]) panel = 0;
             }
             st.qoff[nt] = static_cast<uint32_t>(qs + static_cast<size_t>(panel) * C * kChunkBytes);
-            st.soff[nt] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * C * kScaleChunkBytes);
+            st.soff[nt] = static_cast<uint32_t>(ss + static_cast<size_t>(panel) * C * scale_chunk_bytes<GS>());
         }
 
         __syncthreads();   // previous item is done with s_tok and the A tiles
@@ -407,11 +412,11 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
             st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
         }
         switch (mt) {
-            case 5: run_item<GATEUP, 5>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            case 4: run_item<GATEUP, 4>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            case 3: run_item<GATEUP, 3>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            case 2: run_item<GATEUP, 2>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            default: run_item<GATEUP, 1>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 5: run_item<GATEUP, 5, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 4: run_item<GATEUP, 4, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 3: run_item<GATEUP, 3, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            case 2: run_item<GATEUP, 2, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            default: run_item<GATEUP, 1, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
         }
     }
     // The last workgroup out clears the queue counters for the next launch.
@@ -479,12 +484,16 @@ hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
-    launch(grouped_kernel<true>, grid_for(max_chunks * (a.inter / 128), 2 * n_cu), 256, 0, s, a);
+    const unsigned grid = grid_for(max_chunks * (a.inter / 128), 2 * n_cu);
+    if (a.lay.group == 64) launch(grouped_kernel<true, 64>, grid, 256, 0, s, a);
+    else launch(grouped_kernel<true, 32>, grid, 256, 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
-    launch(grouped_kernel<false>, grid_for(max_chunks * ((a.hidden + 255) / 256), 2 * n_cu), 256, 0, s, a);
+    const unsigned grid = grid_for(max_chunks * ((a.hidden + 255) / 256), 2 * n_cu);
+    if (a.lay.group == 64) launch(grouped_kernel<false, 64>, grid, 256, 0, s, a);
+    else launch(grouped_kernel<false, 32>, grid, 256, 0, s, a);
     return hipGetLastError();
 }
 

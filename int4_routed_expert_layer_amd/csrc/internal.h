@@ -16,8 +16,12 @@
 //   k0+2j and k0+2j+1 in the low and high 16-bit halves: OR-ing an fp16
 //   (0x6400 -> 1024 + u) or bf16 (0x4300 -> 128 + u) exponent turns each
 //   half into an exact small integer.
-//   Scales: chunk (p, c) has 128 bytes at (p * K/128 + c) * 128 in the scale
-//   section: fp16 [16 rows][4 groups], groups 4c .. 4c+3.
+//   Scales: chunk (p, c) has 16 * 128/G fp16 at (p * K/128 + c) times that
+//   size in the scale section, [16 rows][128/G groups]: for group size
+//   G = 32, 128 bytes holding groups 4c .. 4c+3 of each row; for G = 64,
+//   64 bytes holding groups 2c, 2c+1.  Dword s of a lane's weight slot
+//   (columns 32s + ...) takes group s (G = 32) or s / 2 (G = 64) of the
+//   chunk.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,19 +33,27 @@
 
 namespace coli {
 
-constexpr int kGroup = 32;          // reduction elements per fp16 scale
 constexpr int kChunkK = 128;        // reduction elements per 1 KB chunk
 constexpr int kPanel = 16;          // matrix rows per chunk
 constexpr int kChunkBytes = 1024;
-constexpr int kScaleChunkBytes = 128;
+
+// Reduction elements per fp16 scale: 32, or 64 (the container of the README's
+// "Scarica il modello" section).
+constexpr bool group_supported(int g) { return g == 32 || g == 64; }
+// Bytes of one chunk's scales, and of one row's share of them.
+template <int G>
+constexpr int scale_chunk_bytes() { return kPanel * (kChunkK / G) * 2; }
+template <int G>
+constexpr int scale_row_bytes() { return (kChunkK / G) * 2; }
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kChunkRows = 160;     // rows per grouped work chunk: five 32-row MFMA tiles
 
 struct BlobLayout {
     size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
+    int group;
 };
-BlobLayout blob_layout(int hidden, int inter);
+BlobLayout blob_layout(int hidden, int inter, int group);
 
 // One grouped-GEMM work chunk: up to kChunkRows rows of one expert.
 // expert == n_experts means the shared expert.  row0 indexes the rows of the

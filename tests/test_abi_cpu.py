@@ -34,21 +34,25 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lib.coli_abi_version() == 1
+    assert B.lib.coli_abi_version() == 2
     for st, name in enumerate(["COLI_OK", "COLI_E_INVALID", "COLI_E_NOMEM", "COLI_E_DEVICE",
                                "COLI_E_STATE", "COLI_E_UNSUPPORTED"]):
         assert B.status_str(st) == name
 
 
 def test_blob_bytes_matches_layout():
-    for h, i in ((6144, 2048), (256, 128), (512, 256)):
-        assert B.blob_bytes(h, i) == configs.blob_bytes(h, i)
+    for g in (32, 64):
+        for h, i in ((6144, 2048), (256, 128), (512, 256), (384, 640)):
+            assert B.blob_bytes(h, i, g) == configs.blob_bytes(h, i, g)
     assert B.blob_bytes(6144, 2048) == 21233664
+    assert B.blob_bytes(6144, 2048, 64) == 20054016
     assert B.blob_bytes(0, 128) == 0 and B.blob_bytes(100, 128) == 0
+    assert B.blob_bytes(6144, 2048, 16) == 0 and B.blob_bytes(6144, 2048, 128) == 0
+    assert B.blob_bytes(6144, 2080, 64) == 0
 
 
 def create(**kw):
-    d = dict(hidden=256, inter=128, n_experts=16, top_k=4, has_shared=0, max_tokens=8, act=0)
+    d = dict(hidden=256, inter=128, n_experts=16, top_k=4, has_shared=0, max_tokens=8, act=0, group=32)
     d.update(kw)
     h = C.c_void_p()
     st = B.lib.coli_layer_create(C.byref(B.Dims(**d)), 0, C.byref(h))
@@ -62,6 +66,8 @@ def create(**kw):
     (dict(max_tokens=0), B.E_INVALID),
     (dict(has_shared=2), B.E_INVALID),
     (dict(act=7), B.E_INVALID),
+    (dict(group=0), B.E_INVALID),
+    (dict(group=128), B.E_INVALID),
     (dict(hidden=192), B.E_UNSUPPORTED),
     (dict(inter=96), B.E_UNSUPPORTED),
     (dict(n_experts=1024, has_shared=1), B.E_UNSUPPORTED),
@@ -95,9 +101,10 @@ def test_null_layer_calls_are_invalid():
     assert L.coli_layer_destroy(None) == B.OK
 
 
-def documented_layout(blob, H, I):
+def documented_layout(blob, H, I, group=32):
     """The device layout described in coli_moe.h, written with numpy."""
-    sec = configs.blob_sections(H, I)
+    sec = configs.blob_sections(H, I, group)
+    per = 128 // group                                      # scales per row of a tile
     out = np.zeros_like(blob)
     for name, rows, K in (("gate", I, H), ("up", I, H), ("down", H, I)):
         qo, qs = sec[name + "_q"]
@@ -118,20 +125,23 @@ def documented_layout(blob, H, I):
         slot = np.where(i % 2 == 0, i // 2, 4 + i // 2)
         words = (vals << (4 * slot)).sum(-1).astype(np.uint32)
         out[qo:qo + qs] = words.reshape(-1).view(np.uint8)
-        sc = blob[so:so + ss].view(np.uint16).reshape(rows, K // 32)
-        tiles = sc.reshape(P, 16, Cn, 4).transpose(0, 2, 1, 3)   # [P, C, row, group]
+        sc = blob[so:so + ss].view(np.uint16).reshape(rows, K // group)
+        tiles = sc.reshape(P, 16, Cn, per).transpose(0, 2, 1, 3)   # [P, C, row, group]
         out[so:so + ss] = np.ascontiguousarray(tiles).reshape(-1).view(np.uint8)
     return out
 
 
+@pytest.mark.parametrize("group", [32, 64])
 @pytest.mark.parametrize("spec", [configs.TINY, configs.TINY.with_(hidden=512, inter=384)])
-def test_repack_writes_the_documented_layout(spec):
+def test_repack_writes_the_documented_layout(spec, group):
+    spec = spec.with_(group=group)
     blob = inputs.expert_blob(spec, 0, 2)
-    got = B.repack(blob, spec.hidden, spec.inter)
-    np.testing.assert_array_equal(got, documented_layout(blob, spec.hidden, spec.inter))
+    got = B.repack(blob, spec.hidden, spec.inter, group)
+    np.testing.assert_array_equal(got, documented_layout(blob, spec.hidden, spec.inter, group))
 
 
 def test_repack_rejects_bad_sizes():
     buf = np.zeros(1024, np.uint8)
-    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 96, 128) == B.E_INVALID
-    assert B.lib.coli_expert_repack(None, buf.ctypes.data, 128, 128) == B.E_INVALID
+    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 96, 128, 32) == B.E_INVALID
+    assert B.lib.coli_expert_repack(None, buf.ctypes.data, 128, 128, 32) == B.E_INVALID
+    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 128, 128, 48) == B.E_INVALID
