@@ -311,7 +311,7 @@ def cpu_baseline(spec, x, w, b, blobs, shared, seconds):
         idx, wt = orc.topk(logits, spec.top_k)
         orc.union(idx, spec.n_experts)
         need = {int(e): blobs[int(e)] for e in idx[0]}
-        orc.layer_tokens(xt, spec.hidden, spec.inter, idx, wt, need, shared, [0], spec.group)
+        orc.layer_tokens(xt, spec.hidden, spec.inter, idx, wt, need, shared, [0], spec.group, spec.bits)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= x.shape[0]:

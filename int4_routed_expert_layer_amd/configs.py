@@ -41,6 +41,7 @@ class Spec:
     zipf_s: float = 1.1
     zipf_gamma: float = 0.648
     group: int = GROUP           # reduction elements per fp16 weight scale
+    bits: int = 4                # weight width: 4 (int4) or 8 (int8)
 
     @property
     def act_bytes(self) -> int:
@@ -54,17 +55,18 @@ def _align(n: int) -> int:
     return (n + BLOB_ALIGN - 1) // BLOB_ALIGN * BLOB_ALIGN
 
 
-def blob_sections(hidden: int, inter: int, group: int = GROUP) -> dict:
+def blob_sections(hidden: int, inter: int, group: int = GROUP, bits: int = 4) -> dict:
     """Byte offset and size of each section of one expert blob.
 
     Order: gate nibbles, up nibbles, down nibbles, gate scales, up scales,
     down scales.  Gate and up are [I x H] (output rows x reduction), down is
-    [H x I]; nibbles are row-major along the reduction axis, two per byte,
-    element 2j in the low nibble; scales are fp16 [rows x K/group].
+    [H x I]; weights are row-major along the reduction axis, int4 two per
+    byte (element 2j in the low nibble) or int8 one per byte; scales are fp16
+    [rows x K/group].
     """
     h, i = hidden, inter
     sizes = [
-        ("gate_q", i * h // 2), ("up_q", i * h // 2), ("down_q", h * i // 2),
+        ("gate_q", i * h * bits // 8), ("up_q", i * h * bits // 8), ("down_q", h * i * bits // 8),
         ("gate_s", i * (h // group) * 2), ("up_s", i * (h // group) * 2),
         ("down_s", h * (i // group) * 2),
     ]
@@ -76,8 +78,8 @@ def blob_sections(hidden: int, inter: int, group: int = GROUP) -> dict:
     return out
 
 
-def blob_bytes(hidden: int, inter: int, group: int = GROUP) -> int:
-    return blob_sections(hidden, inter, group)["total"][1]
+def blob_bytes(hidden: int, inter: int, group: int = GROUP, bits: int = 4) -> int:
+    return blob_sections(hidden, inter, group, bits)["total"][1]
 
 
 _BIG = dict(hidden=6144, inter=2048, n_experts=256, top_k=8, act="bf16",

@@ -14,8 +14,10 @@ Recipe (the pages name the model, GLM-5.2, and its sizes but print no tensor):
     taken from a seeded permutation, so expert popularity falls off like a
     Zipf law (gamma=0.648 makes the realised rank-frequency slope about -s
     for top-8 of 256);
-  * expert nibbles: uniform over the 16 int4 codes (uniform bytes);
-  * expert scales: U[0.005, 0.02] rounded to fp16;
+  * expert weights: uniform over the 16 int4 codes (uniform bytes), or for
+    int8 experts over the 256 int8 codes;
+  * expert scales: U[0.005, 0.02] rounded to fp16 (int4), or U[0.005, 0.02]/16
+    for int8 (the same real weight range at 16 times the resolution);
   * tiers: the first round(resident_frac * E) experts of a seeded
     permutation are VRAM-resident, the rest live in pinned host memory.
 """
@@ -105,7 +107,7 @@ def expert_blob(spec: Spec, layer: int, expert: int) -> np.ndarray:
         raise ValueError(f"expert {expert} out of range")
     if expert == SHARED and not spec.has_shared:
         raise ValueError("spec has no shared expert")
-    sec = blob_sections(spec.hidden, spec.inter, spec.group)
+    sec = blob_sections(spec.hidden, spec.inter, spec.group, spec.bits)
     blob = np.zeros(sec["total"][1], dtype=np.uint8)
     g = rng(spec, layer, stream)
     for name in ("gate_q", "up_q", "down_q"):
@@ -113,7 +115,8 @@ def expert_blob(spec: Spec, layer: int, expert: int) -> np.ndarray:
         blob[off:off + size] = g.integers(0, 256, size=size, dtype=np.uint8)
     for name in ("gate_s", "up_s", "down_s"):
         off, size = sec[name]
-        s = g.uniform(0.005, 0.02, size=size // 2).astype(np.float16)
+        lo, hi = (0.005, 0.02) if spec.bits == 4 else (0.005 / 16, 0.02 / 16)
+        s = g.uniform(lo, hi, size=size // 2).astype(np.float16)
         blob[off:off + size] = s.view(np.uint8)
     return blob
 

@@ -32,7 +32,12 @@
  *           nibble), one fp16 scale per `group` consecutive reduction
  *           elements (32 in the fixed configurations; 64 in the container the
  *           README's "Scarica il modello" section ships), w = q * s exactly
- *           in fp64.  The scale sections hold [rows x K/group] fp16.  SwiGLU: h = silu(Wg x) * (Wu x),
+ *           in fp64.  The scale sections hold [rows x K/group] fp16.
+ *           Weights are 4-bit as above or, with bits = 8, one two's-complement
+ *           byte per element in [-128, 127] (the README's "Scarica il
+ *           modello" section and the getting-started page require int8 for
+ *           the MTP head; the pages give no layout, so the int8 blob keeps
+ *           the int4 blob's sections, row order and group scales).  SwiGLU: h = silu(Wg x) * (Wu x),
  *           silu(z) = z * sigmoid(z), y_e = Wd h, all fp64.
  *  Combine  y_t = sum_j w_j * y_{e_j}(x_t) + y_shared(x_t), fp64, where the
  *           shared expert (one always-on expert of the same shape) has
@@ -45,7 +50,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 2
+#define ORACLE_ABI_VERSION 3
 #define ALIGN 256
 
 int coli_oracle_version(void) { return ORACLE_ABI_VERSION; }
@@ -211,11 +216,11 @@ static size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 /* Section offsets of a canonical blob: gate_q, up_q, down_q, gate_s, up_s,
  * down_s, total. */
-static void blob_offsets(int hidden, int inter, int group, size_t off[7])
+static void blob_offsets(int hidden, int inter, int group, int bits, size_t off[7])
 {
     size_t sz[6] = {
-        (size_t)inter * hidden / 2, (size_t)inter * hidden / 2,
-        (size_t)hidden * inter / 2,
+        (size_t)inter * hidden * bits / 8, (size_t)inter * hidden * bits / 8,
+        (size_t)hidden * inter * bits / 8,
         (size_t)inter * (hidden / group) * 2, (size_t)inter * (hidden / group) * 2,
         (size_t)hidden * (inter / group) * 2,
     };
@@ -227,42 +232,51 @@ static void blob_offsets(int hidden, int inter, int group, size_t off[7])
     off[6] = o;
 }
 
-/* A group size the layout supports: positive and dividing both widths. */
-static int group_ok(int hidden, int inter, int group)
+/* A format the layout supports: 4- or 8-bit weights, a group size that is
+ * positive and divides both widths (and even widths for 4-bit packing). */
+static int format_ok(int hidden, int inter, int group, int bits)
 {
-    return group > 0 && hidden > 0 && inter > 0 && hidden % group == 0 && inter % group == 0;
+    return (bits == 4 || bits == 8) && group > 0 && hidden > 0 && inter > 0 &&
+           hidden % group == 0 && inter % group == 0 && hidden % 2 == 0 && inter % 2 == 0;
 }
 
-size_t coli_oracle_blob_bytes(int hidden, int inter, int group)
+size_t coli_oracle_blob_bytes(int hidden, int inter, int group, int bits)
 {
     size_t off[7];
-    if (!group_ok(hidden, inter, group))
+    if (!format_ok(hidden, inter, group, bits))
         return 0;
-    blob_offsets(hidden, inter, group, off);
+    blob_offsets(hidden, inter, group, bits, off);
     return off[6];
 }
 
-/* Row r of a [rows x K] int4 matrix with fp16 group scales, dequantised to
- * fp64: out[k] = q[r][k] * s[r][k / group]. */
-static void dequant_row(const uint8_t *q, const uint16_t *s, int K, int group, int r,
+/* Weight k of a packed row: a nibble (bits 4) or a byte (bits 8), two's
+ * complement. */
+static int weight_at(const uint8_t *row, int k, int bits)
+{
+    return bits == 4 ? nibble_at(row, k) : (int)(int8_t)row[k];
+}
+
+/* Row r of a [rows x K] int4 or int8 matrix with fp16 group scales,
+ * dequantised to fp64: out[k] = q[r][k] * s[r][k / group]. */
+static void dequant_row(const uint8_t *q, const uint16_t *s, int K, int group, int bits, int r,
                         double *out)
 {
-    const uint8_t *row = q + (size_t)r * (K / 2);
+    const uint8_t *row = q + (size_t)r * ((size_t)K * bits / 8);
     const uint16_t *srow = s + (size_t)r * (K / group);
     for (int g = 0; g < K / group; ++g) {
         double scale = half_bits_to_double(srow[g]);
         for (int k = g * group; k < (g + 1) * group; ++k)
-            out[k] = (double)nibble_at(row, k) * scale;
+            out[k] = (double)weight_at(row, k, bits) * scale;
     }
 }
 
 /* y[H] = SwiGLU expert applied to x[H], all fp64.  scratch >= I + 2*H
  * doubles. */
-static void expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
+static void expert_ffn(const uint8_t *blob, int hidden, int inter, int group, int bits,
                        const double *x, double *y, double *scratch)
 {
     size_t off[7];
-    blob_offsets(hidden, inter, group, off);
+    blob_offsets(hidden, inter, group, bits, off);
     const uint8_t *gq = blob + off[0], *uq = blob + off[1], *dq = blob + off[2];
     const uint16_t *gs = (const uint16_t *)(blob + off[3]);
     const uint16_t *us = (const uint16_t *)(blob + off[4]);
@@ -271,8 +285,8 @@ static void expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
     double *wa = scratch + inter;
     double *wb = wa + hidden;
     for (int r = 0; r < inter; ++r) {
-        dequant_row(gq, gs, hidden, group, r, wa);
-        dequant_row(uq, us, hidden, group, r, wb);
+        dequant_row(gq, gs, hidden, group, bits, r, wa);
+        dequant_row(uq, us, hidden, group, bits, r, wb);
         double g = 0.0, v = 0.0;
         for (int k = 0; k < hidden; ++k) {
             g += wa[k] * x[k];
@@ -281,7 +295,7 @@ static void expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
         h[r] = g * sigmoid(g) * v;
     }
     for (int n = 0; n < hidden; ++n) {
-        dequant_row(dq, ds, inter, group, n, wa);
+        dequant_row(dq, ds, inter, group, bits, n, wa);
         double acc = 0.0;
         for (int r = 0; r < inter; ++r)
             acc += wa[r] * h[r];
@@ -289,34 +303,34 @@ static void expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
     }
 }
 
-int coli_oracle_expert_ffn(const uint8_t *blob, int hidden, int inter, int group,
+int coli_oracle_expert_ffn(const uint8_t *blob, int hidden, int inter, int group, int bits,
                            const double *x, double *y)
 {
-    if (!group_ok(hidden, inter, group))
+    if (!format_ok(hidden, inter, group, bits))
         return -1;
     double *scratch = (double *)malloc(sizeof(double) * ((size_t)inter + 2 * (size_t)hidden));
     if (!scratch)
         return -2;
-    expert_ffn(blob, hidden, inter, group, x, y, scratch);
+    expert_ffn(blob, hidden, inter, group, bits, x, y, scratch);
     free(scratch);
     return 0;
 }
 
 /* Dequantise one [rows x K] matrix of a blob to fp64 (row-major). which:
  * 0 gate, 1 up, 2 down. */
-int coli_oracle_dequant(const uint8_t *blob, int hidden, int inter, int group, int which,
-                        double *out)
+int coli_oracle_dequant(const uint8_t *blob, int hidden, int inter, int group, int bits,
+                        int which, double *out)
 {
     size_t off[7];
-    if (which < 0 || which > 2 || !group_ok(hidden, inter, group))
+    if (which < 0 || which > 2 || !format_ok(hidden, inter, group, bits))
         return -1;
-    blob_offsets(hidden, inter, group, off);
+    blob_offsets(hidden, inter, group, bits, off);
     int rows = which == 2 ? hidden : inter;
     int K = which == 2 ? inter : hidden;
     const uint8_t *q = blob + off[which];
     const uint16_t *s = (const uint16_t *)(blob + off[3 + which]);
     for (int r = 0; r < rows; ++r)
-        dequant_row(q, s, K, group, r, out + (size_t)r * K);
+        dequant_row(q, s, K, group, bits, r, out + (size_t)r * K);
     return 0;
 }
 
@@ -327,11 +341,11 @@ int coli_oracle_dequant(const uint8_t *blob, int hidden, int inter, int group, i
  * expert some selected token routes to; shared may be NULL (no shared
  * expert). */
 int coli_oracle_layer_tokens(const void *x, int x_bf16, int hidden, int inter, int group,
-                             int top_k, const int32_t *idx, const double *weight,
+                             int bits, int top_k, const int32_t *idx, const double *weight,
                              const uint8_t *const *blobs, const uint8_t *shared,
                              const int32_t *sel, int n_sel, double *y)
 {
-    if (!group_ok(hidden, inter, group))
+    if (!format_ok(hidden, inter, group, bits))
         return -1;
     double *xt = (double *)malloc(sizeof(double) * (size_t)hidden);
     double *ye = (double *)malloc(sizeof(double) * (size_t)hidden);
@@ -357,12 +371,12 @@ int coli_oracle_layer_tokens(const void *x, int x_bf16, int hidden, int inter, i
                 return -1;
             }
             double w = weight[(size_t)t * top_k + j];
-            expert_ffn(blobs[e], hidden, inter, group, xt, ye, scratch);
+            expert_ffn(blobs[e], hidden, inter, group, bits, xt, ye, scratch);
             for (int n = 0; n < hidden; ++n)
                 yt[n] += w * ye[n];
         }
         if (shared) {
-            expert_ffn(shared, hidden, inter, group, xt, ye, scratch);
+            expert_ffn(shared, hidden, inter, group, bits, xt, ye, scratch);
             for (int n = 0; n < hidden; ++n)
                 yt[n] += ye[n];
         }

@@ -50,11 +50,11 @@ def lib() -> C.CDLL:
         L.coli_oracle_router.argtypes = [p, i, p, p, i, i, i, p]
         L.coli_oracle_topk.argtypes = [p, i, i, i, p, p]
         L.coli_oracle_union.argtypes = [p, i, i, i, p, p, p, p, p]
-        L.coli_oracle_blob_bytes.argtypes = [i, i, i]
+        L.coli_oracle_blob_bytes.argtypes = [i, i, i, i]
         L.coli_oracle_blob_bytes.restype = C.c_size_t
-        L.coli_oracle_expert_ffn.argtypes = [p, i, i, i, p, p]
-        L.coli_oracle_dequant.argtypes = [p, i, i, i, i, p]
-        L.coli_oracle_layer_tokens.argtypes = [p, i, i, i, i, i, p, p, p, p, p, i, p]
+        L.coli_oracle_expert_ffn.argtypes = [p, i, i, i, i, p, p]
+        L.coli_oracle_dequant.argtypes = [p, i, i, i, i, i, p]
+        L.coli_oracle_layer_tokens.argtypes = [p, i, i, i, i, i, i, p, p, p, p, p, i, p]
         for f in ("router", "topk", "union", "expert_ffn", "dequant",
                   "layer_tokens"):
             getattr(L, "coli_oracle_" + f).restype = i
@@ -131,36 +131,39 @@ def union(idx: np.ndarray, n_experts: int) -> dict:
                 offsets=offsets, gather=gather)
 
 
-def blob_bytes(hidden: int, inter: int, group: int = 32) -> int:
-    n = int(lib().coli_oracle_blob_bytes(hidden, inter, group))
+def blob_bytes(hidden: int, inter: int, group: int = 32, bits: int = 4) -> int:
+    n = int(lib().coli_oracle_blob_bytes(hidden, inter, group, bits))
     if n == 0:
-        raise ValueError(f"group {group} does not divide hidden {hidden} and inter {inter}")
+        raise ValueError(f"no {bits}-bit layout with group {group} for hidden {hidden}, inter {inter}")
     return n
 
 
-def dequant(blob: np.ndarray, hidden: int, inter: int, which: str, group: int = 32) -> np.ndarray:
-    """One matrix of a canonical blob as fp64 [rows x K] (one fp16 scale per
-    ``group`` consecutive reduction elements)."""
+def dequant(blob: np.ndarray, hidden: int, inter: int, which: str, group: int = 32,
+            bits: int = 4) -> np.ndarray:
+    """One matrix of a canonical blob as fp64 [rows x K] (``bits``-bit
+    weights, one fp16 scale per ``group`` consecutive reduction elements)."""
     w = {"gate": 0, "up": 1, "down": 2}[which]
     rows, K = (hidden, inter) if w == 2 else (inter, hidden)
     out = np.empty((rows, K), dtype=np.float64)
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
-    _check(lib().coli_oracle_dequant(_ptr(blob), hidden, inter, group, w, _ptr(out)),
+    _check(lib().coli_oracle_dequant(_ptr(blob), hidden, inter, group, bits, w, _ptr(out)),
            "dequant")
     return out
 
 
-def expert_ffn(blob: np.ndarray, hidden: int, inter: int, x: np.ndarray, group: int = 32) -> np.ndarray:
+def expert_ffn(blob: np.ndarray, hidden: int, inter: int, x: np.ndarray, group: int = 32,
+               bits: int = 4) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty(hidden, dtype=np.float64)
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
-    _check(lib().coli_oracle_expert_ffn(_ptr(blob), hidden, inter, group, _ptr(x), _ptr(y)),
+    _check(lib().coli_oracle_expert_ffn(_ptr(blob), hidden, inter, group, bits, _ptr(x), _ptr(y)),
            "expert_ffn")
     return y
 
 
 def layer_tokens(x: np.ndarray, hidden: int, inter: int, idx: np.ndarray,
-                 weight: np.ndarray, blobs: dict, shared, tokens, group: int = 32) -> np.ndarray:
+                 weight: np.ndarray, blobs: dict, shared, tokens, group: int = 32,
+                 bits: int = 4) -> np.ndarray:
     """y [len(tokens) x H] fp64 for the listed tokens.
 
     blobs maps expert id -> canonical blob and must cover every expert the
@@ -179,18 +182,18 @@ def layer_tokens(x: np.ndarray, hidden: int, inter: int, idx: np.ndarray,
     sel = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
     y = np.empty((len(sel), hidden), dtype=np.float64)
     _check(lib().coli_oracle_layer_tokens(
-        _ptr(x), bf, hidden, inter, group, k, _ptr(idx), _ptr(weight), table,
+        _ptr(x), bf, hidden, inter, group, bits, k, _ptr(idx), _ptr(weight), table,
         None if sh is None else _ptr(sh), _ptr(sel), len(sel), _ptr(y)),
         "layer_tokens (missing expert blob?)")
     return y
 
 
-def run_layer(x, w_router, bias, k, blobs, shared, hidden, inter, tokens=None, group=32):
+def run_layer(x, w_router, bias, k, blobs, shared, hidden, inter, tokens=None, group=32, bits=4):
     """Route, union and (for ``tokens``, default all) the layer output."""
     logits = router_logits(x, w_router, bias)
     idx, w = topk(logits, k)
     un = union(idx, w_router.shape[1])
     if tokens is None:
         tokens = range(x.shape[0])
-    y = layer_tokens(x, hidden, inter, idx, w, blobs, shared, tokens, group)
+    y = layer_tokens(x, hidden, inter, idx, w, blobs, shared, tokens, group, bits)
     return dict(logits=logits, idx=idx, weight=w, y=y, **un)

@@ -102,7 +102,7 @@ def oracle_y(data, ref, tokens):
 
     def one(t):
         return orc.layer_tokens(data.x, spec.hidden, spec.inter, ref["idx"], ref["weight"],
-                                blobs, data.shared, [t], spec.group)[0]
+                                blobs, data.shared, [t], spec.group, spec.bits)[0]
     with ThreadPoolExecutor(THREADS) as ex:
         ys = list(ex.map(one, tokens))
     return np.stack(ys)

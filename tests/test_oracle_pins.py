@@ -224,16 +224,19 @@ def test_union_matches_brute_force(seed, B, E, k):
 
 # ------------------------------------------------------------------ experts
 
-def numpy_dequant(blob, H, I, which, group=32):
-    sec = configs.blob_sections(H, I, group)
+def numpy_dequant(blob, H, I, which, group=32, bits=4):
+    sec = configs.blob_sections(H, I, group, bits)
     rows, K = (H, I) if which == "down" else (I, H)
     off, size = sec[which + "_q"]
-    b = blob[off:off + size].reshape(rows, K // 2)
-    lo = (b & 15).astype(np.int64)
-    hi = (b >> 4).astype(np.int64)
-    q = np.empty((rows, K), np.int64)
-    q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
-    q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
+    if bits == 8:
+        q = blob[off:off + size].view(np.int8).reshape(rows, K).astype(np.int64)
+    else:
+        b = blob[off:off + size].reshape(rows, K // 2)
+        lo = (b & 15).astype(np.int64)
+        hi = (b >> 4).astype(np.int64)
+        q = np.empty((rows, K), np.int64)
+        q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
+        q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
     soff, ssize = sec[which + "_s"]
     s = blob[soff:soff + ssize].view(np.float16).reshape(rows, K // group).astype(np.float64)
     return q * np.repeat(s, group, axis=1)
@@ -255,41 +258,44 @@ def test_group64_blob_size():
         orc.blob_bytes(6144, 2048, 48)      # 48 does not divide 2048
 
 
-@pytest.mark.parametrize("group", [32, 64])
+FORMATS = [(32, 4), (64, 4), (32, 8), (64, 8)]
+
+
+@pytest.mark.parametrize("group,bits", FORMATS)
 @pytest.mark.parametrize("which", ["gate", "up", "down"])
-def test_dequant_matches_numpy(which, group):
-    spec = configs.TINY.with_(group=group)
+def test_dequant_matches_numpy(which, group, bits):
+    spec = configs.TINY.with_(group=group, bits=bits)
     blob = inputs.expert_blob(spec, 0, 3)
-    np.testing.assert_array_equal(orc.dequant(blob, spec.hidden, spec.inter, which, group),
-                                  numpy_dequant(blob, spec.hidden, spec.inter, which, group))
+    np.testing.assert_array_equal(orc.dequant(blob, spec.hidden, spec.inter, which, group, bits),
+                                  numpy_dequant(blob, spec.hidden, spec.inter, which, group, bits))
 
 
-def numpy_ffn(blob, H, I, x, group=32):
-    g = numpy_dequant(blob, H, I, "gate", group) @ x
-    v = numpy_dequant(blob, H, I, "up", group) @ x
+def numpy_ffn(blob, H, I, x, group=32, bits=4):
+    g = numpy_dequant(blob, H, I, "gate", group, bits) @ x
+    v = numpy_dequant(blob, H, I, "up", group, bits) @ x
     h = g * expit(g) * v
-    return numpy_dequant(blob, H, I, "down", group) @ h
+    return numpy_dequant(blob, H, I, "down", group, bits) @ h
 
 
-@pytest.mark.parametrize("group", [32, 64])
-def test_expert_ffn_matches_numpy_matmul(group):
-    spec = configs.TINY.with_(group=group)
+@pytest.mark.parametrize("group,bits", FORMATS)
+def test_expert_ffn_matches_numpy_matmul(group, bits):
+    spec = configs.TINY.with_(group=group, bits=bits)
     rng = np.random.default_rng(11)
     for e in (0, 5):
         blob = inputs.expert_blob(spec, 0, e)
         x = rng.standard_normal(spec.hidden)
-        got = orc.expert_ffn(blob, spec.hidden, spec.inter, x, group)
-        ref = numpy_ffn(blob, spec.hidden, spec.inter, x, group)
+        got = orc.expert_ffn(blob, spec.hidden, spec.inter, x, group, bits)
+        ref = numpy_ffn(blob, spec.hidden, spec.inter, x, group, bits)
         assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
-def make_blob(H, I, gate_q, up_q, down_q, gate_s, up_s, down_s, group=32):
-    """Canonical blob from explicit int4 matrices and fp16 scales."""
-    sec = configs.blob_sections(H, I, group)
+def make_blob(H, I, gate_q, up_q, down_q, gate_s, up_s, down_s, group=32, bits=4):
+    """Canonical blob from explicit int4 or int8 matrices and fp16 scales."""
+    sec = configs.blob_sections(H, I, group, bits)
     blob = np.zeros(sec["total"][1], np.uint8)
     for name, q in (("gate_q", gate_q), ("up_q", up_q), ("down_q", down_q)):
         q = np.asarray(q, np.int64)
-        packed = ((q[:, 1::2] & 15) << 4) | (q[:, 0::2] & 15)
+        packed = (q & 255) if bits == 8 else ((q[:, 1::2] & 15) << 4) | (q[:, 0::2] & 15)
         off, size = sec[name]
         blob[off:off + size] = packed.astype(np.uint8).ravel()
     for name, s in (("gate_s", gate_s), ("up_s", up_s), ("down_s", down_s)):
@@ -351,6 +357,37 @@ def test_group64_is_group32_with_each_scale_repeated():
         np.testing.assert_array_equal(orc.dequant(b64, H, I, which, 64), orc.dequant(b32, H, I, which, 32))
     x = rng.standard_normal(H)
     np.testing.assert_array_equal(orc.expert_ffn(b64, H, I, x, 64), orc.expert_ffn(b32, H, I, x, 32))
+
+
+def test_int8_blob_size_and_extremes():
+    # int8: one byte per weight, the same scale sections as int4.
+    H, I = 6144, 2048
+    assert orc.blob_bytes(H, I, 32, 8) == configs.blob_bytes(H, I, 32, 8) == 3 * H * I + 3 * H * I // 32 * 2
+    assert orc.blob_bytes(H, I, 64, 8) == configs.blob_bytes(H, I, 64, 8) == 3 * H * I + 3 * H * I // 64 * 2
+    with pytest.raises(ValueError):
+        orc.blob_bytes(H, I, 32, 6)
+    H = I = 64
+    gq = np.tile(np.array([-128, 127, -1, 0]), (I, H // 4))
+    s = np.full((I, 2), 0.0009765625)  # 2^-10, exact in fp16
+    blob = make_blob(H, I, gq, gq, gq.T, s, s, s, bits=8)
+    d = orc.dequant(blob, H, I, "gate", 32, 8)
+    assert d[0, 0] == -128 * 2.0 ** -10 and d[0, 1] == 127 * 2.0 ** -10 and d[0, 2] == -2.0 ** -10
+
+
+def test_int8_holding_int4_values_equals_int4():
+    # The same integers in [-8, 7] stored one per byte and two per byte, with
+    # the same scales, are the same matrices and the same expert, bit for bit.
+    H, I = 256, 128
+    rng = np.random.default_rng(15)
+    q = {n: rng.integers(-8, 8, size=sh) for n, sh in (("g", (I, H)), ("u", (I, H)), ("d", (H, I)))}
+    sc = {n: rng.uniform(0.005, 0.02, size=(sh[0], sh[1] // 32)).astype(np.float16)
+          for n, sh in (("g", (I, H)), ("u", (I, H)), ("d", (H, I)))}
+    b4 = make_blob(H, I, q["g"], q["u"], q["d"], sc["g"], sc["u"], sc["d"])
+    b8 = make_blob(H, I, q["g"], q["u"], q["d"], sc["g"], sc["u"], sc["d"], bits=8)
+    for which in ("gate", "up", "down"):
+        np.testing.assert_array_equal(orc.dequant(b8, H, I, which, 32, 8), orc.dequant(b4, H, I, which, 32, 4))
+    x = rng.standard_normal(H)
+    np.testing.assert_array_equal(orc.expert_ffn(b8, H, I, x, 32, 8), orc.expert_ffn(b4, H, I, x, 32, 4))
 
 
 def test_int4_extremes_and_scale_product_are_exact():
@@ -449,14 +486,14 @@ def test_layer_expert_relabelling_is_invariant():
     np.testing.assert_array_equal(r2["y"], r1["y"])
 
 
-@pytest.mark.parametrize("group", [32, 64])
-def test_layer_matches_numpy_composition_on_tiny(group):
-    spec = configs.TINY.with_(group=group)
+@pytest.mark.parametrize("group,bits", FORMATS)
+def test_layer_matches_numpy_composition_on_tiny(group, bits):
+    spec = configs.TINY.with_(group=group, bits=bits)
     x, w, b, blobs, _ = layer_inputs(spec)
-    r = orc.run_layer(x, w, b, spec.top_k, blobs, None, spec.hidden, spec.inter, group=group)
+    r = orc.run_layer(x, w, b, spec.top_k, blobs, None, spec.hidden, spec.inter, group=group, bits=bits)
     xf = x64(x)
     for t in range(spec.n_tok):
-        ref = sum(r["weight"][t, j] * numpy_ffn(blobs[int(e)], spec.hidden, spec.inter, xf[t], group)
+        ref = sum(r["weight"][t, j] * numpy_ffn(blobs[int(e)], spec.hidden, spec.inter, xf[t], group, bits)
                   for j, e in enumerate(r["idx"][t]))
         assert np.max(np.abs(r["y"][t] - ref)) <= 1e-12 * np.max(np.abs(ref))
 
@@ -480,6 +517,19 @@ def test_generator_is_deterministic_and_per_expert():
     assert not np.array_equal(a[0], a[5])
     assert not np.array_equal(inputs.expert_blob(spec, 1, 0), a[0])
     np.testing.assert_array_equal(inputs.activations(spec, 0), inputs.activations(spec, 0))
+
+
+def test_int8_generator_value_ranges():
+    spec = configs.TINY.with_(bits=8)
+    blob = inputs.expert_blob(spec, 0, 1)
+    sec = configs.blob_sections(spec.hidden, spec.inter, spec.group, 8)
+    for name in ("gate_s", "up_s", "down_s"):
+        off, size = sec[name]
+        s = blob[off:off + size].view(np.float16).astype(np.float64)
+        assert s.min() >= 0.005 / 16 - 1e-6 and s.max() <= 0.02 / 16 + 1e-6
+    off, size = sec["gate_q"]
+    counts = np.bincount(blob[off:off + size], minlength=256)
+    assert counts.min() > 0 and counts.max() < 3 * counts.mean()
 
 
 def test_generator_value_ranges():
