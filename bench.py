@@ -43,12 +43,12 @@ def algorithmic_bytes(spec, n_union, n_tok):
     once, the shared expert's blob, the router weight, activations in, output
     out; and the share of them each expert kernel streams."""
     from int4_routed_expert_layer_amd import configs
-    blob = configs.blob_bytes(spec.hidden, spec.inter, spec.group)
+    blob = configs.blob_bytes(spec.hidden, spec.inter, spec.group, spec.bits)
     experts = n_union + (1 if spec.has_shared else 0)
-    h, i, g = spec.hidden, spec.inter, spec.group
+    h, i, g, b = spec.hidden, spec.inter, spec.group, spec.bits
     gu_experts = n_union if (fused_decode(spec) and spec.has_shared) else experts
-    gateup = gu_experts * (2 * i * h // 2 + 2 * i * (h // g) * 2)
-    down = experts * (h * i // 2 + h * (i // g) * 2)
+    gateup = gu_experts * (2 * i * h * b // 8 + 2 * i * (h // g) * 2)
+    down = experts * (h * i * b // 8 + h * (i // g) * 2)
     router = h * spec.n_experts * 4
     act = n_tok * h * spec.act_bytes + n_tok * h * 4
     return dict(total=experts * blob + router + act, gateup=gateup, down=down, router=router)
@@ -328,7 +328,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--instances", type=int, default=8, help="layer copies rotated per step")
     ap.add_argument("--workloads", default="decode_b1,decode_b4,decode_b64,prefill_b4096,tiered_b16,"
-                                           "decode_b1_g64,prefill_b4096_g64")
+                                           "decode_b1_g64,prefill_b4096_g64,decode_b1_i8")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -449,6 +449,26 @@ def main():
             L3.close()
         del blobs_g, shared_g
 
+    # Int8 experts with group-64 scales (the format the pages require for the
+    # MTP head), decode B=1: twice the weight bytes of int4.
+    if "decode_b1_i8" in wanted:
+        spec1i = spec1.with_(name="decode_b1_i8_g64_h6144_i2048_e256_k8", group=64, bits=8)
+        specs["decode_b1_i8"] = spec1i
+        log(f"generating experts of {spec1i.name}")
+        blobs_i = inputs.expert_blobs(spec1i, 0, range(spec1i.n_experts), threads=8)
+        shared_i = inputs.expert_blob(spec1i, 0, inputs.SHARED)
+        log(f"placing {args.instances} int8 decode layer instances")
+        layers_i = make_layers(B, spec1i, blobs_i, shared_i, args.instances, 64, w1, b1)
+        del blobs_i, shared_i
+        x = B.activations_to_device(inputs.activations(spec1i, 0, 256))
+        wl = Workload("decode_b1_i8", spec1i, layers_i, args.steps, args.warmup, graph_steps=64)
+        log("timing decode_b1_i8")
+        results["decode_b1_i8"] = run_workload(B, torch, wl, x, use_graph=not args.no_graph)
+        for L in layers_i:
+            L.close()
+        del layers_i
+        torch.cuda.empty_cache()
+
     # ---- report
     out_also = {}
     for name, r in results.items():
@@ -475,7 +495,7 @@ def main():
         out_also["tiered_b16"] = tiered
 
     kernel_names = [n for n in ("decode_b1", "decode_b4", "decode_b64", "prefill_b4096", "decode_b1_g64",
-                                "prefill_b4096_g64") if n in out_also]
+                                "prefill_b4096_g64", "decode_b1_i8") if n in out_also]
     if not kernel_names:        # the tiered measurement alone
         print(json.dumps({"metric": METRIC, "value": tiered["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
                           "steps": tiered["calls_per_layer"], "warmup": 2, "ms_per_step": tiered["ms_per_call"],

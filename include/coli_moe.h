@@ -34,10 +34,14 @@
  *   output y_t   = sum_j weight_j * expert_{e_j}(x_t) + shared(x_t).
  *
  * Expert weights are int4 (two's complement, element 2j in the low nibble of
- * byte j, 2j+1 in the high nibble) with one fp16 scale per `group`
- * consecutive reduction elements (w = q * s), group 32 or 64.  The int4
- * container and its group scales follow the README "Scarica il modello"
- * (group-scaled int4, 64 elements per scale in the shipped files).
+ * byte j, 2j+1 in the high nibble) or int8 (one two's-complement byte per
+ * element) with one fp16 scale per `group` consecutive reduction elements
+ * (w = q * s), group 32 or 64.  The int4 container and its group scales
+ * follow the README "Scarica il modello" (group-scaled int4, 64 elements per
+ * scale in the shipped files); the same section and the getting-started page
+ * require int8 for the MTP head, whose layout the pages do not give: int8
+ * blobs keep the int4 blob's sections and scales with one byte per weight.
+ * Int8 layers run on the GEMV path for every batch size.
  *
  * Conventions for every entry point:
  *  - Return codes only; nothing aborts or throws across the ABI.  On error
@@ -61,7 +65,7 @@
 extern "C" {
 #endif
 
-#define COLI_ABI_VERSION 2
+#define COLI_ABI_VERSION 3
 
 typedef enum {
     COLI_OK = 0,
@@ -80,8 +84,8 @@ typedef enum { COLI_TIER_VRAM = 0, COLI_TIER_HOST = 1 } coli_tier;
  * definition; for a given strategy results are deterministic. */
 typedef enum {
     COLI_PATH_AUTO = 0,
-    COLI_PATH_GEMV = 1,      /* wave-per-row int4 GEMV on the vector ALUs */
-    COLI_PATH_GROUPED = 2    /* grouped int4->fp16 GEMM on MFMA */
+    COLI_PATH_GEMV = 1,      /* int4 or int8 GEMV on the vector ALUs */
+    COLI_PATH_GROUPED = 2    /* grouped int4->fp16 GEMM on MFMA (int4 only) */
 } coli_path;
 
 /* Expert id of the shared expert in coli_expert_place. */
@@ -96,17 +100,19 @@ typedef struct {
     int32_t max_tokens;  /* largest n_tok any call will pass (>= 1) */
     int32_t act;         /* coli_act: dtype of x */
     int32_t group;       /* reduction elements per fp16 weight scale: 32 or 64 */
+    int32_t weight_bits; /* 4 (int4) or 8 (int8) */
 } coli_moe_dims;
 
 typedef struct coli_layer coli_layer;   /* opaque, library-owned */
 
-/* Bytes of one expert blob for H, I and scale group G: gate_q, up_q
- * ([I x H/2] bytes each), down_q ([H x I/2]), gate_s, up_s (fp16
- * [I x H/G]), down_s (fp16 [H x I/G]), in that order, each section starting
- * on a 256-byte boundary.  The README stores an expert's three matrices
- * contiguously so one read fetches all of them; this blob is that unit.
- * Returns 0 for invalid sizes or a group other than 32 and 64. */
-size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group);
+/* Bytes of one expert blob for H, I, scale group G and weight width b:
+ * gate_q, up_q ([I x H*b/8] bytes each), down_q ([H x I*b/8]), gate_s, up_s
+ * (fp16 [I x H/G]), down_s (fp16 [H x I/G]), in that order, each section
+ * starting on a 256-byte boundary.  The README stores an expert's three
+ * matrices contiguously so one read fetches all of them; this blob is that
+ * unit.  Returns 0 for invalid sizes, a group other than 32 and 64, or a
+ * width other than 4 and 8. */
+size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group, int32_t weight_bits);
 
 /* Repack a blob (host pointer, layout above) into the library's device
  * layout (host pointer `out`, same size): the bytes coli_expert_place keeps
@@ -115,11 +121,14 @@ size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group);
  * of a tile: row L mod 16, columns 32s + 8(L div 16) + 0..7 in dword s, each
  * stored as q + 8 with columns 2j and 2j+1 in nibbles j and 4+j; each tile's
  * 16 x 128/group fp16 scales are stored row-major at the same tile index in
- * the scale section.  Host-only, no device needed.  COLI_E_INVALID for NULL
- * pointers, sizes that are not multiples of 128, or a group other than 32
- * and 64. */
+ * the scale section.  Int8 tiles are 16 rows x 64 columns: dword s of lane
+ * L holds row L mod 16, columns 32(s div 2) + 8(L div 16) + 4(s mod 2) +
+ * 0..3 as q + 128 in byte order 0, 2, 1, 3; their 16 x 64/group scales
+ * likewise.  Host-only, no device needed.  COLI_E_INVALID for NULL pointers,
+ * sizes that are not multiples of 128, a group other than 32 and 64, or a
+ * width other than 4 and 8. */
 coli_status coli_expert_repack(const void *blob_host, void *out_host,
-                               int32_t hidden, int32_t inter, int32_t group);
+                               int32_t hidden, int32_t inter, int32_t group, int32_t weight_bits);
 
 /* Create a layer on HIP device `device`.  Allocates the router copy, the
  * expert pointer table and scratch sized from dims->max_tokens.
@@ -206,7 +215,9 @@ coli_status coli_moe_layer(coli_layer *layer, const void *x, int32_t n_tok,
                            int32_t *offsets, int32_t *gather, float *y,
                            void *stream);
 
-/* Choose the forward strategy (coli_path).  Default COLI_PATH_AUTO. */
+/* Choose the forward strategy (coli_path).  Default COLI_PATH_AUTO.
+ * COLI_E_UNSUPPORTED for COLI_PATH_GROUPED on an int8 layer (int8 layers
+ * always take the GEMV path). */
 coli_status coli_layer_set_path(coli_layer *layer, int32_t path);
 
 /* Statistics of the last tiered forward call (host pointers, may be NULL):

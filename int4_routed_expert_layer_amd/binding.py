@@ -27,8 +27,8 @@ SIGNATURES = {
     "coli_abi_version": (_i32, []),
     "coli_status_str": (C.c_char_p, [C.c_int]),
     "coli_last_error": (C.c_char_p, [_p]),
-    "coli_expert_blob_bytes": (_sz, [_i32, _i32, _i32]),
-    "coli_expert_repack": (C.c_int, [_p, _p, _i32, _i32, _i32]),
+    "coli_expert_blob_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "coli_expert_repack": (C.c_int, [_p, _p, _i32, _i32, _i32, _i32]),
     "coli_layer_create": (C.c_int, [_p, C.c_int, _p]),
     "coli_layer_destroy": (C.c_int, [_p]),
     "coli_router_set": (C.c_int, [_p, _p, _p]),
@@ -52,7 +52,7 @@ KERNEL_KINDS = ["router", "topk", "union", "plan", "gateup", "down", "combine"]
 class Dims(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("inter", C.c_int32), ("n_experts", C.c_int32),
                 ("top_k", C.c_int32), ("has_shared", C.c_int32), ("max_tokens", C.c_int32),
-                ("act", C.c_int32), ("group", C.c_int32)]
+                ("act", C.c_int32), ("group", C.c_int32), ("weight_bits", C.c_int32)]
 
 
 class ColiError(RuntimeError):
@@ -86,15 +86,15 @@ def status_str(st: int) -> str:
     return lib.coli_status_str(st).decode()
 
 
-def blob_bytes(hidden: int, inter: int, group: int = 32) -> int:
-    return int(lib.coli_expert_blob_bytes(hidden, inter, group))
+def blob_bytes(hidden: int, inter: int, group: int = 32, bits: int = 4) -> int:
+    return int(lib.coli_expert_blob_bytes(hidden, inter, group, bits))
 
 
-def repack(blob: np.ndarray, hidden: int, inter: int, group: int = 32) -> np.ndarray:
+def repack(blob: np.ndarray, hidden: int, inter: int, group: int = 32, bits: int = 4) -> np.ndarray:
     """Device-layout bytes of a canonical expert blob (host-side repack)."""
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
     out = np.empty_like(blob)
-    _check(lib.coli_expert_repack(blob.ctypes.data, out.ctypes.data, hidden, inter, group))
+    _check(lib.coli_expert_repack(blob.ctypes.data, out.ctypes.data, hidden, inter, group, bits))
     return out
 
 
@@ -116,9 +116,9 @@ class MoELayer:
     """One MoE layer living on a HIP device (owns its router and experts)."""
 
     def __init__(self, hidden, inter, n_experts, top_k, has_shared, max_tokens,
-                 act="bf16", device=0, group=32):
+                 act="bf16", device=0, group=32, bits=4):
         self.dims = Dims(hidden, inter, n_experts, top_k, int(bool(has_shared)),
-                         max_tokens, ACT_BF16 if act == "bf16" else ACT_F32, group)
+                         max_tokens, ACT_BF16 if act == "bf16" else ACT_F32, group, bits)
         self.device = device
         h = C.c_void_p()
         _check(lib.coli_layer_create(C.byref(self.dims), device, C.byref(h)))
@@ -127,7 +127,7 @@ class MoELayer:
     @classmethod
     def from_spec(cls, spec, max_tokens=None, device=0):
         return cls(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared,
-                   max_tokens or spec.n_tok, spec.act, device, spec.group)
+                   max_tokens or spec.n_tok, spec.act, device, spec.group, spec.bits)
 
     def close(self):
         if getattr(self, "handle", None):

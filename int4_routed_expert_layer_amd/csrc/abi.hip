@@ -20,9 +20,10 @@ namespace coli {
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-BlobLayout blob_layout(int hidden, int inter, int group) {
+BlobLayout blob_layout(int hidden, int inter, int group, int bits) {
     const size_t h = static_cast<size_t>(hidden), i = static_cast<size_t>(inter), g = static_cast<size_t>(group);
-    const size_t sz[6] = {i * h / 2, i * h / 2, h * i / 2,
+    const size_t b = static_cast<size_t>(bits);
+    const size_t sz[6] = {i * h * b / 8, i * h * b / 8, h * i * b / 8,
                           i * (h / g) * 2, i * (h / g) * 2, h * (i / g) * 2};
     size_t off[7];
     size_t o = 0;
@@ -31,7 +32,7 @@ BlobLayout blob_layout(int hidden, int inter, int group) {
         o = align256(o + sz[k]);
     }
     off[6] = o;
-    return BlobLayout{off[0], off[1], off[2], off[3], off[4], off[5], off[6], group};
+    return BlobLayout{off[0], off[1], off[2], off[3], off[4], off[5], off[6], group, bits};
 }
 
 namespace {
@@ -94,8 +95,39 @@ void repack_panels(const uint8_t *q_src, const uint16_t *s_src, int K, int group
     }
 }
 
-void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter, int group) {
-    const BlobLayout L = blob_layout(hidden, inter, group);
+// Int8 variant: chunks of 16 rows x 64 columns; dword s of lane L holds
+// columns k0 = 64c + 32(s >> 1) + 8(L >> 4) + 4(s & 1) .. k0+3 of row
+// L & 15 as u = q + 128 in byte order k0, k0+2, k0+1, k0+3; the chunk's
+// 16 x 64/group scales follow row-major at its index in the scale section.
+void repack_panels_i8(const uint8_t *q_src, const uint16_t *s_src, int K, int group, int p_begin,
+                      int p_end, uint8_t *q_dst, uint16_t *s_dst) {
+    constexpr int kCols = 64;
+    const int C = K / kCols;
+    const int groups = K / group, per_chunk = kCols / group;
+    for (int p = p_begin; p < p_end; ++p) {
+        for (int c = 0; c < C; ++c) {
+            uint8_t *qc = q_dst + (static_cast<size_t>(p) * C + c) * kChunkBytes;
+            uint16_t *sc = s_dst + (static_cast<size_t>(p) * C + c) * (kPanel * per_chunk);
+            for (int lane = 0; lane < 64; ++lane) {
+                const uint8_t *row = q_src + static_cast<size_t>(p * kPanel + (lane & 15)) * K;
+                for (int s = 0; s < 4; ++s) {
+                    const int k0 = c * kCols + 32 * (s >> 1) + 8 * (lane >> 4) + 4 * (s & 1);
+                    uint8_t *out = qc + lane * 16 + s * 4;
+                    out[0] = row[k0] ^ 0x80u;
+                    out[1] = row[k0 + 2] ^ 0x80u;
+                    out[2] = row[k0 + 1] ^ 0x80u;
+                    out[3] = row[k0 + 3] ^ 0x80u;
+                }
+            }
+            for (int r = 0; r < kPanel; ++r)
+                for (int t = 0; t < per_chunk; ++t)
+                    sc[r * per_chunk + t] = s_src[static_cast<size_t>(p * kPanel + r) * groups + per_chunk * c + t];
+        }
+    }
+}
+
+void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter, int group, int bits) {
+    const BlobLayout L = blob_layout(hidden, inter, group, bits);
     std::memset(dst, 0, L.total);
     struct Mat { size_t q, s; int rows, K; } mats[3] = {
         {L.gate_q, L.gate_s, inter, hidden},
@@ -107,8 +139,12 @@ void repack_blob(const uint8_t *src, uint8_t *dst, int hidden, int inter, int gr
     for (const Mat &m : mats) {
         const int P = m.rows / kPanel;
         auto run = [&](int b, int e) {
-            repack_panels(src + m.q, reinterpret_cast<const uint16_t *>(src + m.s), m.K, group, b, e,
-                          dst + m.q, reinterpret_cast<uint16_t *>(dst + m.s));
+            if (bits == 8)
+                repack_panels_i8(src + m.q, reinterpret_cast<const uint16_t *>(src + m.s), m.K, group, b, e,
+                                 dst + m.q, reinterpret_cast<uint16_t *>(dst + m.s));
+            else
+                repack_panels(src + m.q, reinterpret_cast<const uint16_t *>(src + m.s), m.K, group, b, e,
+                              dst + m.q, reinterpret_cast<uint16_t *>(dst + m.s));
         };
         if (nthreads <= 1 || P < 2 * nthreads) {
             run(0, P);
@@ -294,6 +330,7 @@ bool dims_valid(const coli_moe_dims *d, std::string &why) {
     if (d->has_shared != 0 && d->has_shared != 1) { why = "has_shared must be 0 or 1"; return false; }
     if (d->act != COLI_ACT_F32 && d->act != COLI_ACT_BF16) { why = "act must be COLI_ACT_F32 or COLI_ACT_BF16"; return false; }
     if (!group_supported(d->group)) { why = "group must be 32 or 64"; return false; }
+    if (!bits_supported(d->weight_bits)) { why = "weight_bits must be 4 or 8"; return false; }
     if (d->top_k > d->n_experts || d->top_k > kMaxTopK) {
         std::snprintf(buf, sizeof buf, "top_k %d must be <= min(n_experts, %d)", d->top_k, kMaxTopK);
         why = buf;
@@ -329,6 +366,7 @@ bool all_routed_resident(const coli_layer *L) {
 }
 
 int choose_path(const coli_layer *L, int n_tok) {
+    if (L->d.weight_bits == 8) return COLI_PATH_GEMV;        // int8 runs on the GEMV kernels only
     if (L->path != COLI_PATH_AUTO) return L->path;
     return n_tok <= 4 ? COLI_PATH_GEMV : COLI_PATH_GROUPED;   // B=4: 183 us GEMV, 203 us grouped
 }
@@ -463,18 +501,22 @@ const char *coli_last_error(const coli_layer *L) {
     return L ? L->msg.c_str() : g_create_error.c_str();
 }
 
-size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group) {
-    if (!group_supported(group) || hidden <= 0 || inter <= 0 || hidden % group || inter % group) return 0;
-    return blob_layout(hidden, inter, group).total;
+size_t coli_expert_blob_bytes(int32_t hidden, int32_t inter, int32_t group, int32_t weight_bits) {
+    if (!group_supported(group) || !bits_supported(weight_bits) || hidden <= 0 || inter <= 0 ||
+        hidden % group || inter % group)
+        return 0;
+    return blob_layout(hidden, inter, group, weight_bits).total;
 }
 
 coli_status coli_expert_repack(const void *blob_host, void *out_host, int32_t hidden, int32_t inter,
-                               int32_t group) {
+                               int32_t group, int32_t weight_bits) {
     if (!blob_host || !out_host) return fail(nullptr, COLI_E_INVALID, "NULL host pointer");
     if (hidden <= 0 || inter <= 0 || hidden % kChunkK || inter % kChunkK)
         return fail(nullptr, COLI_E_INVALID, "hidden and inter must be positive multiples of %d", kChunkK);
     if (!group_supported(group)) return fail(nullptr, COLI_E_INVALID, "group %d must be 32 or 64", group);
-    repack_blob(static_cast<const uint8_t *>(blob_host), static_cast<uint8_t *>(out_host), hidden, inter, group);
+    if (!bits_supported(weight_bits)) return fail(nullptr, COLI_E_INVALID, "weight_bits %d must be 4 or 8", weight_bits);
+    repack_blob(static_cast<const uint8_t *>(blob_host), static_cast<uint8_t *>(out_host), hidden, inter, group,
+                weight_bits);
     return COLI_OK;
 }
 
@@ -499,7 +541,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     L->device = device;
     L->n_cu = prop.multiProcessorCount;
     L->max_lds = prop.sharedMemPerBlock;
-    L->lay = blob_layout(dims->hidden, dims->inter, dims->group);
+    L->lay = blob_layout(dims->hidden, dims->inter, dims->group, dims->weight_bits);
     const int E = dims->n_experts, H = dims->hidden, I = dims->inter;
     const size_t T = static_cast<size_t>(dims->max_tokens);
     const size_t rows = T * dims->top_k + T;
@@ -560,6 +602,8 @@ coli_status coli_layer_destroy(coli_layer *L) {
 coli_status coli_layer_set_path(coli_layer *L, int32_t path) {
     if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
     if (path < COLI_PATH_AUTO || path > COLI_PATH_GROUPED) return fail(L, COLI_E_INVALID, "bad path %d", path);
+    if (path == COLI_PATH_GROUPED && L->d.weight_bits == 8)
+        return fail(L, COLI_E_UNSUPPORTED, "int8 experts run on the GEMV path only");
     L->path = path;
     return COLI_OK;
 }
@@ -597,7 +641,7 @@ coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_ho
     DeviceGuard guard(L->device);
     const uint8_t *src = static_cast<const uint8_t *>(blob_host);
     if (tier == COLI_TIER_VRAM) {
-        repack_blob(src, L->pin_stage, L->d.hidden, L->d.inter, L->d.group);
+        repack_blob(src, L->pin_stage, L->d.hidden, L->d.inter, L->d.group, L->d.weight_bits);
         if (!x.dev) HIP_TRY(L, hipMalloc(&x.dev, L->lay.total), "expert VRAM");
         HIP_TRY(L, hipMemcpy(x.dev, L->pin_stage, L->lay.total, hipMemcpyHostToDevice), "expert upload");
         if (x.host) {
@@ -607,7 +651,7 @@ coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_ho
         L->table_host[idx] = x.dev;
     } else {
         if (!x.host) HIP_TRY(L, hipHostMalloc(reinterpret_cast<void **>(&x.host), L->lay.total, hipHostMallocDefault), "expert pinned host");
-        repack_blob(src, x.host, L->d.hidden, L->d.inter, L->d.group);
+        repack_blob(src, x.host, L->d.hidden, L->d.inter, L->d.group, L->d.weight_bits);
         L->table_host[idx] = nullptr;
     }
     x.tier = tier;

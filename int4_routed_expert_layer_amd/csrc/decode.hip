@@ -215,13 +215,13 @@ __device__ void select_few_tokens(const FwdArgs &a, const FrontArgs &f) {
     }
 }
 
-template <int GS, int NT, bool BF16>
+template <class F, int NT, bool BF16>
 __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, FrontArgs f, int router_blocks) {
     extern __shared__ __align__(16) uint8_t lds[];
     if (static_cast<int>(blockIdx.x) >= router_blocks) {
         const int p = blockIdx.x - router_blocks;
         // One block per CU here: a deeper load pipeline than the routed kernel.
-        dev::gateup_panel<GS, NT, false, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
+        dev::gateup_panel<F, NT, false, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
                                                             a.n_tok, p, lds, dev::lds_address(lds));
         return;
     }
@@ -233,22 +233,22 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
     }
 }
 
-template <int GS, int NT>
+template <class F, int NT>
 hipError_t launch_t(const FwdArgs &a, const FrontArgs &f, size_t lds, hipStream_t s) {
     const int router_blocks = (a.n_experts + 3) / 4;
     const int grid = router_blocks + (a.has_shared ? a.inter / kPanel : 0);
     if (a.act_bf16)
-        launch(decode_front_kernel<GS, NT, true>, grid, kFrontThreads, lds, s, a, f, router_blocks);
+        launch(decode_front_kernel<F, NT, true>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     else
-        launch(decode_front_kernel<GS, NT, false>, grid, kFrontThreads, lds, s, a, f, router_blocks);
+        launch(decode_front_kernel<F, NT, false>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     return hipGetLastError();
 }
 
-template <int GS>
+template <class F>
 hipError_t launch_nt(const FwdArgs &a, const FrontArgs &f, int nt, size_t lds, hipStream_t s) {
-    if (nt == 1) return launch_t<GS, 1>(a, f, lds, s);
-    if (nt == 2) return launch_t<GS, 2>(a, f, lds, s);
-    return launch_t<GS, 4>(a, f, lds, s);
+    if (nt == 1) return launch_t<F, 1>(a, f, lds, s);
+    if (nt == 2) return launch_t<F, 2>(a, f, lds, s);
+    return launch_t<F, 4>(a, f, lds, s);
 }
 
 }  // namespace
@@ -258,7 +258,10 @@ hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_
     const int nt = a.n_tok == 1 ? 1 : (a.n_tok == 2 ? 2 : 4);
     const size_t lds = a.has_shared ? dev::gateup_lds_bytes(nt, a.hidden) : 0;
     if (lds > max_lds) return hipErrorInvalidValue;
-    return a.lay.group == 64 ? launch_nt<64>(a, f, nt, lds, s) : launch_nt<32>(a, f, nt, lds, s);
+    hipError_t e = hipSuccess;
+    dev::dispatch_format(a.lay.group, a.lay.bits,
+                         [&](auto fmt) { e = launch_nt<decltype(fmt)>(a, f, nt, lds, s); });
+    return e;
 }
 
 }  // namespace coli

@@ -25,9 +25,15 @@
 // fp16 (bf16/fp32 inputs are rounded once when staged; they must lie inside
 // the fp16 range).
 //
+// Int8 weights (WFmt<.., 8>) use the same scheme with one byte per column:
+// u = q + 128 sits in the low byte of each fp16 half, the activations are
+// staged plainly and the seed is -1152 times their sum.
+//
 // Partial sums are reduced across the four lanes that share a row and then
 // across waves in a fixed order, so results are deterministic.
 #pragma once
+
+#include <type_traits>
 
 #include "dev_common.h"
 
@@ -89,28 +95,99 @@ __host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
 constexpr int kGateUpGroup = 2;   // gate/up chunks per register buffer
 constexpr int kPipeGroup = 2;   // down chunks per register buffer
 
-// One lane's scales of a chunk: the 128/GS fp16 scales of its row (8 bytes
-// for group size 32, 4 bytes for 64).
-template <int GS> struct ScaleRec { using T = uint2; };
-template <> struct ScaleRec<64> { using T = uint32_t; };
-template <int GS> using scale_rec_t = typename ScaleRec<GS>::T;
+// sum over the 8 columns k0..k0+7 of two int8 dwords (columns k0..k0+3 in
+// w0, k0+4..k0+7 in w1, each stored as u = q + 128 in byte order k, k+2, k+1,
+// k+3) of q * x, given the plainly staged activations xv and their seed c:
+// (w & 0x00FF00FF) | 0x64006400 is the fp16 pair (1024 + u_k, 1024 + u_k+1),
+// the same on w >> 8 gives columns k+2, k+3, and the seed removes
+// 1152 x per column.
+__device__ __forceinline__ float dot8_i8(uint32_t w0, uint32_t w1, uint4 xv, float c, uint32_t M8,
+                                         uint32_t G) {
+    float d = dot2_f16((w0 & M8) | G, xv.x, c);
+    d = dot2_f16(((w0 >> 8) & M8) | G, xv.y, d);
+    d = dot2_f16((w1 & M8) | G, xv.z, d);
+    d = dot2_f16(((w1 >> 8) & M8) | G, xv.w, d);
+    return d;
+}
 
-// Scale of dword s (chunk columns 32s .. 32s+31) from a lane's record.
-template <int GS>
-__device__ __forceinline__ float slice_scale(scale_rec_t<GS> r, int s) {
-    if constexpr (GS == 32) {
-        const uint32_t d = (s >> 1) ? r.y : r.x;
-        return half_bits_to_f32((d >> (16 * (s & 1))) & 0xFFFFu);
+// Stage 8 activations into LDS as plain fp16 with the int8 dot seed.
+__device__ __forceinline__ void stage8_i8(const float *v, uint8_t *dst_x, float *dst_c) {
+    _Float16 h[8];
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[i] = static_cast<_Float16>(v[i]);
+        sum = sum + static_cast<float>(h[i]);
+    }
+    // (1024 + q + 128) x - 1152 x = q x.
+    *dst_c = -1152.0f * sum;
+    *reinterpret_cast<uint4 *>(dst_x) = __builtin_bit_cast(uint4, h);
+}
+
+// Weight format of the GEMV work items: GS reduction elements per fp16 scale
+// (32 or 64) and WB bits per weight (4 or 8).  A 1 KB chunk covers 16 rows x
+// kCols columns (128 int4 or 64 int8); the 16 bytes of lane L hold row L & 15
+// and, for each 32-column slice j of the chunk, columns 32j + 8(L >> 4) +
+// 0..7: one dword (int4 nibbles, dword j) or two (int8 bytes, dwords 2j and
+// 2j + 1).  A chunk's scales are [16 rows][kCols / GS] fp16; each lane
+// loads its row's record (an int8 group-64 record of 2 bytes is read as the
+// dword of its row pair).
+template <int GS, int WB>
+struct WFmt {
+    static_assert((GS == 32 || GS == 64) && (WB == 4 || WB == 8), "group 32 or 64, 4 or 8 bits");
+    static constexpr int kGroup = GS;
+    static constexpr int kBits = WB;
+    static constexpr int kCols = WB == 4 ? 128 : 64;
+    static constexpr int kSlices = kCols / 32;
+    static constexpr int kGroupsPerChunk = kCols / GS;
+    static constexpr int kScaleChunkBytes = kPanel * kGroupsPerChunk * 2;
+    using Rec = typename std::conditional<kGroupsPerChunk == 4, uint2, uint32_t>::type;
+    static constexpr uint32_t kMask0 = WB == 4 ? 0x000F000Fu : 0x00FF00FFu;
+    static constexpr uint32_t kMask1 = WB == 4 ? 0x00F000F0u : 0x00FF00FFu;
+
+    __device__ static uint32_t rec_offset(int row) {
+        return kGroupsPerChunk == 1 ? static_cast<uint32_t>(row & ~1) * 2
+                                    : static_cast<uint32_t>(row) * kGroupsPerChunk * 2;
+    }
+    // Scale of slice j for the lane of row `row`.
+    __device__ static float scale(Rec r, int j, int row) {
+        if constexpr (kGroupsPerChunk == 4) {
+            const uint32_t d = (j >> 1) ? r.y : r.x;
+            return half_bits_to_f32((d >> (16 * (j & 1))) & 0xFFFFu);
+        } else if constexpr (kGroupsPerChunk == 2) {
+            return half_bits_to_f32((r >> (16 * (j / (GS / 32)))) & 0xFFFFu);
+        } else {
+            return half_bits_to_f32((r >> (16 * (row & 1))) & 0xFFFFu);
+        }
+    }
+    // q . x over the lane's 8 columns of slice j.
+    __device__ static float dot(const uint32_t (&w)[4], int j, uint4 xv, float c, uint32_t M0, uint32_t M1,
+                                uint32_t G) {
+        if constexpr (WB == 4) return dot8(w[j], xv, c, M0, M1, G);
+        else return dot8_i8(w[2 * j], w[2 * j + 1], xv, c, M0, G);
+    }
+    __device__ static void stage(const float *v, uint8_t *dst_x, float *dst_c) {
+        if constexpr (WB == 4) stage8(v, dst_x, dst_c);
+        else stage8_i8(v, dst_x, dst_c);
+    }
+};
+
+// Calls fn(F{}) with the format of a layer.
+template <class Fn>
+inline void dispatch_format(int group, int bits, Fn &&fn) {
+    if (bits == 8) {
+        if (group == 64) fn(WFmt<64, 8>{});
+        else fn(WFmt<32, 8>{});
     } else {
-        static_assert(GS == 64, "group size 32 or 64");
-        return half_bits_to_f32((r >> (16 * (s >> 1))) & 0xFFFFu);
+        if (group == 64) fn(WFmt<64, 4>{});
+        else fn(WFmt<32, 4>{});
     }
 }
 
-template <int NG, int GS>
+template <int NG, class F>
 struct GateUpBuf {
     uint4 gw[NG], uw[NG];
-    scale_rec_t<GS> gs[NG], us[NG];
+    typename F::Rec gs[NG], us[NG];
 };
 
 // Sources of one gate/up panel: the blob descriptor, the lane offsets of a
@@ -121,21 +198,21 @@ struct GateUpSrc {
     uint32_t gq, uq, gs, us;  // uniform
 };
 
-template <int NG, int GS>
-__device__ __forceinline__ void gateup_load(GateUpBuf<NG, GS> &b, const GateUpSrc &S, int first, int step, int C) {
+template <int NG, class F>
+__device__ __forceinline__ void gateup_load(GateUpBuf<NG, F> &b, const GateUpSrc &S, int first, int step, int C) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + step * g, C - 1));
         b.gw[g] = bload<uint4>(S.r, S.vq, S.gq + c * kChunkBytes);
         b.uw[g] = bload<uint4>(S.r, S.vq, S.uq + c * kChunkBytes);
-        b.gs[g] = bload<scale_rec_t<GS>>(S.r, S.vs, S.gs + c * scale_chunk_bytes<GS>());
-        b.us[g] = bload<scale_rec_t<GS>>(S.r, S.vs, S.us + c * scale_chunk_bytes<GS>());
+        b.gs[g] = bload<typename F::Rec>(S.r, S.vs, S.gs + c * F::kScaleChunkBytes);
+        b.us[g] = bload<typename F::Rec>(S.r, S.vs, S.us + c * F::kScaleChunkBytes);
     }
 }
 
-template <int MAXM, int NG, int GS>
-__device__ __forceinline__ void gateup_math(const GateUpBuf<NG, GS> &b, const uint8_t *xs, const float *cs, int H,
-                                            int first, int step, int count, int kq, int mc,
+template <int MAXM, int NG, class F>
+__device__ __forceinline__ void gateup_math(const GateUpBuf<NG, F> &b, const uint8_t *xs, const float *cs, int H,
+                                            int first, int step, int count, int row, int kq, int mc,
                                             uint32_t M0, uint32_t M1, uint32_t G, float *gacc,
                                             float *vacc) {
 #pragma unroll
@@ -145,17 +222,17 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf<NG, GS> &b, const ui
         const uint32_t gws[4] = {b.gw[g].x, b.gw[g].y, b.gw[g].z, b.gw[g].w};
         const uint32_t uws[4] = {b.uw[g].x, b.uw[g].y, b.uw[g].z, b.uw[g].w};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float sg = slice_scale<GS>(b.gs[g], s);
-            const float su = slice_scale<GS>(b.us[g], s);
-            const int k0 = c * kChunkK + 32 * s + 8 * kq;
+        for (int s = 0; s < F::kSlices; ++s) {
+            const float sg = F::scale(b.gs[g], s, row);
+            const float su = F::scale(b.us[g], s, row);
+            const int k0 = c * F::kCols + 32 * s + 8 * kq;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 if (m < mc) {
                     const uint4 xv = *reinterpret_cast<const uint4 *>(xs + (static_cast<size_t>(m) * H + k0) * 2);
                     const float c8 = cs[m * (H / 8) + (k0 >> 3)];
-                    gacc[m] = __builtin_fmaf(sg, dot8(gws[s], xv, c8, M0, M1, G), gacc[m]);
-                    vacc[m] = __builtin_fmaf(su, dot8(uws[s], xv, c8, M0, M1, G), vacc[m]);
+                    gacc[m] = __builtin_fmaf(sg, F::dot(gws, s, xv, c8, M0, M1, G), gacc[m]);
+                    vacc[m] = __builtin_fmaf(su, F::dot(uws, s, xv, c8, M0, M1, G), vacc[m]);
                 }
             }
         }
@@ -167,25 +244,25 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf<NG, GS> &b, const ui
 // a row).  Writes h rows (fp16; device-coherent stores when COHERENT, for a
 // consumer in the same launch).  All 256 threads must call it (it
 // synchronises the workgroup).  NG chunks per register buffer (two buffers in
-// flight): more for few workgroups per CU.  GS is the scale group size.
-template <int GS, int MAXM, bool COHERENT = false, int NG = kGateUpGroup, class Rows>
+// flight): more for few workgroups per CU.  F is the weight format (WFmt).
+template <class F, int MAXM, bool COHERENT = false, int NG = kGateUpGroup, class Rows>
 __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int p,
                              uint8_t *lds, uint32_t lds_addr) {
     const int H = a.hidden, I = a.inter;
-    const int C = H / kChunkK;
+    const int C = H / F::kCols;
     const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
     const int row = lane & 15, kq = lane >> 4;
     GateUpSrc P;
     P.r = make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
     P.vq = static_cast<uint32_t>(lane) * 16;
-    P.vs = static_cast<uint32_t>(row) * scale_row_bytes<GS>();
+    P.vs = F::rec_offset(row);
     P.gq = static_cast<uint32_t>(a.lay.gate_q + static_cast<size_t>(p) * C * kChunkBytes);
     P.uq = static_cast<uint32_t>(a.lay.up_q + static_cast<size_t>(p) * C * kChunkBytes);
-    P.gs = static_cast<uint32_t>(a.lay.gate_s + static_cast<size_t>(p) * C * scale_chunk_bytes<GS>());
-    P.us = static_cast<uint32_t>(a.lay.up_s + static_cast<size_t>(p) * C * scale_chunk_bytes<GS>());
+    P.gs = static_cast<uint32_t>(a.lay.gate_s + static_cast<size_t>(p) * C * F::kScaleChunkBytes);
+    P.us = static_cast<uint32_t>(a.lay.up_s + static_cast<size_t>(p) * C * F::kScaleChunkBytes);
     // Chunks of this wave: wave, wave + 4, ...
     const int nper = wave < C ? (C - wave + 3) / 4 : 0;
-    const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+    const uint32_t M0 = vconst(F::kMask0), M1 = vconst(F::kMask1), G = vconst(0x64006400u);
 
     // LDS: x [MAXM][H] fp16, seeds [MAXM][H/8] fp32, partials [4][MAXM][16][2].
     uint8_t *xs = lds;
@@ -198,7 +275,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) gacc[m] = vacc[m] = 0.0f;
 
-        GateUpBuf<NG, GS> A, B;
+        GateUpBuf<NG, F> A, B;
         bool b_issued = false;
         if (a.act_bf16 && (H * 2) % 1024 == 0) {
             // bf16 rows are copied straight into the staging area (1 KB per
@@ -242,7 +319,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                     v[2 * j] = bf16_bits_to_f32(w4[j] & 0xFFFFu);
                     v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
                 }
-                stage8(v, dst, cs + m * (H / 8) + q);
+                F::stage(v, dst, cs + m * (H / 8) + q);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -268,18 +345,18 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                 v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
                 v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
             }
-            stage8(v, xs + (static_cast<size_t>(m) * H + 8 * q) * 2, cs + m * (H / 8) + q);
+            F::stage(v, xs + (static_cast<size_t>(m) * H + 8 * q) * 2, cs + m * (H / 8) + q);
         }
         __syncthreads();
         }
         // i indexes this wave's chunk list; buffers alternate A, B.
         for (int i = 0; i < nper; i += 2 * NG) {
             if (i + NG < nper && (i > 0 || !b_issued)) gateup_load(B, P, wave + 4 * (i + NG), 4, C);
-            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(NG, nper - i), kq, mc, M0, M1, G,
+            gateup_math<MAXM>(A, xs, cs, H, wave + 4 * i, 4, min(NG, nper - i), row, kq, mc, M0, M1, G,
                               gacc, vacc);
             if (i + 2 * NG < nper) gateup_load(A, P, wave + 4 * (i + 2 * NG), 4, C);
             if (i + NG < nper)
-                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + NG), 4, min(NG, nper - i - NG), kq, mc, M0, M1, G,
+                gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + NG), 4, min(NG, nper - i - NG), row, kq, mc, M0, M1, G,
                                   gacc, vacc);
         }
 #pragma unroll
@@ -327,26 +404,26 @@ struct PlainRows {
     __device__ float weight(int row) const { return row < a.n_tok * a.k ? a.topk_w[a.gather[row]] : 1.0f; }
 };
 
-template <int GS>
+template <class F>
 struct DownBuf {
     uint4 w[kPipeGroup];
-    scale_rec_t<GS> s[kPipeGroup];
+    typename F::Rec s[kPipeGroup];
 };
 
-template <int GS>
-__device__ __forceinline__ void down_load(DownBuf<GS> &b, rsrc_t r, uint32_t vq, uint32_t vs, uint32_t sq, uint32_t ss,
+template <class F>
+__device__ __forceinline__ void down_load(DownBuf<F> &b, rsrc_t r, uint32_t vq, uint32_t vs, uint32_t sq, uint32_t ss,
                                           int first, int C) {
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + g, C - 1));
         b.w[g] = bload<uint4>(r, vq, sq + c * kChunkBytes);
-        b.s[g] = bload<scale_rec_t<GS>>(r, vs, ss + c * scale_chunk_bytes<GS>());
+        b.s[g] = bload<typename F::Rec>(r, vs, ss + c * F::kScaleChunkBytes);
     }
 }
 
-template <int MAXM, int GS>
-__device__ __forceinline__ void down_math(const DownBuf<GS> &b, const uint8_t *hs, const float *cs, int I,
-                                          int first, int count, int kq, int mc, uint32_t M0,
+template <int MAXM, class F>
+__device__ __forceinline__ void down_math(const DownBuf<F> &b, const uint8_t *hs, const float *cs, int I,
+                                          int first, int count, int row, int kq, int mc, uint32_t M0,
                                           uint32_t M1, uint32_t G, float *acc) {
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
@@ -354,15 +431,15 @@ __device__ __forceinline__ void down_math(const DownBuf<GS> &b, const uint8_t *h
         const int c = first + g;
         const uint32_t ws[4] = {b.w[g].x, b.w[g].y, b.w[g].z, b.w[g].w};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float sf = slice_scale<GS>(b.s[g], s);
-            const int k0 = c * kChunkK + 32 * s + 8 * kq;
+        for (int s = 0; s < F::kSlices; ++s) {
+            const float sf = F::scale(b.s[g], s, row);
+            const int k0 = c * F::kCols + 32 * s + 8 * kq;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 if (m < mc) {
                     const uint4 hv = *reinterpret_cast<const uint4 *>(hs + (static_cast<size_t>(m) * I + k0) * 2);
                     const float c8 = cs[m * (I / 8) + (k0 >> 3)];
-                    acc[m] = __builtin_fmaf(sf, dot8(ws[s], hv, c8, M0, M1, G), acc[m]);
+                    acc[m] = __builtin_fmaf(sf, F::dot(ws, s, hv, c8, M0, M1, G), acc[m]);
                 }
             }
         }
@@ -376,13 +453,13 @@ __device__ __forceinline__ void down_math(const DownBuf<GS> &b, const uint8_t *h
 // routed row, 1 for a shared row).  With COHERENT, ys is written
 // device-coherently (a consumer in the same launch reads it); before_h()
 // runs, by all threads, after the first weight loads are issued and before h
-// is read (a wait for h's producers).  All 256 threads must call it.  GS is
-// the scale group size.
-template <int GS, int MAXM, bool COHERENT = false, class Rows, class BeforeH>
+// is read (a wait for h's producers).  All 256 threads must call it.  F is
+// the weight format (WFmt).
+template <class F, int MAXM, bool COHERENT = false, class Rows, class BeforeH>
 __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int pg,
                                 uint8_t *lds, uint32_t lds_addr, const BeforeH &before_h) {
     const int H = a.hidden, I = a.inter;
-    const int C = I / kChunkK;
+    const int C = I / F::kCols;
     const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
     const int row = lane & 15, kq = lane >> 4;
     const int p = 2 * pg + (wave & 1), half = wave >> 1;
@@ -390,20 +467,20 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
     const int c_end = half == 0 ? (C + 1) / 2 : C;
     const int nper = c_end - c_begin;
     const rsrc_t rs = make_rsrc(blob, static_cast<uint32_t>(a.lay.total));
-    const uint32_t vq = static_cast<uint32_t>(lane) * 16, vs = static_cast<uint32_t>(row) * scale_row_bytes<GS>();
+    const uint32_t vq = static_cast<uint32_t>(lane) * 16, vs = F::rec_offset(row);
     const uint32_t sq = static_cast<uint32_t>(a.lay.down_q + static_cast<size_t>(p) * C * kChunkBytes);
-    const uint32_t ss = static_cast<uint32_t>(a.lay.down_s + static_cast<size_t>(p) * C * scale_chunk_bytes<GS>());
+    const uint32_t ss = static_cast<uint32_t>(a.lay.down_s + static_cast<size_t>(p) * C * F::kScaleChunkBytes);
     uint8_t *hs = lds;
     float *cs = reinterpret_cast<float *>(lds + static_cast<size_t>(MAXM) * I * 2);
     float *red = cs + MAXM * (I / 8);
-    const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+    const uint32_t M0 = vconst(F::kMask0), M1 = vconst(F::kMask1), G = vconst(0x64006400u);
 
     for (int mb = 0; mb < M; mb += MAXM) {
         const int mc = min(MAXM, M - mb);
         float acc[MAXM];
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
-        DownBuf<GS> A, B;
+        DownBuf<F> A, B;
         bool b_issued = false;
         if (mb == 0) before_h();
         __syncthreads();                        // the previous row block is done with hs
@@ -433,7 +510,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
                 float v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
-                stage8(v, dst, cs + m * (I / 8) + q);
+                F::stage(v, dst, cs + m * (I / 8) + q);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -448,18 +525,18 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
                 float v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
-                stage8(v, hs + (static_cast<size_t>(m) * I + 8 * q) * 2, cs + m * (I / 8) + q);
+                F::stage(v, hs + (static_cast<size_t>(m) * I + 8 * q) * 2, cs + m * (I / 8) + q);
             }
             __syncthreads();
         }
         for (int i = 0; i < nper; i += 2 * kPipeGroup) {
             if (i + kPipeGroup < nper && (i > 0 || !b_issued))
                 down_load(B, rs, vq, vs, sq, ss, c_begin + i + kPipeGroup, C);
-            down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), kq, mc, M0, M1, G, acc);
+            down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), row, kq, mc, M0, M1, G, acc);
             if (i + 2 * kPipeGroup < nper) down_load(A, rs, vq, vs, sq, ss, c_begin + i + 2 * kPipeGroup, C);
             if (i + kPipeGroup < nper)
                 down_math<MAXM>(B, hs, cs, I, c_begin + i + kPipeGroup, min(kPipeGroup, nper - i - kPipeGroup),
-                                kq, mc, M0, M1, G, acc);
+                                row, kq, mc, M0, M1, G, acc);
         }
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {

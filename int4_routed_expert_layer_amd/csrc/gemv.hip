@@ -11,7 +11,7 @@
 namespace coli {
 namespace {
 
-template <int GS, int MAXM>
+template <class F, int MAXM>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int P = a.inter / kPanel;
@@ -21,10 +21,10 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin
     if (a.skip_shared && e == a.n_experts) return;
     const uint8_t *blob = a.table[e];
     if (!blob || M <= 0) return;
-    dev::gateup_panel<GS, MAXM>(a, dev::PlainRows{a}, blob, r0, M, p, lds, dev::lds_address(lds));
+    dev::gateup_panel<F, MAXM>(a, dev::PlainRows{a}, blob, r0, M, p, lds, dev::lds_address(lds));
 }
 
-template <int GS, int MAXM, bool FUSED_COMBINE>
+template <class F, int MAXM, bool FUSED_COMBINE>
 __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *counters) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int PG = a.hidden / (2 * kPanel);
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
     if (!dev::resolve(a, u, e, r0, M)) return;
     const uint8_t *blob = a.table[e];
     if (blob && M > 0)
-        dev::down_panelgroup<GS, MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::lds_address(lds),
+        dev::down_panelgroup<F, MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::lds_address(lds),
                                                   dev::NoWait{});
     if (FUSED_COMBINE) {
         const int units = *a.n_union + (a.has_shared ? 1 : 0);
@@ -52,23 +52,23 @@ int units_bound(const FwdArgs &a) {
 
 int pick_maxm(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1); }
 
-template <int GS>
+template <class F>
 void launch_gateup_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStream_t s, int u_begin) {
-    if (maxm == 4) launch(gemv_gateup_kernel<GS, 4>, grid, 256, lds, s, a, u_begin);
-    else if (maxm == 2) launch(gemv_gateup_kernel<GS, 2>, grid, 256, lds, s, a, u_begin);
-    else launch(gemv_gateup_kernel<GS, 1>, grid, 256, lds, s, a, u_begin);
+    if (maxm == 4) launch(gemv_gateup_kernel<F, 4>, grid, 256, lds, s, a, u_begin);
+    else if (maxm == 2) launch(gemv_gateup_kernel<F, 2>, grid, 256, lds, s, a, u_begin);
+    else launch(gemv_gateup_kernel<F, 1>, grid, 256, lds, s, a, u_begin);
 }
 
-template <int GS>
+template <class F>
 void launch_down_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStream_t s, int32_t *combine_counters) {
     if (combine_counters) {
-        if (maxm == 4) launch(gemv_down_kernel<GS, 4, true>, grid, 256, lds, s, a, combine_counters);
-        else if (maxm == 2) launch(gemv_down_kernel<GS, 2, true>, grid, 256, lds, s, a, combine_counters);
-        else launch(gemv_down_kernel<GS, 1, true>, grid, 256, lds, s, a, combine_counters);
+        if (maxm == 4) launch(gemv_down_kernel<F, 4, true>, grid, 256, lds, s, a, combine_counters);
+        else if (maxm == 2) launch(gemv_down_kernel<F, 2, true>, grid, 256, lds, s, a, combine_counters);
+        else launch(gemv_down_kernel<F, 1, true>, grid, 256, lds, s, a, combine_counters);
     } else {
-        if (maxm == 4) launch(gemv_down_kernel<GS, 4, false>, grid, 256, lds, s, a, nullptr);
-        else if (maxm == 2) launch(gemv_down_kernel<GS, 2, false>, grid, 256, lds, s, a, nullptr);
-        else launch(gemv_down_kernel<GS, 1, false>, grid, 256, lds, s, a, nullptr);
+        if (maxm == 4) launch(gemv_down_kernel<F, 4, false>, grid, 256, lds, s, a, nullptr);
+        else if (maxm == 2) launch(gemv_down_kernel<F, 2, false>, grid, 256, lds, s, a, nullptr);
+        else launch(gemv_down_kernel<F, 1, false>, grid, 256, lds, s, a, nullptr);
     }
 }
 
@@ -82,8 +82,8 @@ hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, i
     const int units = u_count >= 0 ? u_count : units_bound(a) - u_begin;
     if (units <= 0) return hipSuccess;
     const int grid = units * (a.inter / kPanel);
-    if (a.lay.group == 64) launch_gateup_as<64>(a, maxm, grid, lds, s, u_begin);
-    else launch_gateup_as<32>(a, maxm, grid, lds, s, u_begin);
+    dev::dispatch_format(a.lay.group, a.lay.bits,
+                         [&](auto f) { launch_gateup_as<decltype(f)>(a, maxm, grid, lds, s, u_begin); });
     return hipGetLastError();
 }
 
@@ -94,8 +94,8 @@ hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s, int
     if (combine_counters) lds = sizeof(float) * dev::combine_lds_floats(lds, a.k, a.has_shared);
     if (lds > max_lds) return hipErrorInvalidValue;
     const int grid = units_bound(a) * (a.hidden / (2 * kPanel));
-    if (a.lay.group == 64) launch_down_as<64>(a, maxm, grid, lds, s, combine_counters);
-    else launch_down_as<32>(a, maxm, grid, lds, s, combine_counters);
+    dev::dispatch_format(a.lay.group, a.lay.bits,
+                         [&](auto f) { launch_down_as<decltype(f)>(a, maxm, grid, lds, s, combine_counters); });
     return hipGetLastError();
 }
 

@@ -22,6 +22,13 @@
 //   64 bytes holding groups 2c, 2c+1.  Dword s of a lane's weight slot
 //   (columns 32s + ...) takes group s (G = 32) or s / 2 (G = 64) of the
 //   chunk.
+//   Int8 experts (8 bits per weight): the same 1 KB chunks hold 16 rows x 64
+//   columns, chunk (p, c) at (p * K/64 + c) * 1024; dword s of lane L holds
+//   row 16p + (L & 15), columns k0 = 64c + 32(s >> 1) + 8(L >> 4) + 4(s & 1)
+//   .. k0+3, stored as u = q + 128 in the byte order k0, k0+2, k0+1, k0+3, so
+//   (w & 0x00FF00FF) | 0x64006400 makes the fp16 pair (1024 + u) of columns
+//   k0, k0+1 and the same on w >> 8 that of k0+2, k0+3.  Scales: [16 rows]
+//   [64/G] fp16 per chunk.  Int8 experts run on the GEMV kernels only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,8 +45,10 @@ constexpr int kPanel = 16;          // matrix rows per chunk
 constexpr int kChunkBytes = 1024;
 
 // Reduction elements per fp16 scale: 32, or 64 (the container of the README's
-// "Scarica il modello" section).
+// "Scarica il modello" section); bits per weight: 4, or 8 (the int8 the same
+// section requires for the MTP head).
 constexpr bool group_supported(int g) { return g == 32 || g == 64; }
+constexpr bool bits_supported(int b) { return b == 4 || b == 8; }
 // Bytes of one chunk's scales, and of one row's share of them.
 template <int G>
 constexpr int scale_chunk_bytes() { return kPanel * (kChunkK / G) * 2; }
@@ -51,9 +60,10 @@ constexpr int kChunkRows = 160;     // rows per grouped work chunk: five 32-row 
 
 struct BlobLayout {
     size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
-    int group;
+    int group;   // reduction elements per fp16 scale: 32 or 64
+    int bits;    // bits per weight: 4 or 8
 };
-BlobLayout blob_layout(int hidden, int inter, int group);
+BlobLayout blob_layout(int hidden, int inter, int group, int bits);
 
 // One grouped-GEMM work chunk: up to kChunkRows rows of one expert.
 // expert == n_experts means the shared expert.  row0 indexes the rows of the

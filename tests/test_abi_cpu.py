@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lib.coli_abi_version() == 2
+    assert B.lib.coli_abi_version() == 3
     for st, name in enumerate(["COLI_OK", "COLI_E_INVALID", "COLI_E_NOMEM", "COLI_E_DEVICE",
                                "COLI_E_STATE", "COLI_E_UNSUPPORTED"]):
         assert B.status_str(st) == name
@@ -42,8 +42,11 @@ def test_abi_version_and_status_strings():
 
 def test_blob_bytes_matches_layout():
     for g in (32, 64):
-        for h, i in ((6144, 2048), (256, 128), (512, 256), (384, 640)):
-            assert B.blob_bytes(h, i, g) == configs.blob_bytes(h, i, g)
+        for bits in (4, 8):
+            for h, i in ((6144, 2048), (256, 128), (512, 256), (384, 640)):
+                assert B.blob_bytes(h, i, g, bits) == configs.blob_bytes(h, i, g, bits)
+    assert B.blob_bytes(6144, 2048, 64, 8) == 3 * 6144 * 2048 + 3 * 6144 * 2048 // 64 * 2
+    assert B.blob_bytes(6144, 2048, 32, 6) == 0
     assert B.blob_bytes(6144, 2048) == 21233664
     assert B.blob_bytes(6144, 2048, 64) == 20054016
     assert B.blob_bytes(0, 128) == 0 and B.blob_bytes(100, 128) == 0
@@ -52,7 +55,8 @@ def test_blob_bytes_matches_layout():
 
 
 def create(**kw):
-    d = dict(hidden=256, inter=128, n_experts=16, top_k=4, has_shared=0, max_tokens=8, act=0, group=32)
+    d = dict(hidden=256, inter=128, n_experts=16, top_k=4, has_shared=0, max_tokens=8, act=0, group=32,
+             weight_bits=4)
     d.update(kw)
     h = C.c_void_p()
     st = B.lib.coli_layer_create(C.byref(B.Dims(**d)), 0, C.byref(h))
@@ -68,6 +72,7 @@ def create(**kw):
     (dict(act=7), B.E_INVALID),
     (dict(group=0), B.E_INVALID),
     (dict(group=128), B.E_INVALID),
+    (dict(weight_bits=2), B.E_INVALID),
     (dict(hidden=192), B.E_UNSUPPORTED),
     (dict(inter=96), B.E_UNSUPPORTED),
     (dict(n_experts=1024, has_shared=1), B.E_UNSUPPORTED),
@@ -101,8 +106,34 @@ def test_null_layer_calls_are_invalid():
     assert L.coli_layer_destroy(None) == B.OK
 
 
-def documented_layout(blob, H, I, group=32):
+def documented_layout_i8(blob, H, I, group):
+    """The int8 device layout described in coli_moe.h, written with numpy."""
+    sec = configs.blob_sections(H, I, group, 8)
+    per = 64 // group
+    out = np.zeros_like(blob)
+    for name, rows, K in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        qo, qs = sec[name + "_q"]
+        so, ss = sec[name + "_s"]
+        u = blob[qo:qo + qs].reshape(rows, K) ^ 0x80             # q + 128
+        P, Cn = rows // 16, K // 64
+        L = np.arange(64)
+        s = np.arange(4)
+        order = np.array([0, 2, 1, 3])                         # byte b holds column k0 + order[b]
+        r = np.arange(P)[:, None, None, None, None] * 16 + (L % 16)[None, None, :, None, None]
+        k = (np.arange(Cn)[None, :, None, None, None] * 64 + 32 * (s // 2)[None, None, None, :, None]
+             + 8 * (L // 16)[None, None, :, None, None] + 4 * (s % 2)[None, None, None, :, None]
+             + order[None, None, None, None, :])
+        out[qo:qo + qs] = u[r, k].astype(np.uint8).reshape(-1)      # [P, C, lane, dword, byte]
+        sc = blob[so:so + ss].view(np.uint16).reshape(rows, K // group)
+        tiles = sc.reshape(P, 16, Cn, per).transpose(0, 2, 1, 3)
+        out[so:so + ss] = np.ascontiguousarray(tiles).reshape(-1).view(np.uint8)
+    return out
+
+
+def documented_layout(blob, H, I, group=32, bits=4):
     """The device layout described in coli_moe.h, written with numpy."""
+    if bits == 8:
+        return documented_layout_i8(blob, H, I, group)
     sec = configs.blob_sections(H, I, group)
     per = 128 // group                                      # scales per row of a tile
     out = np.zeros_like(blob)
@@ -131,17 +162,18 @@ def documented_layout(blob, H, I, group=32):
     return out
 
 
-@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("group,bits", [(32, 4), (64, 4), (32, 8), (64, 8)])
 @pytest.mark.parametrize("spec", [configs.TINY, configs.TINY.with_(hidden=512, inter=384)])
-def test_repack_writes_the_documented_layout(spec, group):
-    spec = spec.with_(group=group)
+def test_repack_writes_the_documented_layout(spec, group, bits):
+    spec = spec.with_(group=group, bits=bits)
     blob = inputs.expert_blob(spec, 0, 2)
-    got = B.repack(blob, spec.hidden, spec.inter, group)
-    np.testing.assert_array_equal(got, documented_layout(blob, spec.hidden, spec.inter, group))
+    got = B.repack(blob, spec.hidden, spec.inter, group, bits)
+    np.testing.assert_array_equal(got, documented_layout(blob, spec.hidden, spec.inter, group, bits))
 
 
 def test_repack_rejects_bad_sizes():
     buf = np.zeros(1024, np.uint8)
-    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 96, 128, 32) == B.E_INVALID
-    assert B.lib.coli_expert_repack(None, buf.ctypes.data, 128, 128, 32) == B.E_INVALID
-    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 128, 128, 48) == B.E_INVALID
+    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 96, 128, 32, 4) == B.E_INVALID
+    assert B.lib.coli_expert_repack(None, buf.ctypes.data, 128, 128, 32, 4) == B.E_INVALID
+    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 128, 128, 48, 4) == B.E_INVALID
+    assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 128, 128, 32, 16) == B.E_INVALID
