@@ -12,7 +12,7 @@
  *   coli_moe_union    Union: deduplicate the selected experts across the
  *                     batch ("batch-union", README "Mai aspettare il disco due
  *                     volte"), so each unique expert is read once.
- *   coli_moe_forward  the int4 SwiGLU expert FFNs over the union, plus the
+ *   coli_moe_forward  the int4 (or int8) SwiGLU expert FFNs over the union, plus the
  *                     always-on shared expert, and the routing-weighted
  *                     combine.
  *   coli_expert_place Place: keep an expert in VRAM or in pinned host memory
@@ -149,7 +149,8 @@ coli_status coli_router_set(coli_layer *layer, const float *w_host,
                             const float *bias_host);
 
 /* Place expert `expert` (0..E-1, or COLI_SHARED) from a host blob in the
- * layout of coli_expert_blob_bytes.  The library repacks it once into its
+ * layout of coli_expert_blob_bytes for the layer's group and weight_bits
+ * (blob_bytes must equal that size, else COLI_E_INVALID).  The library repacks it once into its
  * device layout and keeps it in VRAM (COLI_TIER_VRAM) or in pinned host
  * memory (COLI_TIER_HOST, copied to a device staging slot when a forward
  * call needs it).  Re-placing an expert replaces its data and tier.  The
