@@ -127,14 +127,16 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
         L.set_timing(True)
     unions = []
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(wl.steps + 1)]   # one per step boundary
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * max(0.02, 1e-4 * wl.steps)))   # ~20+ ms of GPU clock cycles
-    ev0.record()
     for s in range(wl.steps):
+        evs[s].record()
         bf = step(s)
-    ev1.record()
+    evs[-1].record()
     torch.cuda.synchronize()
-    eager_ms = ev0.elapsed_time(ev1) / wl.steps
+    eager_ms = evs[0].elapsed_time(evs[-1]) / wl.steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(wl.steps)]
     kt = {}
     for L in layers:
         L.set_timing(False)
@@ -149,7 +151,9 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
     torch.cuda.synchronize()
 
     # Kernel time per step (a kind may launch more than once per step).
-    res = dict(eager_ms_per_step=eager_ms, kernel_ms={k_: v[0] / wl.steps for k_, v in kt.items() if v[1]},
+    res = dict(eager_ms_per_step=eager_ms, eager_ms_p50=float(np.median(per_step)),
+               eager_ms_p90=float(np.percentile(per_step, 90)),
+               kernel_ms={k_: v[0] / wl.steps for k_, v in kt.items() if v[1]},
                kernel_launches={k_: v[1] / wl.steps for k_, v in kt.items() if v[1]},
                union_mean=float(np.mean(unions)), union_min=int(np.min(unions)),
                union_max=int(np.max(unions)))
@@ -476,7 +480,8 @@ def main():
         ms = r.get("graph_ms_per_step", r["eager_ms_per_step"])
         nb = algorithmic_bytes(spec, r["union_mean"], spec.n_tok)
         entry = dict(tokens_per_s=spec.n_tok / (ms / 1e3), ms_per_step=ms,
-                     eager_ms_per_step=r["eager_ms_per_step"],
+                     eager_ms_per_step=r["eager_ms_per_step"], eager_ms_p50=r["eager_ms_p50"],
+                     eager_ms_p90=r["eager_ms_p90"],
                      union_mean=r["union_mean"], union_min=r["union_min"], union_max=r["union_max"],
                      step_GBs=nb["total"] / (ms / 1e3) / 1e9,
                      step_frac_hbm=nb["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
