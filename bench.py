@@ -185,6 +185,40 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
     return res
 
 
+def hbm_reference(torch, reps=5):
+    """Streaming rates of plain library kernels on this GPU, as a reference for
+    the expert kernels' bandwidth: torch's sum over 2 GiB of fp32 (reads only)
+    and a 1 GiB device-to-device copy (read + write bytes), best of `reps`.
+    Both sizes are far above the 256 MB last-level cache."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    src = torch.ones(512 << 20, dtype=torch.float32, device="cuda:0")
+    out = {}
+    best = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        src.sum()
+        ev1.record()
+        torch.cuda.synchronize()
+        best = max(best, src.numel() * 4 / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    out["sum_read_GBs"] = best
+    del src
+    a = torch.ones(256 << 20, dtype=torch.float32, device="cuda:0")
+    bdst = torch.empty_like(a)
+    best = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        bdst.copy_(a)
+        ev1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * a.numel() * 4 / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    out["copy_read_write_GBs"] = best
+    del a, bdst
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_tiered(B, torch, blobs, shared, n_layers=2, calls=12, warmup=2, cache_slots=48):
     """Host-tier streaming (the a7 step): per layer, a seeded 60% of the
     experts sit in VRAM and the rest in pinned host memory; each call routes
@@ -473,6 +507,9 @@ def main():
         del layers_i
         torch.cuda.empty_cache()
 
+    log("timing the HBM reference kernels")
+    hbm_ref = hbm_reference(torch)
+
     # ---- report
     out_also = {}
     for name, r in results.items():
@@ -498,6 +535,11 @@ def main():
         out_also[name] = entry
     if tiered is not None:
         out_also["tiered_b16"] = tiered
+    out_also["hbm_reference"] = hbm_ref
+    if "decode_b1" in out_also and out_also["decode_b1"].get("gateup_GBs"):
+        g = out_also["decode_b1"]["gateup_GBs"]
+        out_also["decode_b1"]["gateup_vs_sum_read"] = g / hbm_ref["sum_read_GBs"]
+        out_also["decode_b1"]["gateup_vs_copy"] = g / hbm_ref["copy_read_write_GBs"]
 
     kernel_names = [n for n in ("decode_b1", "decode_b4", "decode_b64", "prefill_b4096", "decode_b1_g64",
                                 "prefill_b4096_g64", "decode_b1_i8") if n in out_also]
