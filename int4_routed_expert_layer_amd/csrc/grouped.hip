@@ -484,6 +484,7 @@ hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
+    if (a.lay.bits != 4) return hipErrorInvalidValue;      // the MFMA fragments are int4 only
     const unsigned grid = grid_for(max_chunks * (a.inter / 128), 2 * n_cu);
     if (a.lay.group == 64) launch(grouped_kernel<true, 64>, grid, 256, 0, s, a);
     else launch(grouped_kernel<true, 32>, grid, 256, 0, s, a);
@@ -491,6 +492,7 @@ hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu, hip
 }
 
 hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
+    if (a.lay.bits != 4) return hipErrorInvalidValue;
     const unsigned grid = grid_for(max_chunks * ((a.hidden + 255) / 256), 2 * n_cu);
     if (a.lay.group == 64) launch(grouped_kernel<false, 64>, grid, 256, 0, s, a);
     else launch(grouped_kernel<false, 32>, grid, 256, 0, s, a);
