@@ -1,6 +1,6 @@
 /*
  * coli_moe.h -- C ABI of the int4 routed-expert MoE layer for AMD MI355X
- * (gfx950).  ABI version 1.
+ * (gfx950).  ABI version 4 (COLI_ABI_VERSION).
  *
  * One call sequence runs one Mixture-of-Experts layer over a batch of tokens,
  * following the per-token path of the Colibri pages (getting-started page,
@@ -43,6 +43,13 @@
  * blobs keep the int4 blob's sections and scales with one byte per weight.
  * Int8 layers run on the GEMV path for every batch size.
  *
+ * Accepted values: activations x must be finite with |x| < 65520 (they are
+ * rounded to fp16 on the device), and each SwiGLU value h must round to a
+ * finite fp16.  A value outside that range is not an error return (the
+ * device cannot report it before the call returns): it sets a bit in the
+ * layer's device error flags (coli_layer_device_errors) and the affected
+ * outputs are inf or NaN.
+ *
  * Conventions for every entry point:
  *  - Return codes only; nothing aborts or throws across the ABI.  On error
  *    the layer stays usable and coli_last_error() holds a message.
@@ -65,7 +72,7 @@
 extern "C" {
 #endif
 
-#define COLI_ABI_VERSION 3
+#define COLI_ABI_VERSION 4
 
 typedef enum {
     COLI_OK = 0,
@@ -144,7 +151,9 @@ coli_status coli_layer_destroy(coli_layer *layer);
 
 /* Copy the router weight W_r (host pointer, fp32 [H x E], reduction index
  * outer: w_host[k*E + e]) and optional bias (host pointer, fp32 [E], or NULL
- * for zero) into the layer.  Synchronous. */
+ * for zero) into the layer.  Synchronous: it first waits for all work on the
+ * layer's device (every stream), so calls already queued keep the router
+ * they were issued with. */
 coli_status coli_router_set(coli_layer *layer, const float *w_host,
                             const float *bias_host);
 
@@ -155,7 +164,10 @@ coli_status coli_router_set(coli_layer *layer, const float *w_host,
  * memory (COLI_TIER_HOST, copied to a device staging slot when a forward
  * call needs it).  Re-placing an expert replaces its data and tier.  The
  * shared expert must be VRAM-resident.  blob_host may be freed on return.
- * Synchronous. */
+ * Synchronous: it first waits for all work on the layer's device (every
+ * stream, including copies started by coli_layer_prefetch_union), so calls
+ * already queued read the expert they were issued with; the new data is
+ * seen by calls made after it returns. */
 coli_status coli_expert_place(coli_layer *layer, int32_t expert,
                               const void *blob_host, size_t blob_bytes,
                               coli_tier tier);
@@ -240,8 +252,34 @@ coli_status coli_layer_set_stream_cache(coli_layer *layer, int32_t n_slots);
  * stream cache (host pointer). */
 coli_status coli_layer_stream_hits(const coli_layer *layer, int32_t *hits);
 
-/* Read and clear the device error flags (synchronises the device):
- * bit 0 = an out-of-range expert id reached coli_moe_union. */
+/* Lookahead prefetch into the stream cache: the README ("Mai aspettare il
+ * disco due volte") runs the next layer's router ahead of time and fetches
+ * the experts it predicts while the current layer computes; the
+ * getting-started page's Overlap step overlaps such transfers with compute.
+ * Given a union (device pointers n_union [1] and union_ids [E], as
+ * coli_moe_union writes them, e.g. for this layer's next batch computed
+ * early), this call reads it back (synchronising `stream`), then starts one
+ * host-to-device copy per host-tier expert of the union that is not cached
+ * yet into a stream-cache slot, on the layer's side stream, and returns
+ * without waiting for them.  Slots are taken empty first, then least
+ * recently used; a slot filled by this call or whose earlier prefetch copy
+ * is still in flight is never taken, so when the slots run out the rest of
+ * the union is skipped.  A later forward call that finds a prefetched expert
+ * waits for that copy on its own stream (not on the host).  Results are
+ * bit-identical with or without prefetch.  *n_started (host pointer, may be
+ * NULL) = copies started.  COLI_E_STATE without a stream cache
+ * (coli_layer_set_stream_cache), COLI_E_INVALID for NULL pointers or a
+ * union id out of range, COLI_E_NOMEM if the slots cannot be allocated. */
+coli_status coli_layer_prefetch_union(coli_layer *layer, const int32_t *n_union,
+                                      const int32_t *union_ids, void *stream,
+                                      int32_t *n_started);
+
+/* Read and clear the device error flags (synchronises the device), set by
+ * the kernels of every call since the last read:
+ *   bit 0 (1) = an out-of-range expert id reached coli_moe_union;
+ *   bit 1 (2) = an activation was not finite or had |x| >= 65520 (outside
+ *               the fp16 range the expert kernels compute in);
+ *   bit 2 (4) = a SwiGLU value h rounded to an infinite or NaN fp16. */
 coli_status coli_layer_device_errors(coli_layer *layer, int32_t *flags);
 
 /* Kernel timing, for tracing and benchmarks.  While enabled, every kernel
@@ -267,6 +305,19 @@ coli_status coli_layer_kernel_times(coli_layer *layer, double *ms_total,
 const char *coli_status_str(coli_status status);
 const char *coli_last_error(const coli_layer *layer);
 int32_t coli_abi_version(void);
+
+/* Allocation cap, for tests and capacity planning: the library holds at
+ * most `bytes` of device and pinned host memory in total, over all layers
+ * of the process (-1, the default, removes the cap).  An allocation that
+ * would pass it fails with COLI_E_NOMEM exactly as a real allocation
+ * failure does (coli_layer_create checks its whole need before touching the
+ * device); the call that failed has no other effect and the layer stays
+ * usable.  The cap applies to allocations made after it is set; memory
+ * already held is not released.  COLI_E_INVALID for bytes < -1. */
+coli_status coli_set_alloc_limit(int64_t bytes);
+
+/* Bytes of device and pinned host memory the library currently holds. */
+int64_t coli_alloc_bytes(void);
 
 #ifdef __cplusplus
 }

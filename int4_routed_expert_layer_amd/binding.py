@@ -42,9 +42,12 @@ SIGNATURES = {
     "coli_layer_stream_stats": (C.c_int, [_p, _p, _p]),
     "coli_layer_set_stream_cache": (C.c_int, [_p, _i32]),
     "coli_layer_stream_hits": (C.c_int, [_p, _p]),
+    "coli_layer_prefetch_union": (C.c_int, [_p, _p, _p, _p, _p]),
     "coli_layer_device_errors": (C.c_int, [_p, _p]),
     "coli_layer_set_timing": (C.c_int, [_p, _i32]),
     "coli_layer_kernel_times": (C.c_int, [_p, _p, _p]),
+    "coli_set_alloc_limit": (C.c_int, [_i64]),
+    "coli_alloc_bytes": (_i64, []),
 }
 KERNEL_KINDS = ["router", "topk", "union", "plan", "gateup", "down", "combine"]
 
@@ -231,6 +234,14 @@ class MoELayer:
     def set_stream_cache(self, n_slots: int):
         _check(lib.coli_layer_set_stream_cache(self.handle, n_slots), self.handle)
 
+    def prefetch_union(self, u) -> int:
+        """Start copies of the host-tier experts of union ``u`` (the dict
+        union() returns) into the stream cache; returns the copies started."""
+        n = C.c_int32()
+        _check(lib.coli_layer_prefetch_union(self.handle, _dptr(u["n_union"]), _dptr(u["union_ids"]),
+                                             _stream(), C.byref(n)), self.handle)
+        return n.value
+
     def stream_hits(self) -> int:
         h = C.c_int32()
         _check(lib.coli_layer_stream_hits(self.handle, C.byref(h)), self.handle)
@@ -256,6 +267,15 @@ class MoELayer:
         f = C.c_int32()
         _check(lib.coli_layer_device_errors(self.handle, C.byref(f)), self.handle)
         return f.value
+
+
+def set_alloc_limit(nbytes: int) -> None:
+    """Cap the device + pinned host bytes the library may hold (-1: none)."""
+    _check(lib.coli_set_alloc_limit(int(nbytes)))
+
+
+def alloc_bytes() -> int:
+    return int(lib.coli_alloc_bytes())
 
 
 def activations_to_device(x: np.ndarray, device=0):

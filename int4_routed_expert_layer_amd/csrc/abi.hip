@@ -9,8 +9,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <optional>
 #include <string>
 #include <thread>
+#include <unordered_map>
 #include <vector>
 
 #include "coli_moe.h"
@@ -174,6 +177,70 @@ struct DeviceGuard {
 
 thread_local std::string g_create_error;
 
+// Every device and pinned-host allocation the library makes goes through
+// these helpers, which keep the bytes held (all layers of the process) and
+// apply the optional cap set by coli_set_alloc_limit: an allocation that
+// would pass the cap fails as hipErrorOutOfMemory before HIP is called.
+struct MemBook {
+    std::mutex mu;
+    std::unordered_map<void *, size_t> live;
+    int64_t used = 0;
+    int64_t limit = -1;   // -1: no cap
+};
+MemBook &mem_book() {
+    static MemBook *b = new MemBook();
+    return *b;
+}
+bool mem_fits(size_t n) {
+    MemBook &b = mem_book();
+    std::lock_guard<std::mutex> g(b.mu);
+    return b.limit < 0 || b.used + static_cast<int64_t>(n) <= b.limit;
+}
+void mem_note(void *p, size_t n) {
+    MemBook &b = mem_book();
+    std::lock_guard<std::mutex> g(b.mu);
+    b.live[p] = n;
+    b.used += static_cast<int64_t>(n);
+}
+void mem_forget(void *p) {
+    MemBook &b = mem_book();
+    std::lock_guard<std::mutex> g(b.mu);
+    auto it = b.live.find(p);
+    if (it == b.live.end()) return;
+    b.used -= static_cast<int64_t>(it->second);
+    b.live.erase(it);
+}
+template <typename T>
+hipError_t dev_alloc(T **p, size_t n) {
+    if (!mem_fits(n)) return hipErrorOutOfMemory;
+    void *q = nullptr;
+    const hipError_t e = hipMalloc(&q, n);
+    if (e != hipSuccess) return e;
+    mem_note(q, n);
+    *p = static_cast<T *>(q);
+    return hipSuccess;
+}
+template <typename T>
+hipError_t host_alloc(T **p, size_t n) {
+    if (!mem_fits(n)) return hipErrorOutOfMemory;
+    void *q = nullptr;
+    const hipError_t e = hipHostMalloc(&q, n, hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    mem_note(q, n);
+    *p = static_cast<T *>(q);
+    return hipSuccess;
+}
+void dev_free(const void *p) {
+    if (!p) return;
+    mem_forget(const_cast<void *>(p));
+    (void)hipFree(const_cast<void *>(p));
+}
+void host_free(const void *p) {
+    if (!p) return;
+    mem_forget(const_cast<void *>(p));
+    (void)hipHostFree(const_cast<void *>(p));
+}
+
 }  // namespace
 }  // namespace coli
 
@@ -231,6 +298,11 @@ struct coli_layer {
     std::vector<int> slot_expert;    // expert held by each slot, -1 none
     std::vector<int64_t> slot_stamp; // last call that used the slot
     std::vector<int> expert_slot;    // [E] slot holding the expert, -1 none
+    // Prefetch (coli_layer_prefetch_union): a slot filled by a prefetch copy
+    // on the side stream is pending until a forward call waits on its
+    // slot_ready event.
+    std::vector<hipEvent_t> slot_ready;
+    std::vector<char> slot_pending;
     int64_t call_no = 0;
 
     // kernel timing
@@ -356,7 +428,38 @@ bool dims_supported(const coli_moe_dims *d, std::string &why) {
         why = "max_tokens * top_k too large";
         return false;
     }
+    // The grouped kernels address activation and h rows with 32-bit element
+    // offsets (row * width + column) over the rows of one call plus the
+    // discard row; buffer descriptors cover one expert blob with a 32-bit
+    // byte count.
+    const int64_t rows = static_cast<int64_t>(d->max_tokens) * (d->top_k + 1) + 1;
+    if (rows * std::max(d->hidden, d->inter) >= (int64_t(1) << 32)) {
+        std::snprintf(buf, sizeof buf, "(max_tokens * (top_k + 1) + 1) * max(hidden, inter) = %lld must be < 2^32",
+                      static_cast<long long>(rows * std::max(d->hidden, d->inter)));
+        why = buf;
+        return false;
+    }
+    if (group_supported(d->group) && bits_supported(d->weight_bits) &&
+        blob_layout(d->hidden, d->inter, d->group, d->weight_bits).total >= (size_t(1) << 32)) {
+        why = "one expert blob must be smaller than 4 GiB";
+        return false;
+    }
     return true;
+}
+
+// Bytes coli_layer_create allocates (device scratch and tables, the router,
+// pinned staging), for the allocation cap's check before any device call.
+size_t create_bytes(const coli_moe_dims *d) {
+    const size_t E = static_cast<size_t>(d->n_experts), H = static_cast<size_t>(d->hidden),
+                 I = static_cast<size_t>(d->inter), T = static_cast<size_t>(d->max_tokens),
+                 k = static_cast<size_t>(d->top_k);
+    const size_t rows = T * k + T;
+    const size_t chunks = static_cast<size_t>(max_work_chunks(d->max_tokens, d->top_k, d->n_experts, d->has_shared));
+    return sizeof(float) * E * H + sizeof(float) * E + sizeof(void *) * (E + 1) + sizeof(float) * T * E +
+           sizeof(_Float16) * (rows + 1) * I + sizeof(_Float16) * T * H + sizeof(float) * (rows + 1) * H +
+           sizeof(ChunkDesc) * chunks + 2 * sizeof(int32_t) + sizeof(int32_t) * (1 + H / 32) +
+           sizeof(int32_t) * kQueueInts + sizeof(int32_t) * (kUnionMaxBlocks * E + 64) + sizeof(int32_t) * T * k +
+           blob_layout(d->hidden, d->inter, d->group, d->weight_bits).total + sizeof(int32_t) * (E + 1);
 }
 
 bool all_routed_resident(const coli_layer *L) {
@@ -400,6 +503,7 @@ FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, 
     a.n_chunks = L->n_chunks;
     a.queues = L->queues;
     a.skip_shared = 0;
+    a.err = L->err;
     return a;
 }
 
@@ -428,26 +532,26 @@ void free_layer(coli_layer *L) {
     if (!L) return;
     (void)hipDeviceSynchronize();
     for (auto &x : L->experts) {
-        if (x.dev) (void)hipFree(x.dev);
-        if (x.host) (void)hipHostFree(x.host);
+        dev_free(x.dev);
+        host_free(x.host);
     }
-    for (auto p : L->slots) (void)hipFree(p);
+    for (auto p : L->slots) dev_free(p);
     for (auto ev : L->slot_free) (void)hipEventDestroy(ev);
+    for (auto ev : L->slot_ready) (void)hipEventDestroy(ev);
     for (auto ev : L->batch_ready) (void)hipEventDestroy(ev);
     for (auto &mk : L->marks) {
         (void)hipEventDestroy(mk.a);
         (void)hipEventDestroy(mk.b);
     }
     for (auto ev : L->ev_pool) (void)hipEventDestroy(ev);
-    for (auto p : L->pin_tables) (void)hipHostFree(const_cast<uint8_t **>(p));
-    for (auto p : L->dev_tables) (void)hipFree(const_cast<uint8_t **>(p));
+    for (auto p : L->pin_tables) host_free(p);
+    for (auto p : L->dev_tables) dev_free(p);
     if (L->side) (void)hipStreamDestroy(L->side);
     void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->xh, L->ys, L->chunks, L->n_chunks, L->err,
                     L->sync_counters, L->queues, L->union_blk, L->union_rank};
-    for (void *p : ptrs)
-        if (p) (void)hipFree(p);
-    if (L->pin_stage) (void)hipHostFree(L->pin_stage);
-    if (L->pin_union) (void)hipHostFree(L->pin_union);
+    for (void *p : ptrs) dev_free(p);
+    host_free(L->pin_stage);
+    host_free(L->pin_union);
     delete L;
 }
 
@@ -457,19 +561,32 @@ coli_status ensure_stream_resources(coli_layer *L, int n_batches) {
     const int n_slots = std::max(kSlotCount, L->cache_slots);
     while (static_cast<int>(L->slots.size()) < n_slots) {
         uint8_t *p = nullptr;
-        HIP_TRY(L, hipMalloc(&p, bytes), "staging slot");
+        HIP_TRY(L, dev_alloc(&p, bytes), "staging slot");
+        hipEvent_t ev = nullptr, rd = nullptr;
+        if (hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming); e != hipSuccess) {
+            dev_free(p);
+            return hip_fail(L, e, "slot event");
+        }
+        if (hipError_t e = hipEventCreateWithFlags(&rd, hipEventDisableTiming); e != hipSuccess) {
+            (void)hipEventDestroy(ev);
+            dev_free(p);
+            return hip_fail(L, e, "slot event");
+        }
         L->slots.push_back(p);
         L->slot_expert.push_back(-1);
         L->slot_stamp.push_back(0);
-        hipEvent_t ev;
-        HIP_TRY(L, hipEventCreateWithFlags(&ev, hipEventDisableTiming), "slot event");
         L->slot_free.push_back(ev);
+        L->slot_ready.push_back(rd);
+        L->slot_pending.push_back(0);
     }
     const size_t tbytes = sizeof(uint8_t *) * (L->d.n_experts + 1);
     while (static_cast<int>(L->dev_tables.size()) < n_batches) {
         void *hp = nullptr, *dp = nullptr;
-        HIP_TRY(L, hipHostMalloc(&hp, tbytes, hipHostMallocDefault), "pinned table");
-        HIP_TRY(L, hipMalloc(&dp, tbytes), "device table");
+        HIP_TRY(L, host_alloc(&hp, tbytes), "pinned table");
+        if (hipError_t e = dev_alloc(&dp, tbytes); e != hipSuccess) {
+            host_free(hp);
+            return hip_fail(L, e, "device table");
+        }
         L->pin_tables.push_back(static_cast<const uint8_t **>(hp));
         L->dev_tables.push_back(static_cast<const uint8_t **>(dp));
         hipEvent_t ev;
@@ -479,11 +596,92 @@ coli_status ensure_stream_resources(coli_layer *L, int n_batches) {
     return COLI_OK;
 }
 
+// Scratch of one fused small-batch call: logits [n_tok x E], h and ys rows
+// (n_tok * k routed + n_tok shared + the discard row), and the arrival
+// counters [1 + H/32] (zero at rest).
+struct FusedScratch {
+    float *logits;
+    _Float16 *h;
+    float *ys;
+    int32_t *counters;
+    int discard_row;
+};
+
+// True when coli_moe_layer takes the fused small-batch path for n_tok.
+bool fused_path(const coli_layer *L, int n_tok) {
+    return n_tok <= kFrontMaxTok && L->d.n_experts <= 256 && all_routed_resident(L) &&
+           choose_path(L, n_tok) == COLI_PATH_GEMV && L->router_set &&
+           (!L->d.has_shared || L->experts[L->d.n_experts].tier == COLI_TIER_VRAM);
+}
+
+// The fused small-batch layer call in three launches: router + top-k + union
+// with the shared expert's gate/up, the routed gate/up, and the down
+// projection that also combines.  `timed` lets the launches carry kernel
+// timestamps (coli_layer_set_timing); without it nothing is created.
+coli_status run_fused(coli_layer *L, const FusedScratch &w, bool timed, const void *x, int n_tok,
+                      int32_t *topk_idx, float *topk_w, int32_t *n_union, int32_t *union_ids, int32_t *counts,
+                      int32_t *offsets, int32_t *gather, float *y, hipStream_t s) {
+    FwdArgs a = make_args(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y);
+    a.h = w.h;
+    a.ys = w.ys;
+    a.xh = nullptr;                      // the fp16 copy of x is a grouped-path buffer
+    a.discard_row = w.discard_row;
+    FrontArgs f{};
+    f.wt = L->wt;
+    f.bias = L->bias;
+    f.logits = w.logits;
+    f.topk_idx = topk_idx;
+    f.topk_w = topk_w;
+    f.n_union = n_union;
+    f.union_ids = union_ids;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.gather = gather;
+    f.counter = w.counters;
+    f.next_counters = w.counters + 1;
+    f.n_next = L->d.hidden / 32;
+    coli_layer *Lt = timed ? L : nullptr;
+    hipError_t e;
+    {
+        std::optional<KernelMark> m;
+        if (Lt) m.emplace(Lt, COLI_K_ROUTER, s);
+        if ((e = launch_decode_front(a, f, L->max_lds, s)) != hipSuccess) return hip_fail(L, e, "decode front launch");
+    }
+    {
+        std::optional<KernelMark> m;
+        if (Lt) m.emplace(Lt, COLI_K_GATEUP, s);
+        FwdArgs ar = a;
+        ar.skip_shared = 1;
+        const int routed = std::min(n_tok * L->d.top_k, L->d.n_experts);
+        if ((e = launch_gemv_gateup(ar, L->max_lds, s, 0, routed)) != hipSuccess)
+            return hip_fail(L, e, "gemv gate/up launch");
+    }
+    std::optional<KernelMark> m;
+    if (Lt) m.emplace(Lt, COLI_K_DOWN, s);
+    if ((e = launch_gemv_down(a, L->max_lds, s, w.counters + 1, w.counters)) != hipSuccess)
+        return hip_fail(L, e, "gemv down launch");
+    return COLI_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t coli_abi_version(void) { return COLI_ABI_VERSION; }
+
+coli_status coli_set_alloc_limit(int64_t bytes) {
+    if (bytes < -1) return fail(nullptr, COLI_E_INVALID, "limit %lld: -1 or >= 0", static_cast<long long>(bytes));
+    MemBook &b = mem_book();
+    std::lock_guard<std::mutex> g(b.mu);
+    b.limit = bytes;
+    return COLI_OK;
+}
+
+int64_t coli_alloc_bytes(void) {
+    MemBook &b = mem_book();
+    std::lock_guard<std::mutex> g(b.mu);
+    return b.used;
+}
 
 const char *coli_status_str(coli_status s) {
     switch (s) {
@@ -525,6 +723,8 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     if (!out) return fail(nullptr, COLI_E_INVALID, "out is NULL");
     if (!dims_valid(dims, why)) return fail(nullptr, COLI_E_INVALID, "%s", why.c_str());
     if (!dims_supported(dims, why)) return fail(nullptr, COLI_E_UNSUPPORTED, "%s", why.c_str());
+    if (!mem_fits(create_bytes(dims)))
+        return fail(nullptr, COLI_E_NOMEM, "allocation cap: the layer needs %zu bytes", create_bytes(dims));
     int ndev = 0;
     hipError_t he = hipGetDeviceCount(&ndev);
     if (he != hipSuccess || ndev <= 0)
@@ -567,7 +767,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->union_rank), sizeof(int32_t) * T * dims->top_k, "union ranks"},
     };
     for (auto &a : allocs) {
-        if ((he = hipMalloc(a.p, a.n)) != hipSuccess) {
+        if ((he = dev_alloc(a.p, a.n)) != hipSuccess) {
             coli_status st = he == hipErrorOutOfMemory ? COLI_E_NOMEM : COLI_E_DEVICE;
             fail(nullptr, st, "hipMalloc %s (%zu bytes): %s", a.what, a.n, hipGetErrorString(he));
             free_layer(L);
@@ -580,8 +780,8 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         (he = hipMemset(L->queues, 0, sizeof(int32_t) * kQueueInts)) != hipSuccess ||
         (he = hipMemset(L->union_blk, 0, sizeof(int32_t) * (kUnionMaxBlocks * E + 64))) != hipSuccess ||
         (he = hipMemset(L->bias, 0, sizeof(float) * E)) != hipSuccess ||
-        (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_stage), L->lay.total, hipHostMallocDefault)) != hipSuccess ||
-        (he = hipHostMalloc(reinterpret_cast<void **>(&L->pin_union), sizeof(int32_t) * (E + 1), hipHostMallocDefault)) != hipSuccess ||
+        (he = host_alloc(&L->pin_stage, L->lay.total)) != hipSuccess ||
+        (he = host_alloc(&L->pin_union, sizeof(int32_t) * (E + 1))) != hipSuccess ||
         (he = hipDeviceSynchronize()) != hipSuccess) {
         coli_status st = he == hipErrorOutOfMemory ? COLI_E_NOMEM : COLI_E_DEVICE;
         fail(nullptr, st, "layer setup: %s", hipGetErrorString(he));
@@ -618,6 +818,8 @@ coli_status coli_router_set(coli_layer *L, const float *w_host, const float *bia
     std::vector<float> b(E, 0.0f);
     if (bias_host) std::memcpy(b.data(), bias_host, sizeof(float) * E);
     DeviceGuard guard(L->device);
+    // Work already queued on any stream may still read the old router.
+    HIP_TRY(L, hipDeviceSynchronize(), "sync before the router update");
     HIP_TRY(L, hipMemcpy(L->wt, wt.data(), sizeof(float) * wt.size(), hipMemcpyHostToDevice), "router upload");
     HIP_TRY(L, hipMemcpy(L->bias, b.data(), sizeof(float) * E, hipMemcpyHostToDevice), "bias upload");
     L->router_set = true;
@@ -639,30 +841,35 @@ coli_status coli_expert_place(coli_layer *L, int32_t expert, const void *blob_ho
     const int idx = expert == COLI_SHARED ? L->d.n_experts : expert;
     ExpertSlot &x = L->experts[idx];
     DeviceGuard guard(L->device);
+    // Work already queued on any stream (caller streams, the side stream of
+    // the tiered path, prefetch copies) may still read this expert's blob,
+    // table entry or cached copy: let it finish before anything changes.
+    HIP_TRY(L, hipDeviceSynchronize(), "sync before placement");
     const uint8_t *src = static_cast<const uint8_t *>(blob_host);
     if (tier == COLI_TIER_VRAM) {
         repack_blob(src, L->pin_stage, L->d.hidden, L->d.inter, L->d.group, L->d.weight_bits);
-        if (!x.dev) HIP_TRY(L, hipMalloc(&x.dev, L->lay.total), "expert VRAM");
+        if (!x.dev) HIP_TRY(L, dev_alloc(&x.dev, L->lay.total), "expert VRAM");
         HIP_TRY(L, hipMemcpy(x.dev, L->pin_stage, L->lay.total, hipMemcpyHostToDevice), "expert upload");
         if (x.host) {
-            (void)hipHostFree(x.host);
+            host_free(x.host);
             x.host = nullptr;
         }
         L->table_host[idx] = x.dev;
     } else {
-        if (!x.host) HIP_TRY(L, hipHostMalloc(reinterpret_cast<void **>(&x.host), L->lay.total, hipHostMallocDefault), "expert pinned host");
+        if (!x.host) HIP_TRY(L, host_alloc(&x.host, L->lay.total), "expert pinned host");
         repack_blob(src, x.host, L->d.hidden, L->d.inter, L->d.group, L->d.weight_bits);
         L->table_host[idx] = nullptr;
     }
     x.tier = tier;
     if (idx < L->d.n_experts && L->expert_slot[idx] >= 0) {   // a cached copy is stale now
         L->slot_expert[L->expert_slot[idx]] = -1;
+        L->slot_pending[L->expert_slot[idx]] = 0;
         L->expert_slot[idx] = -1;
     }
     HIP_TRY(L, hipMemcpy(L->table_dev + idx, &L->table_host[idx], sizeof(void *), hipMemcpyHostToDevice), "table update");
     if (tier == COLI_TIER_HOST && x.dev) {
         HIP_TRY(L, hipDeviceSynchronize(), "sync before free");
-        (void)hipFree(x.dev);
+        dev_free(x.dev);
         x.dev = nullptr;
     }
     return COLI_OK;
@@ -772,6 +979,18 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
         }
     }
 
+    // Host-tier experts already in the stream cache form the first batch (no
+    // copy); the others are copied into slots in batches of kBatchExperts,
+    // each batch computed once its copies have landed.  The slots, tables and
+    // events are allocated before any launch, so a failed allocation leaves
+    // no work behind.
+    const bool cache = L->cache_slots > 0;
+    std::vector<int> hits, misses;
+    for (int e : streamed) (cache && L->expert_slot[e] >= 0 ? hits : misses).push_back(e);
+    const int n_hit_batches = hits.empty() ? 0 : 1;
+    const int n_batches = n_hit_batches + (static_cast<int>(misses.size()) + kBatchExperts - 1) / kBatchExperts;
+    if (!streamed.empty() && (st = ensure_stream_resources(L, n_batches)) != COLI_OK) return st;
+
     if (path == COLI_PATH_GROUPED) {
         {
             KernelMark m(L, COLI_K_PLAN, s);
@@ -784,18 +1003,10 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
     if ((st = launch_experts(L, a, path, s)) != COLI_OK) return st;
 
     if (!streamed.empty()) {
-        // Host-tier experts already in the stream cache form the first batch
-        // (no copy); the others are copied into slots in batches of
-        // kBatchExperts, each batch computed once its copies have landed.
         // Every earlier call ended with a stream synchronisation, so only
-        // slots read earlier in this call can still be in use.
-        const bool cache = L->cache_slots > 0;
+        // slots read earlier in this call, or filled by a prefetch, can
+        // still be in use.
         const int64_t call = ++L->call_no;
-        std::vector<int> hits, misses;
-        for (int e : streamed) (cache && L->expert_slot[e] >= 0 ? hits : misses).push_back(e);
-        const int n_hit_batches = hits.empty() ? 0 : 1;
-        const int n_batches = n_hit_batches + (static_cast<int>(misses.size()) + kBatchExperts - 1) / kBatchExperts;
-        if ((st = ensure_stream_resources(L, n_batches)) != COLI_OK) return st;
         const int n_slots = cache ? L->cache_slots : kSlotCount;
         const size_t bytes = L->lay.total;
         const size_t tbytes = sizeof(uint8_t *) * (L->d.n_experts + 1);
@@ -821,6 +1032,10 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
             if (b < n_hit_batches) {
                 for (int e : hits) {
                     const int slot = L->expert_slot[e];
+                    if (L->slot_pending[slot]) {     // filled by a prefetch: after its copy
+                        HIP_TRY(L, hipStreamWaitEvent(s, L->slot_ready[slot], 0), "prefetch wait");
+                        L->slot_pending[slot] = 0;
+                    }
                     pt[e] = L->slots[slot];
                     slot_batch[slot] = b;
                     batch_slots.push_back(slot);
@@ -835,6 +1050,7 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
                         HIP_TRY(L, hipStreamWaitEvent(L->side, L->slot_free[slot], 0), "slot wait");
                     if (L->slot_expert[slot] >= 0) L->expert_slot[L->slot_expert[slot]] = -1;
                     L->slot_expert[slot] = -1;
+                    L->slot_pending[slot] = 0;     // a prefetch copy into it is ordered before this one
                     HIP_TRY(L, hipMemcpyAsync(L->slots[slot], L->experts[e].host, bytes, hipMemcpyHostToDevice,
                                               L->side),
                             "expert H2D");
@@ -879,10 +1095,7 @@ coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t 
     if (n_tok == 0) return COLI_OK;
     if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
         return fail(L, COLI_E_INVALID, "NULL device pointer");
-    const bool fused = n_tok <= kFrontMaxTok && L->d.n_experts <= 256 && all_routed_resident(L) &&
-                       choose_path(L, n_tok) == COLI_PATH_GEMV && L->router_set &&
-                       (!L->d.has_shared || L->experts[L->d.n_experts].tier == COLI_TIER_VRAM);
-    if (!fused) {
+    if (!fused_path(L, n_tok)) {
         if ((st = coli_moe_route(L, x, n_tok, topk_idx, topk_w, stream)) != COLI_OK) return st;
         if ((st = coli_moe_union(L, topk_idx, n_tok, n_union, union_ids, counts, offsets, gather, stream)) != COLI_OK)
             return st;
@@ -890,37 +1103,10 @@ coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t 
                                 stream);
     }
     DeviceGuard guard(L->device);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    FwdArgs a = make_args(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y);
-    FrontArgs f{};
-    f.wt = L->wt;
-    f.bias = L->bias;
-    f.logits = L->logits;
-    f.topk_idx = topk_idx;
-    f.topk_w = topk_w;
-    f.n_union = n_union;
-    f.union_ids = union_ids;
-    f.counts = counts;
-    f.offsets = offsets;
-    f.gather = gather;
-    f.counter = L->sync_counters;
-    hipError_t e;
-    {
-        KernelMark m(L, COLI_K_ROUTER, s);
-        if ((e = launch_decode_front(a, f, L->max_lds, s)) != hipSuccess) return hip_fail(L, e, "decode front launch");
-    }
-    {
-        KernelMark m(L, COLI_K_GATEUP, s);
-        FwdArgs ar = a;
-        ar.skip_shared = 1;
-        const int routed = std::min(n_tok * L->d.top_k, L->d.n_experts);
-        if ((e = launch_gemv_gateup(ar, L->max_lds, s, 0, routed)) != hipSuccess)
-            return hip_fail(L, e, "gemv gate/up launch");
-    }
-    KernelMark m(L, COLI_K_DOWN, s);
-    if ((e = launch_gemv_down(a, L->max_lds, s, L->sync_counters + 1)) != hipSuccess)
-        return hip_fail(L, e, "gemv down launch");
-    return COLI_OK;
+    const FusedScratch w{L->logits, L->h, L->ys, L->sync_counters,
+                         static_cast<int>(L->d.max_tokens) * (L->d.top_k + 1)};
+    return run_fused(L, w, true, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
+                     static_cast<hipStream_t>(stream));
 }
 
 coli_status coli_layer_set_timing(coli_layer *L, int32_t enable) {
@@ -963,20 +1149,26 @@ coli_status coli_layer_set_stream_cache(coli_layer *L, int32_t n_slots) {
     if (n_slots != 0 && (n_slots < kBatchExperts || n_slots > L->d.n_experts))
         return fail(L, COLI_E_INVALID, "n_slots %d: 0 or %d..%d", n_slots, kBatchExperts, L->d.n_experts);
     DeviceGuard guard(L->device);
+    // Prefetch copies may still be in flight into the slots; every tiered
+    // forward call ended with a synchronisation.
+    if (L->side) HIP_TRY(L, hipStreamSynchronize(L->side), "side stream sync");
     L->cache_slots = n_slots;
-    // Slots past the new need are released (every tiered call ended with a
-    // synchronisation, so none is in use).
+    // Slots past the new need are released.
     const size_t keep = static_cast<size_t>(std::max(kSlotCount, n_slots));
     while (L->slots.size() > keep) {
-        (void)hipFree(L->slots.back());
+        dev_free(L->slots.back());
         (void)hipEventDestroy(L->slot_free.back());
+        (void)hipEventDestroy(L->slot_ready.back());
         L->slots.pop_back();
         L->slot_free.pop_back();
+        L->slot_ready.pop_back();
         L->slot_expert.pop_back();
         L->slot_stamp.pop_back();
+        L->slot_pending.pop_back();
     }
     for (auto &x : L->slot_expert) x = -1;
     for (auto &x : L->slot_stamp) x = 0;
+    for (auto &x : L->slot_pending) x = 0;
     for (auto &x : L->expert_slot) x = -1;
     return COLI_OK;
 }
@@ -985,6 +1177,63 @@ coli_status coli_layer_stream_hits(const coli_layer *L, int32_t *hits) {
     if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
     if (!hits) return fail(const_cast<coli_layer *>(L), COLI_E_INVALID, "hits is NULL");
     *hits = L->last_hits;
+    return COLI_OK;
+}
+
+coli_status coli_layer_prefetch_union(coli_layer *L, const int32_t *n_union, const int32_t *union_ids,
+                                      void *stream, int32_t *n_started) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    if (!n_union || !union_ids) return fail(L, COLI_E_INVALID, "NULL device pointer");
+    if (L->cache_slots <= 0) return fail(L, COLI_E_STATE, "prefetch needs the stream cache (coli_layer_set_stream_cache)");
+    DeviceGuard guard(L->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int E = L->d.n_experts;
+    if (n_started) *n_started = 0;
+    coli_status st;
+    if ((st = ensure_stream_resources(L, 0)) != COLI_OK) return st;
+    HIP_TRY(L, hipMemcpyAsync(L->pin_union, n_union, sizeof(int32_t), hipMemcpyDeviceToHost, s), "union readback");
+    HIP_TRY(L, hipMemcpyAsync(L->pin_union + 1, union_ids, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s),
+            "union readback");
+    HIP_TRY(L, hipStreamSynchronize(s), "union readback sync");
+    const int nu = L->pin_union[0];
+    if (nu < 0 || nu > E) return fail(L, COLI_E_INVALID, "n_union %d out of range", nu);
+    for (int u = 0; u < nu; ++u) {
+        const int e = L->pin_union[1 + u];
+        if (e < 0 || e >= E) return fail(L, COLI_E_INVALID, "union id %d out of range", e);
+    }
+    const int n_slots = L->cache_slots;
+    const size_t bytes = L->lay.total;
+    const int64_t stamp = ++L->call_no;
+    int started = 0;
+    for (int u = 0; u < nu; ++u) {
+        const int e = L->pin_union[1 + u];
+        if (L->experts[e].tier != COLI_TIER_HOST || L->expert_slot[e] >= 0) continue;
+        // An empty slot, else the least recently used one; never a slot
+        // filled by this call, nor one whose earlier prefetch copy is still
+        // in flight.  None left: the rest of the union is not prefetched.
+        int best = -1;
+        for (int q = 0; q < n_slots; ++q) {
+            if (L->slot_stamp[q] == stamp) continue;
+            if (L->slot_pending[q]) {
+                if (hipEventQuery(L->slot_ready[q]) != hipSuccess) continue;
+                L->slot_pending[q] = 0;        // landed: no forward call needs to wait for it
+            }
+            if (best < 0 || (L->slot_expert[q] < 0 && L->slot_expert[best] >= 0) ||
+                ((L->slot_expert[q] < 0) == (L->slot_expert[best] < 0) && L->slot_stamp[q] < L->slot_stamp[best]))
+                best = q;
+        }
+        if (best < 0) break;
+        if (L->slot_expert[best] >= 0) L->expert_slot[L->slot_expert[best]] = -1;
+        HIP_TRY(L, hipMemcpyAsync(L->slots[best], L->experts[e].host, bytes, hipMemcpyHostToDevice, L->side),
+                "prefetch H2D");
+        HIP_TRY(L, hipEventRecord(L->slot_ready[best], L->side), "prefetch event");
+        L->slot_expert[best] = e;
+        L->expert_slot[e] = best;
+        L->slot_stamp[best] = stamp;
+        L->slot_pending[best] = 1;
+        ++started;
+    }
+    if (n_started) *n_started = started;
     return COLI_OK;
 }
 

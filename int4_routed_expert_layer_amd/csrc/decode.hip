@@ -225,6 +225,8 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
                                                             a.n_tok, p, lds, dev::lds_address(lds));
         return;
     }
+    if (blockIdx.x == 0 && f.next_counters)
+        for (int i = threadIdx.x; i < f.n_next; i += kFrontThreads) dev::store_coherent(f.next_counters + i, 0);
     const int e = static_cast<int>(blockIdx.x) * 4 + dev::wave_id();   // uniform per wave
     if (e < a.n_experts) wave_router<NT, BF16>(a, f, e);
     if (dev::arrive_last(f.counter, router_blocks)) {

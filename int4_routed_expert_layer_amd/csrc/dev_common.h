@@ -63,6 +63,25 @@ __device__ __forceinline__ float swiglu(float g, float v) {
     return g * __builtin_amdgcn_rcpf(1.0f + e) * v;
 }
 
+// True when v is NaN or rounds to an infinite fp16 (|v| >= 65520, the
+// midpoint between the largest half, 65504, and 2^16).
+__device__ __forceinline__ bool outside_half(float v) { return !(__builtin_fabsf(v) < 65520.0f); }
+
+// True when an fp16 value is inf or NaN (all exponent bits set): the result
+// of rounding a value outside the fp16 range, or of a non-finite input.
+__device__ __forceinline__ bool half_nonfinite(_Float16 h) {
+    return (__builtin_bit_cast(uint16_t, h) & 0x7C00u) == 0x7C00u;
+}
+
+// Sets `bit` in the device error flags when `bad` holds in any active lane
+// of the wave: one atomic from the lowest such lane, and none in the usual
+// case.  Call it where the lanes that matter are active.
+__device__ __forceinline__ void flag_if(bool bad, int32_t *err, int32_t bit) {
+    const uint64_t m = __ballot(bad);
+    if (__builtin_expect(m != 0, 0) && __lane_id() == static_cast<unsigned>(__ffsll(static_cast<unsigned long long>(m)) - 1))
+        __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wave index as a scalar (uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
 

@@ -22,8 +22,9 @@
 // (x' the staged, divided values), computed once per 8 activations, so the
 // dot of one dword is sum (u-8) x = sum q x up to fp32 rounding, and one
 // fused multiply-add applies the fp16 group scale.  Activations enter as
-// fp16 (bf16/fp32 inputs are rounded once when staged; they must lie inside
-// the fp16 range).
+// fp16 (bf16/fp32 inputs are rounded once when staged; a value outside the
+// fp16 range, or not finite, sets a device error flag, as does an h value
+// that rounds to inf).
 //
 // Int8 weights (WFmt<.., 8>) use the same scheme with one byte per column:
 // u = q + 128 sits in the low byte of each fp16 half, the activations are
@@ -53,13 +54,16 @@ __device__ __forceinline__ float dot8(uint32_t w, uint4 xv, float c, uint32_t M0
 }
 
 // Stage 8 activations into LDS as fp16 with the pair-1/3 columns divided by
-// 16, and their dot seed.
-__device__ __forceinline__ void stage8(const float *v, uint8_t *dst_x, float *dst_c) {
+// 16, and their dot seed.  Returns true if a value lies outside the fp16
+// range (or is not finite).
+__device__ __forceinline__ bool stage8(const float *v, uint8_t *dst_x, float *dst_c) {
     _Float16 h[8];
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const bool odd_pair = (i & 2) != 0;          // columns 2,3,6,7
         h[i] = static_cast<_Float16>(odd_pair ? v[i] * 0.0625f : v[i]);
+        bad = bad || outside_half(v[i]);
     }
     float ce = 0.0f, co = 0.0f;
     ce = ce + static_cast<float>(h[0]);
@@ -73,6 +77,7 @@ __device__ __forceinline__ void stage8(const float *v, uint8_t *dst_x, float *ds
     // (1024+u) x - 1032 x = (u-8) x;  (1024+16u) x' - 1152 x' = (u-8) (16 x').
     *dst_c = -1032.0f * ce - 1152.0f * co;
     *reinterpret_cast<uint4 *>(dst_x) = __builtin_bit_cast(uint4, h);
+    return bad;
 }
 
 // LDS bytes of one gate/up panel item / one down panel-group item.
@@ -110,18 +115,22 @@ __device__ __forceinline__ float dot8_i8(uint32_t w0, uint32_t w1, uint4 xv, flo
     return d;
 }
 
-// Stage 8 activations into LDS as plain fp16 with the int8 dot seed.
-__device__ __forceinline__ void stage8_i8(const float *v, uint8_t *dst_x, float *dst_c) {
+// Stage 8 activations into LDS as plain fp16 with the int8 dot seed; true
+// if a value lies outside the fp16 range.
+__device__ __forceinline__ bool stage8_i8(const float *v, uint8_t *dst_x, float *dst_c) {
     _Float16 h[8];
     float sum = 0.0f;
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         h[i] = static_cast<_Float16>(v[i]);
         sum = sum + static_cast<float>(h[i]);
+        bad = bad || outside_half(v[i]);
     }
     // (1024 + q + 128) x - 1152 x = q x.
     *dst_c = -1152.0f * sum;
     *reinterpret_cast<uint4 *>(dst_x) = __builtin_bit_cast(uint4, h);
+    return bad;
 }
 
 // Weight format of the GEMV work items: GS reduction elements per fp16 scale
@@ -166,9 +175,9 @@ struct WFmt {
         if constexpr (WB == 4) return dot8(w[j], xv, c, M0, M1, G);
         else return dot8_i8(w[2 * j], w[2 * j + 1], xv, c, M0, G);
     }
-    __device__ static void stage(const float *v, uint8_t *dst_x, float *dst_c) {
-        if constexpr (WB == 4) stage8(v, dst_x, dst_c);
-        else stage8_i8(v, dst_x, dst_c);
+    __device__ static bool stage(const float *v, uint8_t *dst_x, float *dst_c) {
+        if constexpr (WB == 4) return stage8(v, dst_x, dst_c);
+        else return stage8_i8(v, dst_x, dst_c);
     }
 };
 
@@ -308,6 +317,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * NG) : "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
+            bool bad = false;
             for (int i = tid; i < mc * (H / 8); i += 256) {
                 const int m = i / (H / 8), q = i % (H / 8);
                 uint8_t *dst = xs + (static_cast<size_t>(m) * H + 8 * q) * 2;
@@ -319,14 +329,16 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                     v[2 * j] = bf16_bits_to_f32(w4[j] & 0xFFFFu);
                     v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
                 }
-                F::stage(v, dst, cs + m * (H / 8) + q);
+                bad = F::stage(v, dst, cs + m * (H / 8) + q) || bad;
             }
+            flag_if(bad, a.err, kErrActRange);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         } else {
         gateup_load(A, P, wave, 4, C);          // weights do not depend on x
         __syncthreads();
+        bool bad = false;
         for (int i = tid; i < mc * (H / 8); i += 256) {
             const int m = i / (H / 8), q = i % (H / 8);
             const int t = rows.token(r0 + mb + m);
@@ -345,8 +357,9 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                 v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
                 v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
             }
-            F::stage(v, xs + (static_cast<size_t>(m) * H + 8 * q) * 2, cs + m * (H / 8) + q);
+            bad = F::stage(v, xs + (static_cast<size_t>(m) * H + 8 * q) * 2, cs + m * (H / 8) + q) || bad;
         }
+        flag_if(bad, a.err, kErrActRange);
         __syncthreads();
         }
         // i indexes this wave's chunk list; buffers alternate A, B.
@@ -374,6 +387,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
             }
         }
         __syncthreads();
+        bool hbad = false;
         if (tid < mc * 16) {
             const int m = tid >> 4, r = tid & 15;
             float g = 0.0f, v = 0.0f;
@@ -382,11 +396,13 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                 g = g + red[((w * MAXM + m) * 16 + r) * 2 + 0];
                 v = v + red[((w * MAXM + m) * 16 + r) * 2 + 1];
             }
-            const float hval = swiglu(g, v);
+            const _Float16 hh = static_cast<_Float16>(swiglu(g, v));
+            hbad = half_nonfinite(hh);
             _Float16 *dst = a.h + static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r;
-            if (COHERENT) store_coherent(dst, static_cast<_Float16>(hval));
-            else *dst = static_cast<_Float16>(hval);
+            if (COHERENT) store_coherent(dst, hh);
+            else *dst = hh;
         }
+        flag_if(hbad, a.err, kErrHiddenRange);
     }
 }
 

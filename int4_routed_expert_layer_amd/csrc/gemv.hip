@@ -25,8 +25,11 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin
 }
 
 template <class F, int MAXM, bool FUSED_COMBINE>
-__global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *counters) {
+__global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *counters, int32_t *idle_counter) {
     extern __shared__ __align__(16) uint8_t lds[];
+    // A counter of an earlier launch of this call (idle now) starts the next
+    // call at zero even after calls that overlapped and raced on it.
+    if (idle_counter && blockIdx.x == 0 && threadIdx.x == 0) dev::store_coherent(idle_counter, 0);
     const int PG = a.hidden / (2 * kPanel);
     const int u = blockIdx.x / PG, pg = blockIdx.x % PG;
     int e, r0, M;
@@ -60,15 +63,17 @@ void launch_gateup_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStrea
 }
 
 template <class F>
-void launch_down_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStream_t s, int32_t *combine_counters) {
+void launch_down_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStream_t s, int32_t *combine_counters,
+                    int32_t *idle_counter) {
+    int32_t *none = nullptr;
     if (combine_counters) {
-        if (maxm == 4) launch(gemv_down_kernel<F, 4, true>, grid, 256, lds, s, a, combine_counters);
-        else if (maxm == 2) launch(gemv_down_kernel<F, 2, true>, grid, 256, lds, s, a, combine_counters);
-        else launch(gemv_down_kernel<F, 1, true>, grid, 256, lds, s, a, combine_counters);
+        if (maxm == 4) launch(gemv_down_kernel<F, 4, true>, grid, 256, lds, s, a, combine_counters, idle_counter);
+        else if (maxm == 2) launch(gemv_down_kernel<F, 2, true>, grid, 256, lds, s, a, combine_counters, idle_counter);
+        else launch(gemv_down_kernel<F, 1, true>, grid, 256, lds, s, a, combine_counters, idle_counter);
     } else {
-        if (maxm == 4) launch(gemv_down_kernel<F, 4, false>, grid, 256, lds, s, a, nullptr);
-        else if (maxm == 2) launch(gemv_down_kernel<F, 2, false>, grid, 256, lds, s, a, nullptr);
-        else launch(gemv_down_kernel<F, 1, false>, grid, 256, lds, s, a, nullptr);
+        if (maxm == 4) launch(gemv_down_kernel<F, 4, false>, grid, 256, lds, s, a, none, idle_counter);
+        else if (maxm == 2) launch(gemv_down_kernel<F, 2, false>, grid, 256, lds, s, a, none, idle_counter);
+        else launch(gemv_down_kernel<F, 1, false>, grid, 256, lds, s, a, none, idle_counter);
     }
 }
 
@@ -87,7 +92,8 @@ hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, i
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s, int32_t *combine_counters) {
+hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s, int32_t *combine_counters,
+                            int32_t *idle_counter) {
     int maxm = pick_maxm(a.n_tok);
     while (maxm > 1 && dev::down_lds_bytes(maxm, a.inter) > max_lds) maxm >>= 1;
     size_t lds = dev::down_lds_bytes(maxm, a.inter);
@@ -95,7 +101,7 @@ hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s, int
     if (lds > max_lds) return hipErrorInvalidValue;
     const int grid = units_bound(a) * (a.hidden / (2 * kPanel));
     dev::dispatch_format(a.lay.group, a.lay.bits,
-                         [&](auto f) { launch_down_as<decltype(f)>(a, maxm, grid, lds, s, combine_counters); });
+                         [&](auto f) { launch_down_as<decltype(f)>(a, maxm, grid, lds, s, combine_counters, idle_counter); });
     return hipGetLastError();
 }
 

@@ -254,6 +254,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     // Epilogue.  Lane holds D[m = 8(i / 4) + 4(L / 32) + i % 4][n = L % 32]
     // of each 32x32 tile.  Padding rows (m >= rows) store into the discard
     // row, so no store is predicated.
+    bool hbad = false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         if (GATEUP) {
@@ -262,8 +263,9 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
             for (int i = 0; i < 16; ++i) {
                 const int m = mt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
                 const int r = m < st.rows ? st.row0 + m : a.discard_row;
-                a.h[static_cast<size_t>(r) * I + col] =
-                    static_cast<_Float16>(dev::swiglu(acc[mt][0][i], acc[mt][1][i]));
+                const _Float16 hh = static_cast<_Float16>(dev::swiglu(acc[mt][0][i], acc[mt][1][i]));
+                hbad = hbad || dev::half_nonfinite(hh);
+                a.h[static_cast<size_t>(r) * I + col] = hh;
             }
         } else {
             // The tile's output entries (the discard row for padding) and
@@ -289,6 +291,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
             }
         }
     }
+    if (GATEUP) dev::flag_if(hbad, a.err, kErrHiddenRange);
 }
 
 template <bool GATEUP, int GS>
@@ -424,8 +427,10 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         dev::store_coherent(a.queues + tid * kQueueStride, 0);
 }
 
-// fp16 copy of the activations (the A operand of the gate/up GEMM).
-__global__ __launch_bounds__(256) void to_half_kernel(const void *x, int act_bf16, size_t n8, _Float16 *xh) {
+// fp16 copy of the activations (the A operand of the gate/up GEMM); values
+// outside the fp16 range set a device error flag.
+__global__ __launch_bounds__(256) void to_half_kernel(const void *x, int act_bf16, size_t n8, _Float16 *xh,
+                                                      int32_t *err) {
     const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= n8) return;
     float v[8];
@@ -444,9 +449,14 @@ __global__ __launch_bounds__(256) void to_half_kernel(const void *x, int act_bf1
         v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     }
     half8 h;
+    bool bad = false;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = static_cast<_Float16>(v[j]);
+    for (int j = 0; j < 8; ++j) {
+        h[j] = static_cast<_Float16>(v[j]);
+        bad = bad || dev::outside_half(v[j]);
+    }
     reinterpret_cast<half8 *>(xh)[i] = h;
+    dev::flag_if(bad, err, kErrActRange);
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a) {
@@ -479,7 +489,7 @@ int grid_for(int items, int slots) {
 hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
     const size_t n8 = static_cast<size_t>(a.n_tok) * a.hidden / 8;
     if (n8 == 0) return hipSuccess;
-    launch(to_half_kernel, static_cast<unsigned>((n8 + 255) / 256), 256, 0, s, a.x, a.act_bf16, n8, a.xh);
+    launch(to_half_kernel, static_cast<unsigned>((n8 + 255) / 256), 256, 0, s, a.x, a.act_bf16, n8, a.xh, a.err);
     return hipGetLastError();
 }
 

@@ -97,7 +97,13 @@ struct FwdArgs {
     const int32_t *n_chunks;
     int32_t *queues;                // grouped path: kQueueInts counters, zero at rest
     int skip_shared;                // gate/up: the shared unit was already done
+    int32_t *err;                   // device error flags (kErr* bits), sticky until read
 };
+
+// Device error flags (coli_layer_device_errors).
+constexpr int32_t kErrExpertId = 1;     // an out-of-range expert id reached the union
+constexpr int32_t kErrActRange = 2;     // an activation was non-finite or outside the fp16 range
+constexpr int32_t kErrHiddenRange = 4;  // a SwiGLU value h was non-finite or outside the fp16 range
 
 // Kernel launch used by every launcher.  When the calling thread has armed
 // a pair of events (timing mode), the next launch records the kernel's own
@@ -151,11 +157,13 @@ hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
                        hipStream_t s);
 // gemv.hip.  gate/up covers units [u_begin, u_begin + u_count) (u_count < 0:
 // to the end).  down with non-NULL combine_counters ([H/32] ints, zero at
-// rest) also writes y and needs every unit to be computed in this launch.
+// rest) also writes y and needs every unit to be computed in this launch;
+// idle_counter (may be NULL), a counter of an earlier launch of the same
+// call, is cleared by it (see FrontArgs::next_counters).
 hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, int u_begin = 0,
                               int u_count = -1);
 hipError_t launch_gemv_down(const FwdArgs &a, size_t max_lds, hipStream_t s,
-                            int32_t *combine_counters = nullptr);
+                            int32_t *combine_counters = nullptr, int32_t *idle_counter = nullptr);
 // decode.hip: route + top-k + union of up to kFrontMaxTok tokens and, in the
 // same launch, the shared expert's gate/up.  Needs n_experts <= 256.
 constexpr int kFrontMaxTok = 4;
@@ -167,6 +175,12 @@ struct FrontArgs {
     float *topk_w;            // [n_tok x k]
     int32_t *n_union, *union_ids, *counts, *offsets, *gather;
     int32_t *counter;         // one int, zero at rest
+    // The arrival counters of the fused down launch that follows (n_next
+    // ints): idle while this launch runs, so the first router block clears
+    // them, and a call that follows calls which overlapped (and raced) on
+    // the counters starts from zero again.
+    int32_t *next_counters;
+    int n_next;
 };
 hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_lds, hipStream_t s);
 // grouped.hip

@@ -4,6 +4,7 @@ inputs, and compare (bit-exact routing and union, output within
 2e-3 * max|ref|)."""
 from __future__ import annotations
 
+import os
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
@@ -13,7 +14,12 @@ from int4_routed_expert_layer_amd import inputs
 from oracle import oracle as orc
 
 TOL = 2e-3          # max|y_gpu - y_ref| <= TOL * max|y_ref|
-THREADS = 8
+# Oracle worker threads: the host's cores, at most 16 (the CPU share of a
+# one-GPU machine).
+THREADS = max(1, min(16, os.cpu_count() or 1))
+# Rows per grouped-GEMM work chunk (five 32-row MFMA tiles): experts with
+# more rows are split into several chunks.
+CHUNK_ROWS = 160
 
 
 def log(msg: str) -> None:
@@ -128,3 +134,65 @@ def check_outputs(y_gpu, y_ref, what=""):
     assert np.all(np.isfinite(y_gpu))
     assert err <= TOL * scale, f"{what}: {err / scale:.3e} > {TOL}"
     return err / scale
+
+
+def edge_tokens(ref, k, extra=()):
+    """Tokens whose outputs cover every union expert's grouped work: the
+    tokens on the first and last gather row of each expert and on both sides
+    of every CHUNK_ROWS boundary inside an expert's rows, plus ``extra``.
+    Comparing these checks each expert's first and last MFMA tile of every
+    chunk the grouped path cuts it into."""
+    gather, counts, offsets = ref["gather"], ref["counts"], ref["offsets"]
+    rows = set()
+    for e in np.nonzero(counts)[0]:
+        r0, m = int(offsets[e]), int(counts[e])
+        rows.update((r0, r0 + m - 1))
+        for b in range(CHUNK_ROWS, m, CHUNK_ROWS):
+            rows.update((r0 + b - 1, r0 + b))
+    toks = {int(gather[r]) // k for r in rows}
+    toks.update(int(t) for t in extra)
+    return sorted(toks)
+
+
+def planted_routing(n_experts, top_k, counts, n_tok, seed):
+    """Token sets S_t (n_tok x top_k expert ids, each row distinct) in which
+    expert e is chosen by exactly counts[e] tokens.  Experts are laid out one
+    after another on a cycle over the tokens, so an expert's counts[e] <=
+    n_tok entries land on distinct tokens and every token gets exactly top_k
+    entries (sum(counts) must be n_tok * top_k)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    assert counts.shape == (n_experts,) and counts.sum() == n_tok * top_k
+    assert counts.max() <= n_tok
+    order = np.random.default_rng(seed).permutation(n_experts)
+    slots = [[] for _ in range(n_tok)]
+    pos = 0
+    for e in order:
+        for i in range(int(counts[e])):
+            slots[(pos + i) % n_tok].append(int(e))
+        pos += int(counts[e])
+    sets = np.array(slots, dtype=np.int32)
+    assert sets.shape == (n_tok, top_k)
+    return sets
+
+
+def planted_inputs(spec, sets, seed):
+    """Activations (bf16 bits) and router weight under which the oracle's
+    top-k of token t is exactly the set sets[t]: W_r[:, e] is the unit vector
+    of row e plus N(0, 0.01^2) on the rows past E, x[t, e] lies in [2, 3) for
+    chosen experts and in (-3, -2] otherwise, and the other columns are
+    N(0, 1).  A logit is then x[t, e] plus noise of deviation
+    0.01 sqrt(H - E) (0.32 at H = 1024), against a gap of 4 between chosen
+    and other experts."""
+    from int4_routed_expert_layer_amd.inputs import f32_to_bf16_bits
+    g = np.random.default_rng(seed)
+    n_tok, E, H = sets.shape[0], spec.n_experts, spec.hidden
+    assert H > E
+    x = g.standard_normal((n_tok, H)).astype(np.float32)
+    chosen = np.zeros((n_tok, E), dtype=bool)
+    chosen[np.arange(n_tok)[:, None], sets] = True
+    mag = 2.0 + g.random((n_tok, E))
+    x[:, :E] = np.where(chosen, mag, -mag).astype(np.float32)
+    w = (g.standard_normal((H, E)) * 0.01).astype(np.float32)
+    w[:E, :] = 0.0
+    w[np.arange(E), np.arange(E)] = 1.0
+    return f32_to_bf16_bits(x), w

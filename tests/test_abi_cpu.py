@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lib.coli_abi_version() == 3
+    assert B.lib.coli_abi_version() == 4
     for st, name in enumerate(["COLI_OK", "COLI_E_INVALID", "COLI_E_NOMEM", "COLI_E_DEVICE",
                                "COLI_E_STATE", "COLI_E_UNSUPPORTED"]):
         assert B.status_str(st) == name
@@ -177,3 +177,24 @@ def test_repack_rejects_bad_sizes():
     assert B.lib.coli_expert_repack(None, buf.ctypes.data, 128, 128, 32, 4) == B.E_INVALID
     assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 128, 128, 48, 4) == B.E_INVALID
     assert B.lib.coli_expert_repack(buf.ctypes.data, buf.ctypes.data, 128, 128, 32, 16) == B.E_INVALID
+
+
+def test_create_refuses_shapes_past_32_bit_row_offsets():
+    # The grouped kernels index activation and h rows with 32-bit element
+    # offsets: (max_tokens * (k + 1) + 1) * max(H, I) must stay below 2^32.
+    st, h = create(hidden=2048, inter=1024, n_experts=16, top_k=8, max_tokens=262144)
+    assert st == B.E_UNSUPPORTED and not h.value
+    assert b"2^32" in B.lib.coli_last_error(None)
+
+
+def test_alloc_cap_fails_create_with_nomem_before_the_device():
+    assert B.alloc_bytes() == 0
+    B.set_alloc_limit(1 << 20)      # far below the layer's scratch
+    try:
+        st, h = create(max_tokens=4096)
+        assert st == B.E_NOMEM and not h.value
+        assert b"allocation cap" in B.lib.coli_last_error(None)
+    finally:
+        B.set_alloc_limit(-1)
+    assert B.lib.coli_set_alloc_limit(-2) == B.E_INVALID
+    assert B.alloc_bytes() == 0

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from int4_routed_expert_layer_amd import configs, inputs
-from moe_case import (Data, check_outputs, check_routing, gpu_run, log, make_layer,
+from moe_case import (Data, check_outputs, check_routing, edge_tokens, gpu_run, log, make_layer,
                       oracle_route, oracle_y)
 
 pytestmark = pytest.mark.gpu
@@ -137,5 +137,6 @@ def test_group64_full_size_prefill(full_size_g64):
     gpu = gpu_run(B, L, data)
     ref = oracle_route(data)
     check_routing(gpu, ref)
-    tokens = [0, 1, 777, 2048, 3001, 4095]
+    tokens = edge_tokens(ref, spec.top_k, extra=[0, 1, 777, 2048, 3001, 4095])
+    log(f"  comparing {len(tokens)} tokens")
     check_outputs(gpu["y"][tokens], oracle_y(data, ref, tokens), "g64 prefill_b4096")

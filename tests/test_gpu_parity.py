@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from int4_routed_expert_layer_amd import configs, inputs
-from moe_case import (Data, check_outputs, check_routing, gpu_run, log, make_layer,
+from moe_case import (Data, check_outputs, check_routing, edge_tokens, gpu_run, log, make_layer,
                       oracle_route, oracle_y)
 
 pytestmark = pytest.mark.gpu
@@ -207,7 +207,7 @@ def test_decode_b64_zipf_parity(path):
     check_routing(gpu, ref)
     log(f"  union size {ref['n_union']} of {spec.n_tok * spec.top_k} selections")
     assert ref["n_union"] < spec.n_tok * spec.top_k // 2
-    tokens = list(range(0, 64, 4)) + [63]
+    tokens = list(range(spec.n_tok))          # every token of the batch
     check_outputs(gpu["y"][tokens], oracle_y(data, ref, tokens), f"decode_b64/{path}")
     L.close()
 
@@ -223,7 +223,11 @@ def test_prefill_b4096_parity():
     check_routing(gpu, ref)
     c = ref["counts"]
     log(f"  tokens per expert: min {c.min()} max {c.max()}")
-    tokens = [0, 1, 777, 2048, 3001, 4095]
+    # Every expert's first and last gather row and both sides of each
+    # 160-row chunk boundary: each grouped work chunk of every expert has
+    # its first and last tile compared.
+    tokens = edge_tokens(ref, spec.top_k, extra=[0, 1, 777, 2048, 3001, 4095])
+    log(f"  comparing {len(tokens)} tokens")
     check_outputs(gpu["y"][tokens], oracle_y(data, ref, tokens), "prefill_b4096")
     L.close()
 

@@ -1,0 +1,52 @@
+"""Grouped MFMA path, element by element at every tile count: the router is
+planted so that per-expert token counts are 1, 32, 33, 96, 97, 160, 161 and
+321 (and filler experts take the rest).  The grouped kernels cut an expert's
+rows into chunks of at most 160 rows and run each chunk as one to five 32-row
+MFMA tiles, so these counts reach every tile count (1, 1, 2, 3, 4, 5), the
+160-row split with a one-row tail (161 -> 160 + 1, 321 -> 160 + 160 + 1) and,
+for the 330-token shared expert, 160 + 160 + 10.  Every token's output is
+compared with the oracle, at group sizes 32 and 64, on both strategies;
+routing and the union bit for bit, through the C ABI.
+"""
+import numpy as np
+import pytest
+
+from int4_routed_expert_layer_amd import configs
+from moe_case import (Data, check_outputs, check_routing, gpu_run, log, make_layer,
+                      oracle_route, oracle_y, planted_inputs, planted_routing)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from int4_routed_expert_layer_amd import binding as B  # noqa: E402
+
+# 8 planted counts + 5 fillers = 13 experts; 330 tokens x top-4 = 1320 entries.
+COUNTS = [1, 32, 33, 96, 97, 160, 161, 321, 100, 100, 100, 100, 19]
+SPEC = configs.Spec("tiles_h1024_i384_e13_k4_b330", 1024, 384, len(COUNTS), 4, 330, "bf16", True,
+                    "gauss", seed=4242)
+
+
+def planted_data(group):
+    spec = SPEC.with_(group=group)
+    data = Data(spec)
+    sets = planted_routing(spec.n_experts, spec.top_k, COUNTS, spec.n_tok, seed=11)
+    data.x, data.w = planted_inputs(spec, sets, seed=12)
+    return data
+
+
+@pytest.mark.parametrize("path", ["grouped", "gemv"])
+@pytest.mark.parametrize("group", [32, 64])
+def test_every_tile_count_and_chunk_split(group, path):
+    data = planted_data(group)
+    log(f"case planted counts group={group} path={path}")
+    ref = oracle_route(data)
+    np.testing.assert_array_equal(ref["counts"], COUNTS)     # the plant took
+    L = make_layer(B, data, path={"grouped": B.PATH_GROUPED, "gemv": B.PATH_GEMV}[path])
+    gpu = gpu_run(B, L, data)
+    check_routing(gpu, ref)
+    check_outputs(gpu["y"], oracle_y(data, ref, range(SPEC.n_tok)), f"planted g{group}/{path}")
+    assert L.device_errors() == 0
+    L.close()
