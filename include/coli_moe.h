@@ -228,6 +228,26 @@ coli_status coli_moe_layer(coli_layer *layer, const void *x, int32_t n_tok,
                            int32_t *offsets, int32_t *gather, float *y,
                            void *stream);
 
+/* coli_moe_layer for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, outputs and bits as coli_moe_layer's fused small-batch
+ * path, but its scratch (logits, h and per-entry output rows, arrival
+ * counters) lives in one static device array of 8 MiB per GPU, set up by the
+ * first coli_layer_create on that GPU and held until the process ends; the
+ * call allocates nothing and creates no HIP objects (kernel timing is not
+ * recorded).  Limits: the fused path only (1..4 tokens, n_experts <= 256,
+ * every expert in VRAM, router set, GEMV strategy), else COLI_E_UNSUPPORTED;
+ * a call needing more than 8 MiB of scratch, about
+ * n_tok*(k+1)*(4*H + 2*I) bytes, is refused with COLI_E_UNSUPPORTED before
+ * any device work.  Every layer on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (any layers, any streams) race and give
+ * undefined results; issue them in one stream order. */
+coli_status coli_moe_layer_static(coli_layer *layer, const void *x, int32_t n_tok,
+                                  int32_t *topk_idx, float *topk_w, int32_t *n_union,
+                                  int32_t *union_ids, int32_t *counts,
+                                  int32_t *offsets, int32_t *gather, float *y,
+                                  void *stream);
+
 /* Choose the forward strategy (coli_path).  Default COLI_PATH_AUTO.
  * COLI_E_UNSUPPORTED for COLI_PATH_GROUPED on an int8 layer (int8 layers
  * always take the GEMV path). */

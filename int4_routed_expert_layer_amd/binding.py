@@ -39,6 +39,7 @@ SIGNATURES = {
     "coli_moe_forward": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "coli_layer_set_path": (C.c_int, [_p, _i32]),
     "coli_moe_layer": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "coli_moe_layer_static": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "coli_layer_stream_stats": (C.c_int, [_p, _p, _p]),
     "coli_layer_set_stream_cache": (C.c_int, [_p, _i32]),
     "coli_layer_stream_hits": (C.c_int, [_p, _p]),
@@ -225,6 +226,22 @@ class MoELayer:
                                   _dptr(u["union_ids"]), _dptr(u["counts"]), _dptr(u["offsets"]),
                                   _dptr(u["gather"]), _dptr(y), _stream()), self.handle)
         return y, idx, w, u
+
+    def layer_static(self, x, out=None):
+        """coli_moe_layer_static: the fused small-batch call on the library's
+        static scratch.  ``out`` (optional) is a dict of preallocated outputs
+        with the keys layer() returns (y, idx, w, u)."""
+        import torch
+        n, k = x.shape[0], self.dims.top_k
+        if out is None:
+            out = dict(y=self._new((n, self.dims.hidden), torch.float32), idx=self._new((n, k), torch.int32),
+                       w=self._new((n, k), torch.float32), u=self._union_bufs(n))
+        u = out["u"]
+        _check(lib.coli_moe_layer_static(self.handle, _dptr(x), n, _dptr(out["idx"]), _dptr(out["w"]),
+                                         _dptr(u["n_union"]), _dptr(u["union_ids"]), _dptr(u["counts"]),
+                                         _dptr(u["offsets"]), _dptr(u["gather"]), _dptr(out["y"]), _stream()),
+               self.handle)
+        return out["y"], out["idx"], out["w"], u
 
     def __call__(self, x):
         idx, w = self.route(x)

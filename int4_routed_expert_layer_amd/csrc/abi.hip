@@ -244,6 +244,48 @@ void host_free(const void *p) {
 }  // namespace
 }  // namespace coli
 
+// Scratch of coli_moe_layer_static, the entry point that allocates
+// nothing: one array per GPU, in the code object's device memory, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: host code uses only the per-device address that
+// hipGetSymbolAddress returns (static_scratch_ptr).
+namespace coli {
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr int kStaticMaxDevices = 64;
+}  // namespace coli
+static __device__ __align__(256) uint8_t scratch[coli::kStaticScratchBytes];
+
+namespace coli {
+namespace {
+std::mutex g_static_mu;
+void *g_static_ptr[kStaticMaxDevices] = {};
+
+// Looks up the device address of `scratch` on `device` (current) and zeroes
+// it, once per device; later calls return the stored address.
+hipError_t static_scratch_setup(int device, void **out) {
+    *out = nullptr;
+    if (device < 0 || device >= kStaticMaxDevices) return hipSuccess;   // no static scratch there
+    std::lock_guard<std::mutex> g(g_static_mu);
+    if (!g_static_ptr[device]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if ((e = hipMemset(p, 0, kStaticScratchBytes)) != hipSuccess) return e;
+        if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+        g_static_ptr[device] = p;
+    }
+    *out = g_static_ptr[device];
+    return hipSuccess;
+}
+
+void *static_scratch_ptr(int device) {
+    if (device < 0 || device >= kStaticMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> g(g_static_mu);
+    return g_static_ptr[device];
+}
+}  // namespace
+}  // namespace coli
+
 using namespace coli;
 
 struct ExpertSlot {
@@ -788,6 +830,12 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         free_layer(L);
         return st;
     }
+    void *static_ptr = nullptr;
+    if ((he = static_scratch_setup(device, &static_ptr)) != hipSuccess) {
+        fail(nullptr, COLI_E_DEVICE, "static scratch setup: %s", hipGetErrorString(he));
+        free_layer(L);
+        return COLI_E_DEVICE;
+    }
     *out = L;
     return COLI_OK;
 }
@@ -1106,6 +1154,41 @@ coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t 
     const FusedScratch w{L->logits, L->h, L->ys, L->sync_counters,
                          static_cast<int>(L->d.max_tokens) * (L->d.top_k + 1)};
     return run_fused(L, w, true, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
+                     static_cast<hipStream_t>(stream));
+}
+
+coli_status coli_moe_layer_static(coli_layer *L, const void *x, int32_t n_tok, int32_t *topk_idx, float *topk_w,
+                                  int32_t *n_union, int32_t *union_ids, int32_t *counts, int32_t *offsets,
+                                  int32_t *gather, float *y, void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
+        return fail(L, COLI_E_INVALID, "NULL device pointer");
+    // Layout of this call in the static scratch: counters first (the same
+    // place for every call, zero at rest), then logits, h, ys.
+    const size_t H = static_cast<size_t>(L->d.hidden), I = static_cast<size_t>(L->d.inter);
+    const size_t rows = static_cast<size_t>(n_tok) * (L->d.top_k + 1) + 1;   // + the discard row
+    const size_t o_logits = align256(sizeof(int32_t) * (1 + H / 32));
+    const size_t o_h = o_logits + align256(sizeof(float) * n_tok * L->d.n_experts);
+    const size_t o_ys = o_h + align256(sizeof(_Float16) * rows * I);
+    const size_t need = o_ys + sizeof(float) * rows * H;
+    if (need > kStaticScratchBytes)
+        return fail(L, COLI_E_UNSUPPORTED, "this call needs %zu bytes of static scratch; the maximum is %zu",
+                    need, kStaticScratchBytes);
+    if (!fused_path(L, n_tok))
+        return fail(L, COLI_E_UNSUPPORTED,
+                    "the allocation-free call runs the fused small-batch path only: 1..%d tokens, <= 256 "
+                    "experts all in VRAM, router set, GEMV strategy",
+                    kFrontMaxTok);
+    uint8_t *base = static_cast<uint8_t *>(static_scratch_ptr(L->device));
+    if (!base) return fail(L, COLI_E_UNSUPPORTED, "no static scratch on device %d", L->device);
+    DeviceGuard guard(L->device);
+    const FusedScratch w{reinterpret_cast<float *>(base + o_logits), reinterpret_cast<_Float16 *>(base + o_h),
+                         reinterpret_cast<float *>(base + o_ys), reinterpret_cast<int32_t *>(base),
+                         static_cast<int>(rows) - 1};
+    return run_fused(L, w, false, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
                      static_cast<hipStream_t>(stream));
 }
 

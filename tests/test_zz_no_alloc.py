@@ -1,0 +1,97 @@
+"""The allocation-free entry point coli_moe_layer_static, through the C ABI:
+on the same layer and inputs it gives the bits of coli_moe_layer (the fused
+small-batch path, whose scratch lives in the layer), and outputs within
+tolerance of the oracle; two calls in a row, the second with fewer tokens,
+reuse the static scratch correctly; calls it cannot serve are refused before
+any device work."""
+import numpy as np
+import pytest
+
+from int4_routed_expert_layer_amd import configs
+from moe_case import Data, check_outputs, check_routing, log, make_layer, oracle_route, oracle_y
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from int4_routed_expert_layer_amd import binding as B  # noqa: E402
+
+SPEC = configs.Spec("static_h512_i256_e32_k4", 512, 256, 32, 4, 4, "bf16", True, "zipf", seed=31337)
+KEYS = ("y", "idx", "w")
+
+
+def fetch(y, idx, w, u):
+    torch.cuda.synchronize()
+    nu = int(u["n_union"].cpu()[0])
+    return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy(), w=w.cpu().numpy(), n_union=nu,
+                union_ids=u["union_ids"].cpu().numpy()[:nu], counts=u["counts"].cpu().numpy(),
+                offsets=u["offsets"].cpu().numpy(), gather=u["gather"].cpu().numpy())
+
+
+def same(a, b):
+    for key in ("y", "idx", "w", "union_ids", "counts", "offsets", "gather"):
+        assert np.array_equal(np.asarray(a[key]).view(np.uint8), np.asarray(b[key]).view(np.uint8)), key
+    assert a["n_union"] == b["n_union"]
+
+
+@pytest.mark.parametrize("spec", [SPEC, configs.DECODE_B1.with_(n_tok=4)], ids=["medium", "full"])
+def test_static_matches_layer_call(spec):
+    data = Data(spec)
+    log(f"case static scratch {spec.name}")
+    L = make_layer(B, data, max_tokens=4)
+    ref = oracle_route(data)
+    y_ref = oracle_y(data, ref, range(4))
+    for n in (4, 2, 1, 3):                     # second call smaller than the first
+        x = B.activations_to_device(data.x[:n])
+        st = fetch(*L.layer_static(x))
+        lay = fetch(*L.layer(x))
+        same(st, lay)
+        np.testing.assert_array_equal(st["idx"], ref["idx"][:n])
+        check_outputs(st["y"], y_ref[:n], f"static n_tok={n}")
+        assert L.device_errors() == 0
+    L.close()
+
+
+def test_static_shared_across_layers_in_one_stream():
+    """Two layers on one GPU share the static scratch; calls issued in one
+    stream order do not disturb each other."""
+    d1, d2 = Data(SPEC), Data(SPEC.with_(seed=4711))
+    L1, L2 = make_layer(B, d1, max_tokens=4), make_layer(B, d2, max_tokens=4)
+    x1, x2 = B.activations_to_device(d1.x), B.activations_to_device(d2.x)
+    want1, want2 = fetch(*L1.layer(x1)), fetch(*L2.layer(x2))
+    outs = []
+    for _ in range(3):
+        outs.append((L1.layer_static(x1), L2.layer_static(x2[:3])))
+    for o1, o2 in outs:
+        same(fetch(*o1), want1)
+        got2 = fetch(*o2)
+        want2_3 = fetch(*L2.layer(x2[:3]))
+        same(got2, want2_3)
+    L1.close()
+    L2.close()
+
+
+def test_static_refuses_what_it_cannot_serve():
+    data = Data(SPEC)
+    L = make_layer(B, data, max_tokens=8)
+    x = B.activations_to_device(data.x)
+    x8 = torch.cat([x, x])
+    with pytest.raises(B.ColiError) as ei:              # 8 tokens: not the fused path
+        L.layer_static(x8)
+    assert ei.value.status == B.E_UNSUPPORTED
+    L.place(3, data.blobs([3])[3], B.TIER_HOST)         # a host-tier expert: not the fused path
+    with pytest.raises(B.ColiError) as ei:
+        L.layer_static(x)
+    assert ei.value.status == B.E_UNSUPPORTED
+    L.close()
+    # A shape whose per-call scratch exceeds the 8 MiB array: refused on its
+    # size before anything else is looked at.
+    big = B.MoELayer(16384, 128, 32, 32, True, 4, act="bf16")
+    xb = torch.zeros((4, 16384), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.ColiError) as ei:
+        big.layer_static(xb)
+    assert ei.value.status == B.E_UNSUPPORTED
+    assert "static scratch" in str(ei.value)
+    big.close()
