@@ -99,3 +99,46 @@ def test_prefetch_then_replace_is_not_served_stale():
     ref = oracle_route(data)
     check_outputs(y.cpu().numpy(), oracle_y(data, ref, range(SPEC.n_tok)), "re-placed after prefetch")
     L.close()
+
+
+def test_lookahead_across_layers_on_a_second_stream():
+    """The stack's lookahead: while layer 0 runs on the main stream, layer 1's
+    route and union run on a second stream and its host-tier experts are
+    prefetched; then layer 1 runs.  Both layers give the bits of their
+    all-VRAM twins on every batch."""
+    specs = [SPEC.with_(seed=SPEC.seed + i) for i in range(2)]
+    datas = [Data(sp, n_tok=3 * SPEC.n_tok) for sp in specs]
+    refs = [make_layer(B, d, max_tokens=SPEC.n_tok) for d in datas]
+    layers = [make_layer(B, d, max_tokens=SPEC.n_tok) for d in datas]
+    for d, L in zip(datas, layers):
+        host = [e for e in range(SPEC.n_experts) if e % 2 == 1]
+        for e, blob in d.blobs(host).items():
+            L.place(e, blob, B.TIER_HOST)
+        d.drop_blobs()
+        L.set_stream_cache(8)
+    ahead = torch.cuda.Stream()
+    for b in range(3):
+        xs = [B.activations_to_device(d.x[b * SPEC.n_tok:(b + 1) * SPEC.n_tok]) for d in datas]
+        want = []
+        for L, x in zip(refs, xs):
+            y, _, _, _ = L(x)
+            want.append(y)
+        torch.cuda.synchronize()
+        idx0, w0 = layers[0].route(xs[0])
+        u0 = layers[0].union(idx0)
+        ahead.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(ahead):
+            idx1, w1 = layers[1].route(xs[1])
+            u1 = layers[1].union(idx1)
+            started = layers[1].prefetch_union(u1)
+        y0 = layers[0].forward(xs[0], idx0, w0, u0)
+        torch.cuda.current_stream().wait_stream(ahead)
+        y1 = layers[1].forward(xs[1], idx1, w1, u1)
+        torch.cuda.synchronize()
+        log(f"  batch {b}: layer 1 prefetched {started}, hits {layers[1].stream_hits()}")
+        assert layers[1].stream_hits() >= started
+        for got, ref in ((y0, want[0]), (y1, want[1])):
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
+    for L in refs + layers:
+        assert L.device_errors() == 0
+        L.close()

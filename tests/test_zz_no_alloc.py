@@ -36,7 +36,9 @@ def same(a, b):
     assert a["n_union"] == b["n_union"]
 
 
-@pytest.mark.parametrize("spec", [SPEC, configs.DECODE_B1.with_(n_tok=4)], ids=["medium", "full"])
+@pytest.mark.parametrize("spec", [SPEC, SPEC.with_(group=64), SPEC.with_(group=64, bits=8),
+                                  SPEC.with_(act="f32"), configs.DECODE_B1.with_(n_tok=4)],
+                         ids=["medium", "medium-g64", "medium-int8", "medium-f32", "full"])
 def test_static_matches_layer_call(spec):
     data = Data(spec)
     log(f"case static scratch {spec.name}")
