@@ -80,7 +80,10 @@ __device__ __forceinline__ bool stage8(const float *v, uint8_t *dst_x, float *ds
     return bad;
 }
 
-// LDS bytes of one gate/up panel item / one down panel-group item.
+// LDS bytes of one gate/up panel item / one down panel-group item: staged
+// activations (fp16), their 8-column seeds, the cross-wave partial sums, and
+// for the down items of two or more tokens (the matrix-core form) the
+// 32-column seed sums.
 __host__ __device__ inline size_t gateup_lds_bytes(int maxm, int hidden) {
     return static_cast<size_t>(maxm) * hidden * 2 + static_cast<size_t>(maxm) * (hidden / 8) * 4 +
            static_cast<size_t>(4) * maxm * 16 * 2 * 4;
@@ -92,9 +95,33 @@ __host__ __device__ inline size_t combine_lds_floats(size_t down_bytes, int k, i
     return down_bytes / sizeof(float) > one_token ? down_bytes / sizeof(float) : one_token;
 }
 
+// The down items of two to four tokens multiply on the matrix cores: each
+// 32-column slice of a 16-row chunk is one v_mfma_f32_16x16x32_f16 with the
+// unpacked weights as the B operand (the chunk layout is that operand's lane
+// layout) and the staged h rows of the tokens as A, so the vector ALUs only
+// unpack and scale (per token, the v_dot2 form costs four dots per weight
+// dword).  One-token items and the gate/up items keep the v_dot2 form, which
+// measured faster for them.
+template <int MAXM>
+constexpr bool down_mfma() { return MAXM >= 2; }
+
 __host__ __device__ inline size_t down_lds_bytes(int maxm, int inter) {
     return static_cast<size_t>(maxm) * inter * 2 + static_cast<size_t>(maxm) * (inter / 8) * 4 +
-           static_cast<size_t>(4) * maxm * 16 * 4;
+           static_cast<size_t>(4) * maxm * 16 * 4 + (maxm >= 2 ? static_cast<size_t>(maxm) * (inter / 32) * 4 : 0);
+}
+
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// The matrix-core form needs each 32-column slice's seed, the sum of its four
+// 8-column seeds, (c0 + c1) + (c2 + c3).  The staging loops hand 8-column
+// group q of a row to thread i = m K/8 + q (plus multiples of the block
+// size), so the four groups of a slice are on four adjacent lanes of one
+// wave, all active or all idle; the first of them stores the sum.
+__device__ __forceinline__ void stage_slice_seed(float c8, float *cs32, int K, int m, int q) {
+    float c = c8 + __shfl_xor(c8, 1, 64);
+    c = c + __shfl_xor(c, 2, 64);
+    if ((q & 3) == 0) cs32[m * (K / 32) + (q >> 2)] = c;
 }
 
 constexpr int kGateUpGroup = 2;   // gate/up chunks per register buffer
@@ -179,6 +206,26 @@ struct WFmt {
         if constexpr (WB == 4) return stage8(v, dst_x, dst_c);
         else return stage8_i8(v, dst_x, dst_c);
     }
+    // The lane's 8 columns of slice j as fp16 (1024 + u, or 1024 + 16 u for
+    // the int4 column pairs whose activations are staged divided by 16), in
+    // column order: the B fragment of v_mfma_f32_16x16x32_f16 for this lane.
+    __device__ static half8v frag(const uint32_t (&w)[4], int j, uint32_t M0, uint32_t M1, uint32_t G) {
+        uint4 r;
+        if constexpr (WB == 4) {
+            const uint32_t x = w[j], x8 = x >> 8;
+            r.x = (x & M0) | G;
+            r.y = (x & M1) | G;
+            r.z = (x8 & M0) | G;
+            r.w = (x8 & M1) | G;
+        } else {
+            const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+            r.x = (w0 & M0) | G;
+            r.y = ((w0 >> 8) & M0) | G;
+            r.z = (w1 & M0) | G;
+            r.w = ((w1 >> 8) & M0) | G;
+        }
+        return __builtin_bit_cast(half8v, r);
+    }
 };
 
 // Calls fn(F{}) with the format of a layer.
@@ -230,16 +277,20 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf<NG, F> &b, const uin
         const int c = first + step * g;
         const uint32_t gws[4] = {b.gw[g].x, b.gw[g].y, b.gw[g].z, b.gw[g].w};
         const uint32_t uws[4] = {b.uw[g].x, b.uw[g].y, b.uw[g].z, b.uw[g].w};
+        // The lane's activations and seeds of this chunk: one base address
+        // each, slice s at a constant offset (64 bytes of x, 4 seeds).
+        const int k0 = c * F::kCols + 8 * kq;
 #pragma unroll
         for (int s = 0; s < F::kSlices; ++s) {
             const float sg = F::scale(b.gs[g], s, row);
             const float su = F::scale(b.us[g], s, row);
-            const int k0 = c * F::kCols + 32 * s + 8 * kq;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 if (m < mc) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(xs + (static_cast<size_t>(m) * H + k0) * 2);
-                    const float c8 = cs[m * (H / 8) + (k0 >> 3)];
+                    const uint8_t *xrow = xs + (static_cast<size_t>(m) * H + k0) * 2;
+                    const float *crow = cs + m * (H / 8) + (k0 >> 3);
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(xrow + 64 * s);
+                    const float c8 = crow[4 * s];
                     gacc[m] = __builtin_fmaf(sg, F::dot(gws, s, xv, c8, M0, M1, G), gacc[m]);
                     vacc[m] = __builtin_fmaf(su, F::dot(uws, s, xv, c8, M0, M1, G), vacc[m]);
                 }
@@ -372,6 +423,7 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
                 gateup_math<MAXM>(B, xs, cs, H, wave + 4 * (i + NG), 4, min(NG, nper - i - NG), row, kq, mc, M0, M1, G,
                                   gacc, vacc);
         }
+        // The four lanes of a row hold the dots of its four 8-column groups.
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
             gacc[m] = gacc[m] + __shfl_xor(gacc[m], 16, 64);
@@ -446,18 +498,46 @@ __device__ __forceinline__ void down_math(const DownBuf<F> &b, const uint8_t *hs
         if (g >= count) continue;
         const int c = first + g;
         const uint32_t ws[4] = {b.w[g].x, b.w[g].y, b.w[g].z, b.w[g].w};
+        const int k0 = c * F::kCols + 8 * kq;
 #pragma unroll
         for (int s = 0; s < F::kSlices; ++s) {
             const float sf = F::scale(b.s[g], s, row);
-            const int k0 = c * F::kCols + 32 * s + 8 * kq;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 if (m < mc) {
-                    const uint4 hv = *reinterpret_cast<const uint4 *>(hs + (static_cast<size_t>(m) * I + k0) * 2);
-                    const float c8 = cs[m * (I / 8) + (k0 >> 3)];
+                    const uint8_t *hrow = hs + (static_cast<size_t>(m) * I + k0) * 2;
+                    const float *crow = cs + m * (I / 8) + (k0 >> 3);
+                    const uint4 hv = *reinterpret_cast<const uint4 *>(hrow + 64 * s);
+                    const float c8 = crow[4 * s];
                     acc[m] = __builtin_fmaf(sf, F::dot(ws, s, hv, c8, M0, M1, G), acc[m]);
                 }
             }
+        }
+    }
+}
+
+// Matrix-core form of down_math (see gateup_math_mfma).
+template <int MAXM, class F>
+__device__ __forceinline__ void down_math_mfma(const DownBuf<F> &b, const uint8_t *hs, const float *cs32, int I,
+                                               int first, int count, int row, int kq, int mc, uint32_t M0,
+                                               uint32_t M1, uint32_t G, float *acc) {
+    const int ma = row < MAXM ? row : 0;
+#pragma unroll
+    for (int g = 0; g < kPipeGroup; ++g) {
+        if (g >= count) continue;
+        const int c = first + g;
+        const uint32_t ws[4] = {b.w[g].x, b.w[g].y, b.w[g].z, b.w[g].w};
+        const uint8_t *hrow = hs + (static_cast<size_t>(ma) * I + c * F::kCols + 8 * kq) * 2;
+        const float *crow = cs32 + (c * F::kCols) / 32;
+#pragma unroll
+        for (int s = 0; s < F::kSlices; ++s) {
+            const half8v av = *reinterpret_cast<const half8v *>(hrow + 64 * s);
+            const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            const float4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, F::frag(ws, s, M0, M1, G), zero, 0, 0, 0);
+            const float sf = F::scale(b.s[g], s, row);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+                if (m < mc) acc[m] = __builtin_fmaf(sf, d[m] + crow[m * (I / 32) + s], acc[m]);
         }
     }
 }
@@ -489,6 +569,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
     uint8_t *hs = lds;
     float *cs = reinterpret_cast<float *>(lds + static_cast<size_t>(MAXM) * I * 2);
     float *red = cs + MAXM * (I / 8);
+    float *cs32 = red + 4 * MAXM * 16;
     const uint32_t M0 = vconst(F::kMask0), M1 = vconst(F::kMask1), G = vconst(0x64006400u);
 
     for (int mb = 0; mb < M; mb += MAXM) {
@@ -527,6 +608,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
                 F::stage(v, dst, cs + m * (I / 8) + q);
+                if constexpr (down_mfma<MAXM>()) stage_slice_seed(cs[m * (I / 8) + q], cs32, I, m, q);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -542,22 +624,30 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(hv[j]);
                 F::stage(v, hs + (static_cast<size_t>(m) * I + 8 * q) * 2, cs + m * (I / 8) + q);
+                if constexpr (down_mfma<MAXM>()) stage_slice_seed(cs[m * (I / 8) + q], cs32, I, m, q);
             }
             __syncthreads();
         }
+        auto math = [&](const DownBuf<F> &buf, int first, int count) {
+            if constexpr (down_mfma<MAXM>())
+                down_math_mfma<MAXM>(buf, hs, cs32, I, first, count, row, kq, mc, M0, M1, G, acc);
+            else
+                down_math<MAXM>(buf, hs, cs, I, first, count, row, kq, mc, M0, M1, G, acc);
+        };
         for (int i = 0; i < nper; i += 2 * kPipeGroup) {
             if (i + kPipeGroup < nper && (i > 0 || !b_issued))
                 down_load(B, rs, vq, vs, sq, ss, c_begin + i + kPipeGroup, C);
-            down_math<MAXM>(A, hs, cs, I, c_begin + i, min(kPipeGroup, nper - i), row, kq, mc, M0, M1, G, acc);
+            math(A, c_begin + i, min(kPipeGroup, nper - i));
             if (i + 2 * kPipeGroup < nper) down_load(A, rs, vq, vs, sq, ss, c_begin + i + 2 * kPipeGroup, C);
-            if (i + kPipeGroup < nper)
-                down_math<MAXM>(B, hs, cs, I, c_begin + i + kPipeGroup, min(kPipeGroup, nper - i - kPipeGroup),
-                                row, kq, mc, M0, M1, G, acc);
+            if (i + kPipeGroup < nper) math(B, c_begin + i + kPipeGroup, min(kPipeGroup, nper - i - kPipeGroup));
         }
+        if constexpr (!down_mfma<MAXM>()) {
+            // The four lanes of a row hold the dots of its four 8-column groups.
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) {
-            acc[m] = acc[m] + __shfl_xor(acc[m], 16, 64);
-            acc[m] = acc[m] + __shfl_xor(acc[m], 32, 64);
+            for (int m = 0; m < MAXM; ++m) {
+                acc[m] = acc[m] + __shfl_xor(acc[m], 16, 64);
+                acc[m] = acc[m] + __shfl_xor(acc[m], 32, 64);
+            }
         }
         if (lane < 16) {
 #pragma unroll
