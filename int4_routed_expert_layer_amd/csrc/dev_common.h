@@ -112,23 +112,36 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
 }
 
+// Load through the scalar data cache: a wave-uniform address read as
+// constant memory becomes s_load, which waits on its own counter (not behind
+// vector loads in flight) and skips the vector cache path.  Only for data no
+// workgroup of the running launch writes (the routing arrays, written by
+// earlier launches; the scalar cache is invalidated at every launch).
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)(p);
+}
+
 // Work unit u of a forward call: routed union entry (u < n_union) or the
-// shared expert (u == n_union).  Returns false when u is past the last unit.
-__device__ __forceinline__ bool resolve(const FwdArgs &a, int u, int &e, int &r0, int &m) {
-    const int nu = *a.n_union;
-    if (u < nu) {
-        e = a.union_ids[u];
-        r0 = a.offsets[e];
-        m = a.counts[e];
-        return true;
-    }
-    if (u == nu && a.has_shared) {
-        e = a.n_experts;
-        r0 = a.n_tok * a.k;
-        m = a.n_tok;
-        return true;
-    }
-    return false;
+// shared expert (u == n_union), with its blob pointer.  Returns false when u
+// is past the last unit.  The loads come in two rounds, not four: the union
+// size and the union entry at u are read together (the entry speculatively,
+// at an in-range index), then the entry's offset, count and blob together.
+// u must be wave-uniform and the routing arrays written by earlier launches.
+__device__ __forceinline__ bool resolve(const FwdArgs &a, int u, int &e, int &r0, int &m, const uint8_t *&blob) {
+    const int E = a.n_experts;
+    const int nu = ld_uniform(a.n_union);
+    const int es = ld_uniform(a.union_ids + (u < E ? u : E - 1));
+    asm volatile("" ::"s"(nu), "s"(es));   // both loads issued before the first use
+    const bool routed = u < nu;
+    if (!routed && !(u == nu && a.has_shared)) return false;
+    const int ec = routed ? (es >= 0 && es < E ? es : 0) : 0;
+    const int r0s = ld_uniform(a.offsets + ec), ms = ld_uniform(a.counts + ec);
+    e = routed ? ec : E;
+    blob = ld_uniform(a.table + e);
+    r0 = routed ? r0s : a.n_tok * a.k;
+    m = routed ? ms : a.n_tok;
+    return true;
 }
 
 // Token of hidden-buffer row `row`: routed rows are in gather order, shared
@@ -136,7 +149,7 @@ __device__ __forceinline__ bool resolve(const FwdArgs &a, int u, int &e, int &r0
 __device__ __forceinline__ int token_of_row(const FwdArgs &a, int row) {
     if (a.n_tok == 1) return 0;   // one token: no lookup
     const int routed = a.n_tok * a.k;
-    return row < routed ? a.gather[row] / a.k : row - routed;
+    return row < routed ? ld_uniform(a.gather + row) / a.k : row - routed;
 }
 
 // Monotonic unsigned key of a finite float (larger float -> larger key);

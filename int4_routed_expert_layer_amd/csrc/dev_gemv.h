@@ -468,8 +468,10 @@ struct NoWait {
 struct PlainRows {
     const FwdArgs &a;
     __device__ int token(int row) const { return token_of_row(a, row); }
-    __device__ int entry(int row) const { return row < a.n_tok * a.k ? a.gather[row] : row; }
-    __device__ float weight(int row) const { return row < a.n_tok * a.k ? a.topk_w[a.gather[row]] : 1.0f; }
+    __device__ int entry(int row) const { return row < a.n_tok * a.k ? ld_uniform(a.gather + row) : row; }
+    __device__ float weight(int row) const {
+        return row < a.n_tok * a.k ? ld_uniform(a.topk_w + ld_uniform(a.gather + row)) : 1.0f;
+    }
 };
 
 template <class F>
@@ -577,6 +579,19 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
         float acc[MAXM];
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+        // Output entry and routing weight of each row, looked up while the
+        // first weights and h are in flight (not as a chain in front of the
+        // ys stores, nor in front of the weight loads).
+        int ents[MAXM];
+        float wgts[MAXM];
+        auto lookup_rows = [&]() {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                const int hrow = r0 + mb + (m < mc ? m : 0);
+                ents[m] = rows.entry(hrow);
+                wgts[m] = rows.weight(hrow);
+            }
+        };
         DownBuf<F> A, B;
         bool b_issued = false;
         if (mb == 0) before_h();
@@ -596,6 +611,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
             down_load(A, rs, vq, vs, sq, ss, c_begin, C);
             down_load(B, rs, vq, vs, sq, ss, c_begin + kPipeGroup, C);
             b_issued = true;
+            lookup_rows();
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kPipeGroup) : "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
@@ -615,6 +631,7 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
             asm volatile("" ::: "memory");
         } else {
             down_load(A, rs, vq, vs, sq, ss, c_begin, C);
+            lookup_rows();
             for (int i = tid; i < mc * (I / 8); i += 256) {
                 const int m = i / (I / 8), q = i % (I / 8);
                 const _Float16 *src = a.h + static_cast<size_t>(r0 + mb + m) * I + 8 * q;
@@ -659,9 +676,13 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
             const int m = rest >> 4, r = rest & 15;
             // waves `side` (first half) and `side + 2` (second half)
             const float d = red[(side * MAXM + m) * 16 + r] + red[((side + 2) * MAXM + m) * 16 + r];
-            const int hrow = r0 + mb + m;
-            const int entry = rows.entry(hrow);
-            const float wgt = rows.weight(hrow);
+            int entry = ents[0];
+            float wgt = wgts[0];
+#pragma unroll
+            for (int mm = 1; mm < MAXM; ++mm) {
+                entry = m == mm ? ents[mm] : entry;
+                wgt = m == mm ? wgts[mm] : wgt;
+            }
             float *dst = a.ys + static_cast<size_t>(entry) * H + (2 * pg + side) * kPanel + r;
             if (COHERENT) store_coherent(dst, wgt * d);
             else *dst = wgt * d;

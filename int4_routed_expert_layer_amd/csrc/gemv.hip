@@ -11,15 +11,25 @@
 namespace coli {
 namespace {
 
+// Kernel arguments an item needs once its unit is known, fetched with the
+// first batch of argument loads: otherwise the compiler reads them after the
+// unit lookups, one more scalar round trip in front of the weight stream.
+__device__ __forceinline__ void fetch_args_early(const FwdArgs &a) {
+    asm volatile("" ::"s"(a.x), "s"(a.act_bf16), "s"(a.h), "s"(a.ys), "s"(a.err), "s"(a.skip_shared), "s"(a.lay.total),
+                 "s"(a.lay.gate_q), "s"(a.lay.up_q), "s"(a.lay.down_q), "s"(a.lay.gate_s), "s"(a.lay.up_s),
+                 "s"(a.lay.down_s));
+}
+
 template <class F, int MAXM>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int P = a.inter / kPanel;
     const int u = u_begin + blockIdx.x / P, p = blockIdx.x % P;
+    fetch_args_early(a);
     int e, r0, M;
-    if (!dev::resolve(a, u, e, r0, M)) return;
+    const uint8_t *blob;
+    if (!dev::resolve(a, u, e, r0, M, blob)) return;
     if (a.skip_shared && e == a.n_experts) return;
-    const uint8_t *blob = a.table[e];
     if (!blob || M <= 0) return;
     dev::gateup_panel<F, MAXM>(a, dev::PlainRows{a}, blob, r0, M, p, lds, dev::lds_address(lds));
 }
@@ -32,9 +42,10 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
     if (idle_counter && blockIdx.x == 0 && threadIdx.x == 0) dev::store_coherent(idle_counter, 0);
     const int PG = a.hidden / (2 * kPanel);
     const int u = blockIdx.x / PG, pg = blockIdx.x % PG;
+    fetch_args_early(a);
     int e, r0, M;
-    if (!dev::resolve(a, u, e, r0, M)) return;
-    const uint8_t *blob = a.table[e];
+    const uint8_t *blob;
+    if (!dev::resolve(a, u, e, r0, M, blob)) return;
     if (blob && M > 0)
         dev::down_panelgroup<F, MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::lds_address(lds),
                                                   dev::NoWait{});
