@@ -472,11 +472,11 @@ bool dims_supported(const coli_moe_dims *d, std::string &why) {
     }
     // The grouped kernels address activation and h rows with 32-bit element
     // offsets (row * width + column) over the rows of one call plus the
-    // discard row; buffer descriptors cover one expert blob with a 32-bit
-    // byte count.
-    const int64_t rows = static_cast<int64_t>(d->max_tokens) * (d->top_k + 1) + 1;
+    // discard and zero rows; buffer descriptors cover one expert blob with a
+    // 32-bit byte count.
+    const int64_t rows = static_cast<int64_t>(d->max_tokens) * (d->top_k + 1) + 2;
     if (rows * std::max(d->hidden, d->inter) >= (int64_t(1) << 32)) {
-        std::snprintf(buf, sizeof buf, "(max_tokens * (top_k + 1) + 1) * max(hidden, inter) = %lld must be < 2^32",
+        std::snprintf(buf, sizeof buf, "(max_tokens * (top_k + 1) + 2) * max(hidden, inter) = %lld must be < 2^32",
                       static_cast<long long>(rows * std::max(d->hidden, d->inter)));
         why = buf;
         return false;
@@ -498,7 +498,7 @@ size_t create_bytes(const coli_moe_dims *d) {
     const size_t rows = T * k + T;
     const size_t chunks = static_cast<size_t>(max_work_chunks(d->max_tokens, d->top_k, d->n_experts, d->has_shared));
     return sizeof(float) * E * H + sizeof(float) * E + sizeof(void *) * (E + 1) + sizeof(float) * T * E +
-           sizeof(_Float16) * (rows + 1) * I + sizeof(_Float16) * T * H + sizeof(float) * (rows + 1) * H +
+           sizeof(_Float16) * (rows + 2) * I + sizeof(_Float16) * (T + 1) * H + sizeof(float) * (rows + 1) * H +
            sizeof(ChunkDesc) * chunks + 2 * sizeof(int32_t) + sizeof(int32_t) * (1 + H / 32) +
            sizeof(int32_t) * kQueueInts + sizeof(int32_t) * (kUnionMaxBlocks * E + 64) + sizeof(int32_t) * T * k +
            blob_layout(d->hidden, d->inter, d->group, d->weight_bits).total + sizeof(int32_t) * (E + 1);
@@ -540,6 +540,8 @@ FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, 
     a.xh = L->xh;
     a.ys = L->ys;
     a.discard_row = static_cast<int>(L->d.max_tokens) * (L->d.top_k + 1);
+    a.zero_row_h = a.discard_row + 1;
+    a.zero_row_x = static_cast<int>(L->d.max_tokens);
     a.y = y;
     a.chunks = L->chunks;
     a.n_chunks = L->n_chunks;
@@ -668,6 +670,7 @@ coli_status run_fused(coli_layer *L, const FusedScratch &w, bool timed, const vo
     a.ys = w.ys;
     a.xh = nullptr;                      // the fp16 copy of x is a grouped-path buffer
     a.discard_row = w.discard_row;
+    a.zero_row_x = a.zero_row_h = -1;    // (grouped path only)
     FrontArgs f{};
     f.wt = L->wt;
     f.bias = L->bias;
@@ -797,8 +800,8 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->bias), sizeof(float) * E, "router bias"},
         {reinterpret_cast<void **>(&L->table_dev), sizeof(void *) * (E + 1), "expert table"},
         {reinterpret_cast<void **>(&L->logits), sizeof(float) * T * E, "logits scratch"},
-        {reinterpret_cast<void **>(&L->h), sizeof(_Float16) * (rows + 1) * I, "hidden scratch"},
-        {reinterpret_cast<void **>(&L->xh), sizeof(_Float16) * T * H, "fp16 activation scratch"},
+        {reinterpret_cast<void **>(&L->h), sizeof(_Float16) * (rows + 2) * I, "hidden scratch"},
+        {reinterpret_cast<void **>(&L->xh), sizeof(_Float16) * (T + 1) * H, "fp16 activation scratch"},
         {reinterpret_cast<void **>(&L->ys), sizeof(float) * (rows + 1) * H, "per-entry output scratch"},
         {reinterpret_cast<void **>(&L->chunks), sizeof(ChunkDesc) * L->max_chunks, "work list"},
         {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
@@ -816,7 +819,9 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
             return st;
         }
     }
-    if ((he = hipMemset(L->table_dev, 0, sizeof(void *) * (E + 1))) != hipSuccess ||
+    if ((he = hipMemset(L->h + (rows + 1) * I, 0, sizeof(_Float16) * I)) != hipSuccess ||
+        (he = hipMemset(L->xh + T * H, 0, sizeof(_Float16) * H)) != hipSuccess ||
+        (he = hipMemset(L->table_dev, 0, sizeof(void *) * (E + 1))) != hipSuccess ||
         (he = hipMemset(L->err, 0, sizeof(int32_t))) != hipSuccess ||
         (he = hipMemset(L->sync_counters, 0, sizeof(int32_t) * (1 + H / 32))) != hipSuccess ||
         (he = hipMemset(L->queues, 0, sizeof(int32_t) * kQueueInts)) != hipSuccess ||

@@ -393,10 +393,14 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
 
         __syncthreads();   // previous item is done with s_tok and the A tiles
         for (int m = tid; m < kChunkRows; m += 256) {
-            // Rows past `rows` repeat row 0: their results are discarded.
+            // Rows past `rows` read a row of zeros (their results are
+            // discarded): zero operands draw less power in the matrix cores,
+            // which run at a power limit (measured: B = 64 GEMMs 5-7% faster
+            // than with a repeated real row).
             const int mm = m < d.rows ? m : 0;
             const int r = d.row0 + mm;
-            s_tok[m] = GATEUP ? (r < routed ? a.gather[r] / a.k : r - routed) : r;
+            s_tok[m] = m >= d.rows ? (GATEUP ? a.zero_row_x : a.zero_row_h)
+                                   : (GATEUP ? (r < routed ? a.gather[r] / a.k : r - routed) : r);
             if (!GATEUP) {
                 const int entry = r < routed ? a.gather[r] : r;
                 s_ent[m] = m < d.rows ? entry : a.discard_row;

@@ -88,10 +88,11 @@ struct FwdArgs {
     const float *topk_w;
     int n_tok, k, hidden, inter, n_experts, has_shared;
     BlobLayout lay;
-    _Float16 *h;                    // [(n_tok*k + n_tok) x I], plus the discard row
-    _Float16 *xh;                   // [n_tok x H] fp16 copy of x (grouped path)
+    _Float16 *h;                    // [(n_tok*k + n_tok) x I], plus the discard row and a zero row
+    _Float16 *xh;                   // [n_tok x H] fp16 copy of x (grouped path), plus a zero row
     float *ys;                      // [(n_tok*k + n_tok) x H], plus the discard row
     int discard_row;                // row of h and ys that takes the padding rows' stores
+    int zero_row_x, zero_row_h;     // rows of xh and h holding zeros: the padding rows' A operand
     float *y;                       // [n_tok x H]
     const ChunkDesc *chunks;        // grouped path work list
     const int32_t *n_chunks;

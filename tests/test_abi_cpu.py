@@ -181,10 +181,24 @@ def test_repack_rejects_bad_sizes():
 
 def test_create_refuses_shapes_past_32_bit_row_offsets():
     # The grouped kernels index activation and h rows with 32-bit element
-    # offsets: (max_tokens * (k + 1) + 1) * max(H, I) must stay below 2^32.
+    # offsets: (max_tokens * (k + 1) + 2) * max(H, I) (the rows of a call, the
+    # discard row and the zero row) must stay below 2^32.
     st, h = create(hidden=2048, inter=1024, n_experts=16, top_k=8, max_tokens=262144)
     assert st == B.E_UNSUPPORTED and not h.value
     assert b"2^32" in B.lib.coli_last_error(None)
+    # The exact boundary: 2^32 / 2048 = 2^21 rows; with k = 2, 699050 tokens
+    # make 3 * 699050 + 2 = 2^21 rows.  With the allocation cap far below the
+    # layer's scratch, an accepted shape stops at the cap (E_NOMEM, before any
+    # device call) and a refused one at the shape check.
+    assert 3 * 699050 + 2 == 2 ** 21
+    B.set_alloc_limit(1 << 20)
+    try:
+        st, h = create(hidden=2048, inter=1024, n_experts=16, top_k=2, max_tokens=699049)
+        assert st == B.E_NOMEM and not h.value
+        st, h = create(hidden=2048, inter=1024, n_experts=16, top_k=2, max_tokens=699050)
+        assert st == B.E_UNSUPPORTED and not h.value
+    finally:
+        B.set_alloc_limit(-1)
 
 
 def test_alloc_cap_fails_create_with_nomem_before_the_device():
