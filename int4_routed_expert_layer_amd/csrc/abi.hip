@@ -496,7 +496,7 @@ size_t create_bytes(const coli_moe_dims *d) {
                  I = static_cast<size_t>(d->inter), T = static_cast<size_t>(d->max_tokens),
                  k = static_cast<size_t>(d->top_k);
     const size_t rows = T * k + T;
-    const size_t chunks = static_cast<size_t>(max_work_chunks(d->max_tokens, d->top_k, d->n_experts, d->has_shared));
+    const size_t chunks = static_cast<size_t>(work_list_capacity(d->max_tokens, d->top_k, d->n_experts, d->has_shared));
     return sizeof(float) * E * H + sizeof(float) * E + sizeof(void *) * (E + 1) + sizeof(float) * T * E +
            sizeof(_Float16) * (rows + 2) * I + sizeof(_Float16) * (T + 1) * H + sizeof(float) * (rows + 1) * H +
            sizeof(ChunkDesc) * chunks + 2 * sizeof(int32_t) + sizeof(int32_t) * (1 + H / 32) +
@@ -544,6 +544,7 @@ FwdArgs make_args(coli_layer *L, const void *x, int n_tok, const float *topk_w, 
     a.zero_row_x = static_cast<int>(L->d.max_tokens);
     a.y = y;
     a.chunks = L->chunks;
+    a.chunk_rows = chunk_rows_for(n_tok);
     a.n_chunks = L->n_chunks;
     a.queues = L->queues;
     a.skip_shared = 0;
@@ -561,7 +562,7 @@ coli_status launch_experts(coli_layer *L, const FwdArgs &a, int path, hipStream_
         KernelMark m(L, COLI_K_DOWN, s);
         if ((e = launch_gemv_down(a, L->max_lds, s)) != hipSuccess) return hip_fail(L, e, "gemv down launch");
     } else {
-        const int mc = max_work_chunks(a.n_tok, a.k, a.n_experts, a.has_shared);
+        const int mc = max_work_chunks(a.n_tok, a.k, a.n_experts, a.has_shared, a.chunk_rows);
         {
             KernelMark m(L, COLI_K_GATEUP, s);
             if ((e = launch_grouped_gateup(a, mc, L->n_cu, s)) != hipSuccess) return hip_fail(L, e, "grouped gate/up launch");
@@ -790,7 +791,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
     const int E = dims->n_experts, H = dims->hidden, I = dims->inter;
     const size_t T = static_cast<size_t>(dims->max_tokens);
     const size_t rows = T * dims->top_k + T;
-    L->max_chunks = max_work_chunks(dims->max_tokens, dims->top_k, E, dims->has_shared);
+    L->max_chunks = work_list_capacity(dims->max_tokens, dims->top_k, E, dims->has_shared);
     L->experts.resize(E + 1);
     L->expert_slot.assign(E, -1);
     L->table_host.assign(E + 1, nullptr);

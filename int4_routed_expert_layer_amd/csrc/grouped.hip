@@ -3,11 +3,13 @@
 //
 // When the union gives experts many tokens (large decode batches, prefill)
 // the expert matmuls become dense contractions, [M_u x K] x [K x N] per
-// union expert.  Work is a list of chunks (one expert, <= 160 rows) crossed
-// with N-blocks; a persistent grid walks that list (the N-blocks of a chunk,
-// which share its activation rows, are queued on one XCD and its L2).
+// union expert.  Work is a list of chunks (one expert, <= 160 rows; <= 32
+// rows for calls of at most 64 tokens, where experts get a few rows each)
+// crossed with N-blocks; a persistent grid walks that list (the N-blocks of a
+// chunk, which share its activation rows, are queued on one XCD and its L2).
 //
-// Per item a 256-thread workgroup (two per CU) walks the reduction axis in
+// Per item a 256-thread workgroup (two per CU; four with 32-row chunks, whose
+// stages and registers are smaller) walks the reduction axis in
 // 64-column steps through a ring of three LDS stages: the chunk's fp16
 // activation rows of step c + 2 are copied straight from global memory into
 // LDS (global_load_lds; XOR-swizzled 16-byte units, conflict-free for the
@@ -39,13 +41,17 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // The K loop advances 64 reduction columns per step through a ring of three
-// LDS stages of kChunkRows rows (two workgroups per CU): the activation copy
-// and the weight loads of step c + 2 are issued while step c is multiplied.
+// LDS stages of CR rows (the chunk size: 160 rows, two workgroups per CU, or
+// 32 rows for small calls, four per CU): the activation copy and the weight
+// loads of step c + 2 are issued while step c is multiplied.
 constexpr int kStepK = 64;
 constexpr int kStageRowBytes = kStepK * 2;                  // one staged row: 64 fp16
 constexpr int kStages = 3;
 constexpr int kAhead = 2;                                   // steps issued ahead
-constexpr int kStageBytes = kChunkRows * kStageRowBytes;   // 20 KB
+template <int CR>
+constexpr int stage_bytes() { return CR * kStageRowBytes; }  // 20 KB or 4 KB
+template <int CR>
+constexpr int blocks_per_cu() { return CR == kSmallChunkRows ? 4 : 2; }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
@@ -138,7 +144,7 @@ struct ItemState {
 // make that wait stricter).  Lookahead past the last step repeats the last
 // step's addresses (never used), so that count holds at every step; the loop
 // ends with a full wait before the stages are reused.
-template <bool GATEUP, int MT, int GS>
+template <bool GATEUP, int MT, int GS, int CR>
 __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, const uint8_t *s_a,
                                          uint32_t sa_lds, const int *s_ent, const float *s_w) {
     const int H = a.hidden, I = a.inter;
@@ -150,7 +156,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     };
     auto issue = [&](int c, B64 &f) {
         const int cc = min(c, st.C2 - 1);
-        const uint32_t dst = sa_lds + static_cast<uint32_t>(c % kStages) * kStageBytes;
+        const uint32_t dst = sa_lds + static_cast<uint32_t>(c % kStages) * stage_bytes<CR>();
 #pragma unroll
         for (int j = 0; j < MT; ++j)
             dev::copy16_to_lds(st.asrc + st.src_off[j] + cc * kStepK,
@@ -196,7 +202,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     // latency and dequantisation overlap the matrix pipe.
     auto compute = [&](int c, const B64 &f) {
         if (c >= st.C2) return;
-        const uint8_t *tile = s_a + (c % kStages) * kStageBytes;
+        const uint8_t *tile = s_a + (c % kStages) * stage_bytes<CR>();
         half8 av[MT], bc[2];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -294,16 +300,16 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     if (GATEUP) dev::flag_if(hbad, a.err, kErrHiddenRange);
 }
 
-template <bool GATEUP, int GS>
-__global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
-    // Ring of A stages, kChunkRows rows x kStepK fp16 each.
-    __shared__ __align__(16) uint8_t s_a[kStages * kStageBytes];
+template <bool GATEUP, int GS, int CR>
+__global__ __launch_bounds__(256, blocks_per_cu<CR>()) void grouped_kernel(FwdArgs a) {
+    // Ring of A stages, CR rows x kStepK fp16 each.
+    __shared__ __align__(16) uint8_t s_a[kStages * stage_bytes<CR>()];
     // LDS byte address of s_a (for the copies' M0).
     const uint32_t sa_lds = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)(&s_a[0])));
-    __shared__ int s_tok[kChunkRows];
-    __shared__ int s_ent[GATEUP ? 1 : kChunkRows];     // down: output entry and routing weight per row
-    __shared__ float s_w[GATEUP ? 1 : kChunkRows];
+    __shared__ int s_tok[CR];
+    __shared__ int s_ent[GATEUP ? 1 : CR];     // down: output entry and routing weight per row
+    __shared__ float s_w[GATEUP ? 1 : CR];
     const int H = a.hidden, I = a.inter;
     const int K = GATEUP ? H : I;
     const int NB = GATEUP ? I / 128 : (H + 255) / 256;
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         st.nb = nb;
         st.C2 = K / kStepK;
         const int C = K / kChunkK;
-        // 32-row tiles: 1 to 5 (padding rows are computed and discarded).
+        // 32-row tiles: 1 to CR / 32 (padding rows are computed and discarded).
         const int mt = (d.rows + 31) / 32;
 
         // This wave's two 32-row B tiles (two 16-row panels each), as
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         }
 
         __syncthreads();   // previous item is done with s_tok and the A tiles
-        for (int m = tid; m < kChunkRows; m += 256) {
+        for (int m = tid; m < CR; m += 256) {
             // Rows past `rows` read a row of zeros (their results are
             // discarded): zero operands draw less power in the matrix cores,
             // which run at a power limit (measured: B = 64 GEMMs 5-7% faster
@@ -413,17 +419,21 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(FwdArgs a) {
         // m = 8 (wave + 4j) + L / 8 with logical unit (L & 7) ^ lds_swz(m).
         const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
+        for (int j = 0; j < CR / 32; ++j) {
             const int m = 8 * (wave + 4 * j) + (lane >> 3);
             const int q = (lane & 7) ^ lds_swz(m);
             st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
         }
-        switch (mt) {
-            case 5: run_item<GATEUP, 5, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            case 4: run_item<GATEUP, 4, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            case 3: run_item<GATEUP, 3, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            case 2: run_item<GATEUP, 2, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
-            default: run_item<GATEUP, 1, GS>(a, st, s_a, sa_lds, s_ent, s_w); break;
+        if constexpr (CR == kSmallChunkRows) {
+            run_item<GATEUP, 1, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w);
+        } else {
+            switch (mt) {
+                case 5: run_item<GATEUP, 5, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 4: run_item<GATEUP, 4, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 3: run_item<GATEUP, 3, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 2: run_item<GATEUP, 2, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                default: run_item<GATEUP, 1, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            }
         }
     }
     // The last workgroup out clears the queue counters for the next launch.
@@ -488,6 +498,23 @@ int grid_for(int items, int slots) {
     return g < 1 ? 1 : g;
 }
 
+template <bool GATEUP, int CR>
+void launch_grouped_as(const FwdArgs &a, int items, int n_cu, hipStream_t s) {
+    const unsigned grid = grid_for(items, blocks_per_cu<CR>() * n_cu);
+    if (a.lay.group == 64) launch(grouped_kernel<GATEUP, 64, CR>, grid, 256, 0, s, a);
+    else launch(grouped_kernel<GATEUP, 32, CR>, grid, 256, 0, s, a);
+}
+
+template <bool GATEUP>
+hipError_t launch_grouped(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
+    if (a.lay.bits != 4) return hipErrorInvalidValue;      // the MFMA fragments are int4 only
+    const int items = max_chunks * (GATEUP ? a.inter / 128 : (a.hidden + 255) / 256);
+    if (a.chunk_rows == kSmallChunkRows) launch_grouped_as<GATEUP, kSmallChunkRows>(a, items, n_cu, s);
+    else if (a.chunk_rows == kChunkRows) launch_grouped_as<GATEUP, kChunkRows>(a, items, n_cu, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
@@ -498,19 +525,11 @@ hipError_t launch_to_half(const FwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_grouped_gateup(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
-    if (a.lay.bits != 4) return hipErrorInvalidValue;      // the MFMA fragments are int4 only
-    const unsigned grid = grid_for(max_chunks * (a.inter / 128), 2 * n_cu);
-    if (a.lay.group == 64) launch(grouped_kernel<true, 64>, grid, 256, 0, s, a);
-    else launch(grouped_kernel<true, 32>, grid, 256, 0, s, a);
-    return hipGetLastError();
+    return launch_grouped<true>(a, max_chunks, n_cu, s);
 }
 
 hipError_t launch_grouped_down(const FwdArgs &a, int max_chunks, int n_cu, hipStream_t s) {
-    if (a.lay.bits != 4) return hipErrorInvalidValue;
-    const unsigned grid = grid_for(max_chunks * ((a.hidden + 255) / 256), 2 * n_cu);
-    if (a.lay.group == 64) launch(grouped_kernel<false, 64>, grid, 256, 0, s, a);
-    else launch(grouped_kernel<false, 32>, grid, 256, 0, s, a);
-    return hipGetLastError();
+    return launch_grouped<false>(a, max_chunks, n_cu, s);
 }
 
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s) {

@@ -57,6 +57,12 @@ constexpr int scale_row_bytes() { return (kChunkK / G) * 2; }
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kChunkRows = 160;     // rows per grouped work chunk: five 32-row MFMA tiles
+// Calls of at most kSmallChunkMaxTok tokens cut chunks at one tile (most
+// experts then have a few rows each): the grouped kernel instance for them
+// needs a fifth of the LDS and registers, so twice as many workgroups fit.
+constexpr int kSmallChunkRows = 32;
+constexpr int kSmallChunkMaxTok = 64;
+inline int chunk_rows_for(int n_tok) { return n_tok <= kSmallChunkMaxTok ? kSmallChunkRows : kChunkRows; }
 
 struct BlobLayout {
     size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
@@ -95,6 +101,7 @@ struct FwdArgs {
     int zero_row_x, zero_row_h;     // rows of xh and h holding zeros: the padding rows' A operand
     float *y;                       // [n_tok x H]
     const ChunkDesc *chunks;        // grouped path work list
+    int chunk_rows;                 // grouped path: kChunkRows or kSmallChunkRows (chunk_rows_for)
     const int32_t *n_chunks;
     int32_t *queues;                // grouped path: kQueueInts counters, zero at rest
     int skip_shared;                // gate/up: the shared unit was already done
@@ -198,7 +205,9 @@ constexpr int kGroupedQueues = 8;
 constexpr int kQueueStride = 64;
 constexpr int kQueueInts = (kGroupedQueues + 1) * kQueueStride;
 
-// Upper bound on grouped work chunks for n_tok tokens.
-int max_work_chunks(int n_tok, int k, int n_experts, int has_shared);
+// Upper bound on grouped work chunks for n_tok tokens cut at chunk_rows.
+int max_work_chunks(int n_tok, int k, int n_experts, int has_shared, int chunk_rows);
+// Work-list capacity a layer of max_tokens needs (either chunk size).
+int work_list_capacity(int max_tokens, int k, int n_experts, int has_shared);
 
 }  // namespace coli

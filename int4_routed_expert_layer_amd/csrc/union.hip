@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kUT) void union_scatter_kernel(
 }
 
 // Work chunks for the grouped GEMMs: each union expert (and the shared
-// expert, placed after them) is cut into runs of at most kChunkRows rows.
+// expert, placed after them) is cut into runs of at most a.chunk_rows rows.
 __global__ __launch_bounds__(kThreads) void plan_kernel(FwdArgs a,
                                                         ChunkDesc *__restrict__ chunks,
                                                         int32_t *__restrict__ n_chunks) {
@@ -155,14 +155,15 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(FwdArgs a,
         m = a.n_tok;
         row0 = a.n_tok * a.k;
     }
-    const int nch = (m + kChunkRows - 1) / kChunkRows;
+    const int cr = a.chunk_rows;
+    const int nch = (m + cr - 1) / cr;
     int total = 0;
     const int first = dev::block_exclusive_scan<kThreads>(nch, s_tmp, &total);
     for (int c = 0; c < nch; ++c) {
         ChunkDesc d;
         d.expert = e;
-        d.row0 = row0 + c * kChunkRows;
-        d.rows = min(kChunkRows, m - c * kChunkRows);
+        d.row0 = row0 + c * cr;
+        d.rows = min(cr, m - c * cr);
         d.pad = 0;
         chunks[first + c] = d;
     }
@@ -206,10 +207,16 @@ hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
     return hipGetLastError();
 }
 
-int max_work_chunks(int n_tok, int k, int n_experts, int has_shared) {
+int max_work_chunks(int n_tok, int k, int n_experts, int has_shared, int chunk_rows) {
     const int rows = n_tok * k + (has_shared ? n_tok : 0);
     const int experts = (n_tok * k < n_experts ? n_tok * k : n_experts) + (has_shared ? 1 : 0);
-    return rows / kChunkRows + experts + 1;
+    return rows / chunk_rows + experts + 1;
+}
+
+int work_list_capacity(int max_tokens, int k, int n_experts, int has_shared) {
+    const int small = max_tokens < kSmallChunkMaxTok ? max_tokens : kSmallChunkMaxTok;
+    return std::max(max_work_chunks(max_tokens, k, n_experts, has_shared, chunk_rows_for(max_tokens)),
+                    max_work_chunks(small, k, n_experts, has_shared, kSmallChunkRows));
 }
 
 }  // namespace coli

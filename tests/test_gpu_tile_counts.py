@@ -7,6 +7,12 @@ MFMA tiles, so these counts reach every tile count (1, 1, 2, 3, 4, 5), the
 for the 330-token shared expert, 160 + 160 + 10.  Every token's output is
 compared with the oracle, at group sizes 32 and 64, on both strategies;
 routing and the union bit for bit, through the C ABI.
+
+Calls of at most 64 tokens cut chunks at 32 rows instead (a separate kernel
+instance): a second plant of 64 tokens with counts 1, 31, 32, 33, 63 and 64
+reaches a one-row chunk, full and partial single tiles, the splits
+33 -> 32 + 1, 63 -> 32 + 31 and 64 -> 32 + 32, and the 64-row shared expert
+as two chunks.
 """
 import numpy as np
 import pytest
@@ -48,5 +54,28 @@ def test_every_tile_count_and_chunk_split(group, path):
     gpu = gpu_run(B, L, data)
     check_routing(gpu, ref)
     check_outputs(gpu["y"], oracle_y(data, ref, range(SPEC.n_tok)), f"planted g{group}/{path}")
+    assert L.device_errors() == 0
+    L.close()
+
+
+# Small calls: 8 experts, top-4, 64 tokens = 256 entries.
+SMALL_COUNTS = [1, 31, 32, 33, 63, 64, 16, 16]
+SMALL_SPEC = configs.Spec("tiles_small_h1024_i384_e8_k4_b64", 1024, 384, len(SMALL_COUNTS), 4, 64, "bf16", True,
+                          "gauss", seed=4343)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_small_call_chunks_of_one_tile(group):
+    spec = SMALL_SPEC.with_(group=group)
+    data = Data(spec)
+    sets = planted_routing(spec.n_experts, spec.top_k, SMALL_COUNTS, spec.n_tok, seed=13)
+    data.x, data.w = planted_inputs(spec, sets, seed=14)
+    log(f"case small-call planted counts group={group}")
+    ref = oracle_route(data)
+    np.testing.assert_array_equal(ref["counts"], SMALL_COUNTS)
+    L = make_layer(B, data, path=B.PATH_GROUPED)
+    gpu = gpu_run(B, L, data)
+    check_routing(gpu, ref)
+    check_outputs(gpu["y"], oracle_y(data, ref, range(spec.n_tok)), f"small planted g{group}")
     assert L.device_errors() == 0
     L.close()
