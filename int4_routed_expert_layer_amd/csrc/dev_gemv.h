@@ -518,7 +518,15 @@ __device__ __forceinline__ void down_math(const DownBuf<F> &b, const uint8_t *hs
     }
 }
 
-// Matrix-core form of down_math (see gateup_math_mfma).
+// Matrix-core form of down_math: each 32-column slice s of a chunk is one
+// v_mfma_f32_16x16x32_f16 whose B operand is the lane's unpacked dword s
+// (F::frag: weight row L & 15, columns 32 s + 8 (L >> 4) .. + 7, exactly the
+// chunk layout) and whose A operand is the staged h row of token L & 15
+// (rows past MAXM read token 0; their results are never used).  Lane L < 16
+// then holds token m's dot with weight row L in d[m]; adding the slice's
+// seed sum gives the slice's dot product (the quantity the four v_dot2
+// groups form, summed in another order), and the group scale is applied per
+// slice as in down_math.
 template <int MAXM, class F>
 __device__ __forceinline__ void down_math_mfma(const DownBuf<F> &b, const uint8_t *hs, const float *cs32, int I,
                                                int first, int count, int row, int kq, int mc, uint32_t M0,
