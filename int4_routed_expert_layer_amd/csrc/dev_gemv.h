@@ -259,10 +259,10 @@ __device__ __forceinline__ void gateup_load(GateUpBuf<NG, F> &b, const GateUpSrc
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + step * g, C - 1));
-        b.gw[g] = bload<uint4>(S.r, S.vq, S.gq + c * kChunkBytes);
-        b.uw[g] = bload<uint4>(S.r, S.vq, S.uq + c * kChunkBytes);
-        b.gs[g] = bload<typename F::Rec>(S.r, S.vs, S.gs + c * F::kScaleChunkBytes);
-        b.us[g] = bload<typename F::Rec>(S.r, S.vs, S.us + c * F::kScaleChunkBytes);
+        b.gw[g] = bload<uint4, kLoadStream>(S.r, S.vq, S.gq + c * kChunkBytes);
+        b.uw[g] = bload<uint4, kLoadStream>(S.r, S.vq, S.uq + c * kChunkBytes);
+        b.gs[g] = bload<typename F::Rec, kLoadStream>(S.r, S.vs, S.gs + c * F::kScaleChunkBytes);
+        b.us[g] = bload<typename F::Rec, kLoadStream>(S.r, S.vs, S.us + c * F::kScaleChunkBytes);
     }
 }
 
@@ -486,8 +486,8 @@ __device__ __forceinline__ void down_load(DownBuf<F> &b, rsrc_t r, uint32_t vq, 
 #pragma unroll
     for (int g = 0; g < kPipeGroup; ++g) {
         const uint32_t c = static_cast<uint32_t>(min(first + g, C - 1));
-        b.w[g] = bload<uint4>(r, vq, sq + c * kChunkBytes);
-        b.s[g] = bload<typename F::Rec>(r, vs, ss + c * F::kScaleChunkBytes);
+        b.w[g] = bload<uint4, kLoadStream>(r, vq, sq + c * kChunkBytes);
+        b.s[g] = bload<typename F::Rec, kLoadStream>(r, vs, ss + c * F::kScaleChunkBytes);
     }
 }
 
