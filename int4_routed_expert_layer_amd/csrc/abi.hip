@@ -971,16 +971,26 @@ coli_status coli_moe_route(coli_layer *L, const void *x, int32_t n_tok, int32_t 
     return COLI_OK;
 }
 
-coli_status coli_moe_union(coli_layer *L, const int32_t *topk_idx, int32_t n_tok, int32_t *n_union,
-                           int32_t *union_ids, int32_t *counts, int32_t *offsets, int32_t *gather,
-                           void *stream) {
-    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
-    coli_status st = check_tokens(L, n_tok);
-    if (st != COLI_OK) return st;
-    if (!n_union || !union_ids || !counts || !offsets || (n_tok > 0 && (!topk_idx || !gather)))
-        return fail(L, COLI_E_INVALID, "NULL device pointer");
-    DeviceGuard guard(L->device);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// The union of a call.  Up to kUnionSmallEntries entries it is one launch;
+// with `work` (the arguments of the forward that follows, grouped strategy)
+// that launch also writes the work list and the fp16 copy of x, and
+// *planned says so.
+coli_status union_impl(coli_layer *L, const int32_t *topk_idx, int32_t n_tok, int32_t *n_union,
+                       int32_t *union_ids, int32_t *counts, int32_t *offsets, int32_t *gather, hipStream_t s,
+                       const FwdArgs *work, bool *planned) {
+    if (planned) *planned = false;
+    if (n_tok > 0 && n_tok * L->d.top_k <= kUnionSmallEntries) {
+        KernelMark m(L, COLI_K_UNION, s);
+        FwdArgs a{};
+        if (work) a = *work;
+        a.err = L->err;
+        HIP_TRY(L, launch_union_small(topk_idx, n_tok, L->d.top_k, L->d.n_experts, n_union, union_ids, counts,
+                                      offsets, gather, a, work ? L->chunks : nullptr, work ? L->n_chunks : nullptr,
+                                      s),
+                "union launch");
+        if (planned) *planned = work != nullptr;
+        return COLI_OK;
+    }
     const UnionScratch ws{L->union_blk, L->union_blk + kUnionMaxBlocks * L->d.n_experts, L->union_rank};
     {
         KernelMark m(L, COLI_K_UNION, s);
@@ -994,20 +1004,26 @@ coli_status coli_moe_union(coli_layer *L, const int32_t *topk_idx, int32_t n_tok
     return COLI_OK;
 }
 
-coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const int32_t *topk_idx,
-                             const float *topk_w, const int32_t *n_union, const int32_t *union_ids,
-                             const int32_t *counts, const int32_t *offsets, const int32_t *gather, float *y,
-                             void *stream) {
+coli_status coli_moe_union(coli_layer *L, const int32_t *topk_idx, int32_t n_tok, int32_t *n_union,
+                           int32_t *union_ids, int32_t *counts, int32_t *offsets, int32_t *gather,
+                           void *stream) {
     if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
     coli_status st = check_tokens(L, n_tok);
     if (st != COLI_OK) return st;
-    if (n_tok == 0) return COLI_OK;
-    if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
+    if (!n_union || !union_ids || !counts || !offsets || (n_tok > 0 && (!topk_idx || !gather)))
         return fail(L, COLI_E_INVALID, "NULL device pointer");
-    if (L->d.has_shared && L->experts[L->d.n_experts].tier != COLI_TIER_VRAM)
-        return fail(L, COLI_E_STATE, "shared expert not placed");
     DeviceGuard guard(L->device);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return union_impl(L, topk_idx, n_tok, n_union, union_ids, counts, offsets, gather,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+// The expert FFNs and the combine of one call whose routing and union are
+// already on the device.  `planned`: the union launch also wrote the grouped
+// work list and the fp16 copy of x (union_impl with a work list).
+coli_status forward_impl(coli_layer *L, const void *x, int32_t n_tok, const float *topk_w,
+                         const int32_t *n_union, const int32_t *union_ids, const int32_t *counts,
+                         const int32_t *offsets, const int32_t *gather, float *y, hipStream_t s, bool planned) {
+    coli_status st = COLI_OK;
     const int path = choose_path(L, n_tok);
 
     FwdArgs a = make_args(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y);
@@ -1045,7 +1061,7 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
     const int n_batches = n_hit_batches + (static_cast<int>(misses.size()) + kBatchExperts - 1) / kBatchExperts;
     if (!streamed.empty() && (st = ensure_stream_resources(L, n_batches)) != COLI_OK) return st;
 
-    if (path == COLI_PATH_GROUPED) {
+    if (path == COLI_PATH_GROUPED && !planned) {
         {
             KernelMark m(L, COLI_K_PLAN, s);
             HIP_TRY(L, launch_plan(a, L->chunks, L->n_chunks, s), "plan launch");
@@ -1140,6 +1156,23 @@ coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const 
     return COLI_OK;
 }
 
+coli_status coli_moe_forward(coli_layer *L, const void *x, int32_t n_tok, const int32_t *topk_idx,
+                             const float *topk_w, const int32_t *n_union, const int32_t *union_ids,
+                             const int32_t *counts, const int32_t *offsets, const int32_t *gather, float *y,
+                             void *stream) {
+    if (!L) return fail(nullptr, COLI_E_INVALID, "layer is NULL");
+    coli_status st = check_tokens(L, n_tok);
+    if (st != COLI_OK) return st;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
+        return fail(L, COLI_E_INVALID, "NULL device pointer");
+    if (L->d.has_shared && L->experts[L->d.n_experts].tier != COLI_TIER_VRAM)
+        return fail(L, COLI_E_STATE, "shared expert not placed");
+    DeviceGuard guard(L->device);
+    return forward_impl(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y,
+                        static_cast<hipStream_t>(stream), false);
+}
+
 coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t *topk_idx, float *topk_w,
                            int32_t *n_union, int32_t *union_ids, int32_t *counts, int32_t *offsets,
                            int32_t *gather, float *y, void *stream) {
@@ -1150,11 +1183,19 @@ coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t 
     if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
         return fail(L, COLI_E_INVALID, "NULL device pointer");
     if (!fused_path(L, n_tok)) {
+        if (L->d.has_shared && L->experts[L->d.n_experts].tier != COLI_TIER_VRAM)
+            return fail(L, COLI_E_STATE, "shared expert not placed");
         if ((st = coli_moe_route(L, x, n_tok, topk_idx, topk_w, stream)) != COLI_OK) return st;
-        if ((st = coli_moe_union(L, topk_idx, n_tok, n_union, union_ids, counts, offsets, gather, stream)) != COLI_OK)
+        DeviceGuard guard(L->device);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        // A grouped call hands its work list and fp16 copy to the union launch.
+        const FwdArgs work = make_args(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y);
+        const bool grouped = choose_path(L, n_tok) == COLI_PATH_GROUPED;
+        bool planned = false;
+        if ((st = union_impl(L, topk_idx, n_tok, n_union, union_ids, counts, offsets, gather, s,
+                             grouped ? &work : nullptr, &planned)) != COLI_OK)
             return st;
-        return coli_moe_forward(L, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
-                                stream);
+        return forward_impl(L, x, n_tok, topk_w, n_union, union_ids, counts, offsets, gather, y, s, planned);
     }
     DeviceGuard guard(L->device);
     const FusedScratch w{L->logits, L->h, L->ys, L->sync_counters,

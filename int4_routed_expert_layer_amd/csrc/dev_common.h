@@ -91,6 +91,39 @@ __device__ __forceinline__ void flag_if(bool bad, int32_t *err, int32_t bit) {
         __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// fp16 copy of the 8 activations x[8i .. 8i+7] (bf16 or fp32) into xh, the A
+// operand of the grouped gate/up GEMM; values outside the fp16 range set a
+// device error flag.  Threads with i >= n8 do nothing.
+__device__ __forceinline__ void to_half8(const void *x, int act_bf16, size_t i, size_t n8, _Float16 *xh,
+                                         int32_t *err) {
+    if (i >= n8) return;
+    typedef _Float16 half8x __attribute__((ext_vector_type(8)));
+    float v[8];
+    if (act_bf16) {
+        const uint4 raw = reinterpret_cast<const uint4 *>(x)[i];
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float((w4[j] & 0xFFFFu) << 16);
+            v[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 lo = reinterpret_cast<const float4 *>(x)[2 * i];
+        const float4 hi = reinterpret_cast<const float4 *>(x)[2 * i + 1];
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    }
+    half8x h;
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        h[j] = static_cast<_Float16>(v[j]);
+        bad = bad || outside_half(v[j]);
+    }
+    reinterpret_cast<half8x *>(xh)[i] = h;
+    flag_if(bad, err, kErrActRange);
+}
+
 // Wave index as a scalar (uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
 

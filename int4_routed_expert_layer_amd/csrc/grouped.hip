@@ -53,10 +53,6 @@ constexpr int stage_bytes() { return CR * kStageRowBytes; }  // 20 KB or 4 KB
 template <int CR>
 constexpr int blocks_per_cu() { return CR == kSmallChunkRows ? 4 : 2; }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
-    return __uint_as_float(b16 << 16);
-}
-
 // Keeps a constant in a VGPR so the compiler can use three-operand
 // v_and_or_b32 (VOP3 cannot encode literals on this ISA).
 __device__ __forceinline__ uint32_t vconst(uint32_t c) {
@@ -445,32 +441,7 @@ __global__ __launch_bounds__(256, blocks_per_cu<CR>()) void grouped_kernel(FwdAr
 // outside the fp16 range set a device error flag.
 __global__ __launch_bounds__(256) void to_half_kernel(const void *x, int act_bf16, size_t n8, _Float16 *xh,
                                                       int32_t *err) {
-    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= n8) return;
-    float v[8];
-    if (act_bf16) {
-        const uint4 raw = reinterpret_cast<const uint4 *>(x)[i];
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[2 * j] = bf16_bits_to_f32(w4[j] & 0xFFFFu);
-            v[2 * j + 1] = bf16_bits_to_f32(w4[j] >> 16);
-        }
-    } else {
-        const float4 lo = reinterpret_cast<const float4 *>(x)[2 * i];
-        const float4 hi = reinterpret_cast<const float4 *>(x)[2 * i + 1];
-        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    }
-    half8 h;
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        h[j] = static_cast<_Float16>(v[j]);
-        bad = bad || dev::outside_half(v[j]);
-    }
-    reinterpret_cast<half8 *>(xh)[i] = h;
-    dev::flag_if(bad, err, kErrActRange);
+    dev::to_half8(x, act_bf16, static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x, n8, xh, err);
 }
 
 // The per-entry rows are read exactly once, each by the instruction that

@@ -163,6 +163,16 @@ hipError_t launch_union_scatter(const int32_t *idx, int n_tok, int k, int n_expe
                                 const int32_t *offsets, int32_t *gather, hipStream_t s);
 hipError_t launch_plan(const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks,
                        hipStream_t s);
+// Up to kUnionSmallEntries entries (n_tok * k): the union in one launch of
+// one workgroup, the same outputs as rank + scatter.  With chunks non-NULL
+// the launch also writes the grouped work list (as launch_plan) and the fp16
+// copy of a.x (as launch_to_half); a carries a.err, and for the work list and
+// the copy n_tok, k, n_experts, has_shared, chunk_rows, x, act_bf16, hidden
+// and xh.
+constexpr int kUnionSmallEntries = 2048;
+hipError_t launch_union_small(const int32_t *idx, int n_tok, int k, int n_experts, int32_t *n_union,
+                              int32_t *union_ids, int32_t *counts, int32_t *offsets, int32_t *gather,
+                              const FwdArgs &a, ChunkDesc *chunks, int32_t *n_chunks, hipStream_t s);
 // gemv.hip.  gate/up covers units [u_begin, u_begin + u_count) (u_count < 0:
 // to the end).  down with non-NULL combine_counters ([H/32] ints, zero at
 // rest) also writes y and needs every unit to be computed in this launch;
