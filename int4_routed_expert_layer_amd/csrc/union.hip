@@ -19,6 +19,9 @@
 //    and each slab's per-expert base.
 //  * scatter: entry i of expert e in slab b goes to
 //    gather[offsets[e] + base[b][e] + rank[i]].
+// Up to 2048 entries the same ranking runs in a single workgroup and one
+// launch does everything (union_small_kernel), together with the grouped
+// work list and the fp16 copy of x when a layer call asks for them.
 // Everything is integer and every sum has a fixed order or is order-free, so
 // the results are exact and independent of scheduling.
 #include "dev_common.h"
