@@ -140,12 +140,13 @@ struct ItemState {
 // make that wait stricter).  Lookahead past the last step repeats the last
 // step's addresses (never used), so that count holds at every step; the loop
 // ends with a full wait before the stages are reused.
-template <bool GATEUP, int MT, int GS, int CR>
+template <bool GATEUP, int MT, int GS, int CR, bool TAIL>
 __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, const uint8_t *s_a,
                                          uint32_t sa_lds, const int *s_ent, const float *s_w) {
     const int H = a.hidden, I = a.inter;
     const int wave = dev::wave_id(), lane = threadIdx.x & 63;
     const int l31 = lane & 31, lh = lane >> 5;
+    constexpr int kCopies = MT + (TAIL ? 1 : 0);   // 8-row copies per wave and step
     struct B64 {
         uint2 qe[2], qo[2];
         uint32_t sc[2];
@@ -154,7 +155,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
         const int cc = min(c, st.C2 - 1);
         const uint32_t dst = sa_lds + static_cast<uint32_t>(c % kStages) * stage_bytes<CR>();
 #pragma unroll
-        for (int j = 0; j < MT; ++j)
+        for (int j = 0; j < kCopies; ++j)
             dev::copy16_to_lds(st.asrc + st.src_off[j] + cc * kStepK,
                           dst + static_cast<uint32_t>(8 * (wave + 4 * j) * kStageRowBytes));
         asm volatile("" ::: "memory");
@@ -179,6 +180,13 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
+    // The 16-row tail tile (rows 32 MT .. 32 MT + 15): per B tile nt, its two
+    // 16-column halves hi as 16x16 accumulators.
+    floatx4 acct[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) acct[nt][hi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
 
@@ -199,7 +207,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     auto compute = [&](int c, const B64 &f) {
         if (c >= st.C2) return;
         const uint8_t *tile = s_a + (c % kStages) * stage_bytes<CR>();
-        half8 av[MT], bc[2];
+        half8 av[MT], bc[2], bprev[2];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             av[mt] = *reinterpret_cast<const half8 *>(tile + lds_unit(mt * 32 + l31, lh));
@@ -225,6 +233,38 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
             // MFMA occupies the matrix pipe.
             interleave<0, 2 * MT, 26 / (2 * MT) + 1>();
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (TAIL) {
+                if (t & 1) {
+                    // 32-column slice t / 2 on v_mfma_f32_16x16x32_f16.  Its B
+                    // fragments are the 32x32x16 fragments of slices t - 1 and
+                    // t with their 16-lane rows regrouped: (row r of slice
+                    // t - 1, ...) -> [X0 X2 Y0 Y2] for columns 0-15 and
+                    // [X1 X3 Y1 Y3] for 16-31, two lane swaps per dword.
+                    const half8 at = *reinterpret_cast<const half8 *>(
+                        tile + lds_unit(MT * 32 + (lane & 15), 4 * (t >> 1) + (lane >> 4)));
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const uint4 x = __builtin_bit_cast(uint4, bprev[nt]);
+                        const uint4 y = __builtin_bit_cast(uint4, bc[nt]);
+                        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+                        uint32_t f0[4], f1[4];
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const auto p32 = __builtin_amdgcn_permlane32_swap(xs[d], ys[d], false, false);
+                            const auto p16 = __builtin_amdgcn_permlane16_swap(p32[0], p32[1], false, false);
+                            f0[d] = p16[0];
+                            f1[d] = p16[1];
+                        }
+                        const half8 h0 = __builtin_bit_cast(half8, uint4{f0[0], f0[1], f0[2], f0[3]});
+                        const half8 h1 = __builtin_bit_cast(half8, uint4{f1[0], f1[1], f1[2], f1[3]});
+                        acct[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(at, h0, acct[nt][0], 0, 0, 0);
+                        acct[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(at, h1, acct[nt][1], 0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) bprev[nt] = bc[nt];
+                }
+            }
             if (t + 1 < 4) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) av[mt] = an[mt];
@@ -237,7 +277,7 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
         // A plain barrier, not __syncthreads: its release fence would wait
         // for every load in flight, which is the lookahead itself.  LDS reads
         // of the previous step are complete (lgkmcnt) before any wave passes.
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(6 + (kAhead - 1) * (MT + 6)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(6 + (kAhead - 1) * (kCopies + 6)) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         issue(c + kAhead, ahead);
@@ -290,6 +330,32 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
                     for (int nt = 0; nt < 2; ++nt)
                         if (st.bvalid[nt]) yrow[nt * 32] = wgt[i] * acc[mt][nt][i0 + i];
                 }
+            }
+        }
+    }
+    if constexpr (TAIL) {
+        // The 16x16 tiles: lane L holds D[m = 32 MT + 4 (L / 16) + i][n = L % 16]
+        // of column half hi of B tile nt.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = MT * 32 + 4 * (lane >> 4) + i;
+            if (GATEUP) {
+                const int r = m < st.rows ? st.row0 + m : a.discard_row;
+#pragma unroll
+                for (int hi = 0; hi < 2; ++hi) {
+                    const int col = st.nb * 128 + wave * 32 + 16 * hi + (lane & 15);
+                    const _Float16 hh = static_cast<_Float16>(dev::swiglu(acct[0][hi][i], acct[1][hi][i]));
+                    hbad = hbad || dev::half_nonfinite(hh);
+                    a.h[static_cast<size_t>(r) * I + col] = hh;
+                }
+            } else {
+                float *yrow = a.ys + static_cast<size_t>(s_ent[m]) * H + st.nb * 256 + wave * 64 + (lane & 15);
+                const float wgt = s_w[m];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int hi = 0; hi < 2; ++hi)
+                        if (st.bvalid[nt]) yrow[nt * 32 + 16 * hi] = wgt * acct[nt][hi][i];
             }
         }
     }
@@ -421,14 +487,24 @@ __global__ __launch_bounds__(256, blocks_per_cu<CR>()) void grouped_kernel(FwdAr
             st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
         }
         if constexpr (CR == kSmallChunkRows) {
-            run_item<GATEUP, 1, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w);
+            run_item<GATEUP, 1, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w);
+        } else if (mt >= 2 && d.rows - 32 * (mt - 1) <= 16) {
+            // The last tile would hold 16 rows or fewer: a 16-row tile on
+            // v_mfma_f32_16x16x32_f16 instead of a 32-row one (half the MFMA
+            // work of that tile).
+            switch (mt) {
+                case 5: run_item<GATEUP, 4, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 4: run_item<GATEUP, 3, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 3: run_item<GATEUP, 2, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                default: run_item<GATEUP, 1, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            }
         } else {
             switch (mt) {
-                case 5: run_item<GATEUP, 5, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 4: run_item<GATEUP, 4, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 3: run_item<GATEUP, 3, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 2: run_item<GATEUP, 2, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                default: run_item<GATEUP, 1, GS, CR>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 5: run_item<GATEUP, 5, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 4: run_item<GATEUP, 4, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 3: run_item<GATEUP, 3, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                case 2: run_item<GATEUP, 2, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                default: run_item<GATEUP, 1, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
             }
         }
     }

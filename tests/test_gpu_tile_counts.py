@@ -8,6 +8,14 @@ for the 330-token shared expert, 160 + 160 + 10.  Every token's output is
 compared with the oracle, at group sizes 32 and 64, on both strategies;
 routing and the union bit for bit, through the C ABI.
 
+A chunk whose last 32-row tile would hold 16 rows or fewer ends in a 16-row
+tile on v_mfma_f32_16x16x32_f16 instead; a third plant of 200 tokens with
+counts 48, 49, 65, 80, 129, 144, 16, 17, 1, 33 and 109 reaches that tail
+after one to four full tiles (33, 48, 65, 80, 97-112, 129, 144), its
+boundary (48 ends in a 16-row tail, 49 in a full tile) and chunks without
+one (16, 17, 1); the 200-token shared expert is 160 + 40 rows (a tail after
+one tile).
+
 Calls of at most 64 tokens cut chunks at 32 rows instead (a separate kernel
 instance): a second plant of 64 tokens with counts 1, 31, 32, 33, 63 and 64
 reaches a one-row chunk, full and partial single tiles, the splits
@@ -77,5 +85,28 @@ def test_small_call_chunks_of_one_tile(group):
     gpu = gpu_run(B, L, data)
     check_routing(gpu, ref)
     check_outputs(gpu["y"], oracle_y(data, ref, range(spec.n_tok)), f"small planted g{group}")
+    assert L.device_errors() == 0
+    L.close()
+
+
+# Tail tiles: 12 experts, top-4, 200 tokens = 800 entries.
+TAIL_COUNTS = [48, 49, 65, 80, 129, 144, 16, 17, 1, 33, 109, 109]
+TAIL_SPEC = configs.Spec("tiles_tail_h1024_i384_e12_k4_b200", 1024, 384, len(TAIL_COUNTS), 4, 200, "bf16", True,
+                         "gauss", seed=4444)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_tail_tiles_of_sixteen_rows(group):
+    spec = TAIL_SPEC.with_(group=group)
+    data = Data(spec)
+    sets = planted_routing(spec.n_experts, spec.top_k, TAIL_COUNTS, spec.n_tok, seed=15)
+    data.x, data.w = planted_inputs(spec, sets, seed=16)
+    log(f"case tail-tile planted counts group={group}")
+    ref = oracle_route(data)
+    np.testing.assert_array_equal(ref["counts"], TAIL_COUNTS)
+    L = make_layer(B, data, path=B.PATH_GROUPED)
+    gpu = gpu_run(B, L, data)
+    check_routing(gpu, ref)
+    check_outputs(gpu["y"], oracle_y(data, ref, range(spec.n_tok)), f"tail planted g{group}")
     assert L.device_errors() == 0
     L.close()
