@@ -17,10 +17,10 @@ one (16, 17, 1); the 200-token shared expert is 160 + 40 rows (a tail after
 one tile).
 
 Calls of at most 64 tokens cut chunks at 32 rows instead (a separate kernel
-instance): a second plant of 64 tokens with counts 1, 31, 32, 33, 63 and 64
-reaches a one-row chunk, full and partial single tiles, the splits
-33 -> 32 + 1, 63 -> 32 + 31 and 64 -> 32 + 32, and the 64-row shared expert
-as two chunks.
+instance, one 32-row tile per chunk): a second plant of 64 tokens with
+counts 1, 31, 32, 33, 62, 64, 17 and 16 reaches chunks of 1, 16, 17, 30, 31
+and 32 rows, the splits 33 -> 32 + 1, 62 -> 32 + 30 and 64 -> 32 + 32, and
+the 64-row shared expert as two chunks.
 """
 import numpy as np
 import pytest
@@ -67,7 +67,7 @@ def test_every_tile_count_and_chunk_split(group, path):
 
 
 # Small calls: 8 experts, top-4, 64 tokens = 256 entries.
-SMALL_COUNTS = [1, 31, 32, 33, 63, 64, 16, 16]
+SMALL_COUNTS = [1, 31, 32, 33, 62, 64, 17, 16]
 SMALL_SPEC = configs.Spec("tiles_small_h1024_i384_e8_k4_b64", 1024, 384, len(SMALL_COUNTS), 4, 64, "bf16", True,
                           "gauss", seed=4343)
 
