@@ -20,7 +20,10 @@
 // between the MFMAs of the current one.  Each weight dword becomes eight fp16
 // weights: q = (1024 + u) - 1032 (exact) times the group's fp16 scale (one
 // rounding), so a fragment lies inside one scale group (32 or 64 wide) and
-// the MFMA accumulates in fp32.
+// the MFMA accumulates in fp32.  A chunk that would end in a 32-row tile of
+// 16 rows or fewer ends in a 16-row tile on v_mfma_f32_16x16x32_f16 instead,
+// fed by the same fragments regrouped across lanes; rows past a chunk's end
+// read a zeroed row.
 //   gate/up: A = gathered token rows (fp16 copy of x); each wave owns
 //            32 intermediate rows of both gate and up, so SwiGLU is applied
 //            in registers and h is stored as fp16.
@@ -123,7 +126,9 @@ struct ItemState {
 };
 
 // K loop and epilogue of one item on v_mfma_f32_32x32x16_f16 with MT 32-row
-// tiles of the chunk (rows past `rows` are padding, computed and discarded).
+// tiles of the chunk, and with TAIL a 16-row tile after them (rows 32 MT ..
+// 32 MT + 15) on v_mfma_f32_16x16x32_f16 (rows past `rows` are padding,
+// computed and discarded).
 //
 // B tile nt covers 32 weight rows = two 16-row panels.  For the 16-wide K
 // slice T of a 128-wide chunk, lane L needs rows n = L % 32, columns
@@ -135,9 +140,9 @@ struct ItemState {
 // L % 32 of the staged tile.
 //
 // Step c waits for its own copies with an explicit count: after them this
-// wave has issued exactly the B loads of step c (6) and the copies (MT) and B
-// loads (6) of steps c + 1 .. c + kAhead - 1 (other memory operations only
-// make that wait stricter).  Lookahead past the last step repeats the last
+// wave has issued exactly the B loads of step c (6) and the copies (MT, plus
+// one for the tail tile's rows) and B loads (6) of steps c + 1 .. c + kAhead
+// - 1 (other memory operations only make that wait stricter).  Lookahead past the last step repeats the last
 // step's addresses (never used), so that count holds at every step; the loop
 // ends with a full wait before the stages are reused.
 template <bool GATEUP, int MT, int GS, int CR, bool TAIL>
