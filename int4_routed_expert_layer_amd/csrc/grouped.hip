@@ -8,14 +8,17 @@
 // crossed with N-blocks; a persistent grid walks that list (the N-blocks of a
 // chunk, which share its activation rows, are queued on one XCD and its L2).
 //
-// Per item a 256-thread workgroup (two per CU; four with 32-row chunks, whose
-// stages and registers are smaller) walks the reduction axis in
+// Per item a 256-thread workgroup (two per CU) walks the reduction axis in
 // 64-column steps through a ring of three LDS stages: the chunk's fp16
 // activation rows of step c + 2 are copied straight from global memory into
 // LDS (global_load_lds; XOR-swizzled 16-byte units, conflict-free for the
 // fragment reads) and each wave's int4 weight fragments of step c + 2 are
 // loaded into registers (buffer loads, already in B-fragment order of
-// v_mfma_f32_32x32x16_f16) while step c is multiplied.  Inside a step the LDS
+// v_mfma_f32_32x32x16_f16) while step c is multiplied.  With 32-row chunks
+// (four workgroups per CU) a step is a whole 128-column chunk and the ring
+// has two stages: the weight slots are then read whole, by one load each
+// (the 64-column step reads each slot in two halves a step apart; measured at
+// 64 tokens, 128-column steps take both GEMMs 7-9% faster).  Inside a step the LDS
 // reads and the dequantisation of the next 16-column slice are interleaved
 // between the MFMAs of the current one.  Each weight dword becomes eight fp16
 // weights: q = (1024 + u) - 1032 (exact) times the group's fp16 scale (one
@@ -43,16 +46,23 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// The K loop advances 64 reduction columns per step through a ring of three
-// LDS stages of CR rows (the chunk size: 160 rows, two workgroups per CU, or
-// 32 rows for small calls, four per CU): the activation copy and the weight
-// loads of step c + 2 are issued while step c is multiplied.
+// The K loop of 160-row chunks (two workgroups per CU) advances 64 reduction
+// columns per step through a ring of three LDS stages: the activation copy
+// and the weight loads of step c + 2 are issued while step c is multiplied.
 constexpr int kStepK = 64;
 constexpr int kStageRowBytes = kStepK * 2;                  // one staged row: 64 fp16
 constexpr int kStages = 3;
 constexpr int kAhead = 2;                                   // steps issued ahead
 template <int CR>
-constexpr int stage_bytes() { return CR * kStageRowBytes; }  // 20 KB or 4 KB
+constexpr int stage_bytes() { return CR * kStageRowBytes; }  // 20 KB
+// The 32-row instance steps a whole 128-column chunk at a time (each 16-byte
+// weight slot is then read by one load), through a ring of two stages.
+constexpr int kSmallRowBytes = kChunkK * 2;                  // one staged row: 128 fp16
+constexpr int kSmallStages = 2;
+constexpr int kSmallAhead = kSmallStages - 1;
+constexpr int kSmallStageBytes = kSmallChunkRows * kSmallRowBytes;   // 8 KB
+template <int CR>
+constexpr int ring_bytes() { return CR == kSmallChunkRows ? kSmallStages * kSmallStageBytes : kStages * stage_bytes<CR>(); }
 template <int CR>
 constexpr int blocks_per_cu() { return CR == kSmallChunkRows ? 4 : 2; }
 
@@ -99,6 +109,9 @@ __device__ __forceinline__ int lds_swz(int m) { return (m >> 1) & 7; }
 __device__ __forceinline__ int lds_unit(int m, int q) {
     return m * kStageRowBytes + ((q ^ lds_swz(m)) << 4);
 }
+// The same for the 256-byte rows of the 32-row instance: a row spans all 64
+// banks, and physical unit q ^ (m & 15) spreads 16 rows over them.
+__device__ __forceinline__ int lds_unit256(int m, int q) { return m * kSmallRowBytes + ((q ^ (m & 15)) << 4); }
 
 // Scheduling groups for one slice: N times (one MFMA, on odd turns one LDS
 // read, V VALU instructions), so the reads and dequantisation of the next
@@ -122,8 +135,54 @@ struct ItemState {
     uint32_t qv_even, qv_odd, sv; // per-lane byte offsets of the B slots and scales
     uint32_t qoff[2], soff[2];   // this wave's two 32-row B tiles (uniform)
     bool bvalid[2];
-    int row0, rows, nb, C2;      // C2 = K / kStepK steps
+    int row0, rows, nb, C2;      // C2 = K steps (64 or 128 columns each)
 };
+
+// Stores 32-row tile mt of an item: lane L holds D[m = 8(i / 4) + 4(L / 32)
+// + i % 4][n = L % 32] of the tile's two 32-column B tiles.  gate/up: SwiGLU
+// of the gate (B tile 0) and up (1) values into h as fp16; down: times the
+// row's routing weight into its entry's output row.  Padding rows
+// (m >= rows) store into the discard row, so no store is predicated.
+template <bool GATEUP>
+__device__ __forceinline__ void store_tile(const FwdArgs &a, const ItemState &st, const floatx16 (&acc)[2], int mt,
+                                           const int *s_ent, const float *s_w, bool &hbad) {
+    const int H = a.hidden, I = a.inter;
+    const int wave = dev::wave_id(), lane = threadIdx.x & 63;
+    const int l31 = lane & 31, lh = lane >> 5;
+    if (GATEUP) {
+        const int col = st.nb * 128 + wave * 32 + l31;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = mt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+            const int r = m < st.rows ? st.row0 + m : a.discard_row;
+            const _Float16 hh = static_cast<_Float16>(dev::swiglu(acc[0][i], acc[1][i]));
+            hbad = hbad || dev::half_nonfinite(hh);
+            a.h[static_cast<size_t>(r) * I + col] = hh;
+        }
+    } else {
+        // The tile's output entries (the discard row for padding) and
+        // routing weights, read from LDS in one batch ahead of the stores.
+        const int col = st.nb * 256 + wave * 64 + l31;
+#pragma unroll
+        for (int i0 = 0; i0 < 16; i0 += 8) {
+            int ent[8];
+            float wgt[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int m = mt * 32 + 8 * ((i0 + i) >> 2) + 4 * lh + (i & 3);
+                ent[i] = s_ent[m];
+                wgt[i] = s_w[m];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float *yrow = a.ys + static_cast<size_t>(ent[i]) * H + col;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    if (st.bvalid[nt]) yrow[nt * 32] = wgt[i] * acc[nt][i0 + i];
+            }
+        }
+    }
+}
 
 // K loop and epilogue of one item on v_mfma_f32_32x32x16_f16 with MT 32-row
 // tiles of the chunk, and with TAIL a 16-row tile after them (rows 32 MT ..
@@ -298,46 +357,10 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue.  Lane holds D[m = 8(i / 4) + 4(L / 32) + i % 4][n = L % 32]
-    // of each 32x32 tile.  Padding rows (m >= rows) store into the discard
-    // row, so no store is predicated.
+    // Epilogue (see store_tile); padding rows store into the discard row.
     bool hbad = false;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        if (GATEUP) {
-            const int col = st.nb * 128 + wave * 32 + l31;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = mt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                const int r = m < st.rows ? st.row0 + m : a.discard_row;
-                const _Float16 hh = static_cast<_Float16>(dev::swiglu(acc[mt][0][i], acc[mt][1][i]));
-                hbad = hbad || dev::half_nonfinite(hh);
-                a.h[static_cast<size_t>(r) * I + col] = hh;
-            }
-        } else {
-            // The tile's output entries (the discard row for padding) and
-            // routing weights, read from LDS in one batch ahead of the stores.
-            const int col = st.nb * 256 + wave * 64 + l31;
-#pragma unroll
-            for (int i0 = 0; i0 < 16; i0 += 8) {
-                int ent[8];
-                float wgt[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int m = mt * 32 + 8 * ((i0 + i) >> 2) + 4 * lh + (i & 3);
-                    ent[i] = s_ent[m];
-                    wgt[i] = s_w[m];
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float *yrow = a.ys + static_cast<size_t>(ent[i]) * H + col;
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        if (st.bvalid[nt]) yrow[nt * 32] = wgt[i] * acc[mt][nt][i0 + i];
-                }
-            }
-        }
-    }
+    for (int mt = 0; mt < MT; ++mt) store_tile<GATEUP>(a, st, acc[mt], mt, s_ent, s_w, hbad);
     if constexpr (TAIL) {
         // The 16x16 tiles: lane L holds D[m = 32 MT + 4 (L / 16) + i][n = L % 16]
         // of column half hi of B tile nt.
@@ -367,10 +390,114 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
     if (GATEUP) dev::flag_if(hbad, a.err, kErrHiddenRange);
 }
 
+// K loop and epilogue of an item of the 32-row instance: one 32-row tile,
+// 128-column steps (eight 16-column slices each).  Slice T of chunk c takes
+// dword T / 2 of the even (T even) or odd slot of its lane (the mapping of
+// run_item) and the scale of group T / 2 (size 32) or T / 4 (size 64); a step
+// loads each lane's two 16-byte slots whole, and its scales (four or two per
+// row).  Step c waits for its copies with an explicit count: after them this
+// wave has issued the B loads of step c (6) and the copies (2) and B loads
+// (6) of steps c + 1 .. c + kSmallAhead - 1.
+template <bool GATEUP, int GS>
+__device__ __forceinline__ void run_item_small(const FwdArgs &a, const ItemState &st, const uint8_t *s_a,
+                                               uint32_t sa_lds, const int *s_ent, const float *s_w) {
+    const int wave = dev::wave_id(), lane = threadIdx.x & 63;
+    const int l31 = lane & 31, lh = lane >> 5;
+    struct B128 {
+        uint4 qe[2], qo[2];
+        uint32_t sc[2][GS == 32 ? 2 : 1];
+    };
+    auto issue = [&](int c, B128 &f) {
+        const int cc = min(c, st.C2 - 1);
+        const uint32_t dst = sa_lds + static_cast<uint32_t>(c % kSmallStages) * kSmallStageBytes;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            dev::copy16_to_lds(st.asrc + st.src_off[j] + cc * kChunkK,
+                               dst + static_cast<uint32_t>(4 * (wave + 4 * j) * kSmallRowBytes));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const uint32_t cq = st.qoff[nt] + static_cast<uint32_t>(cc) * kChunkBytes;
+            f.qe[nt] = dev::bload<uint4>(st.brs, st.qv_even, cq);
+            f.qo[nt] = dev::bload<uint4>(st.brs, st.qv_odd, cq);
+            const uint32_t cs = st.soff[nt] + static_cast<uint32_t>(cc) * scale_chunk_bytes<GS>();
+            if constexpr (GS == 32) {
+                const uint2 v = dev::bload<uint2>(st.brs, st.sv, cs);
+                f.sc[nt][0] = v.x;
+                f.sc[nt][1] = v.y;
+            } else {
+                f.sc[nt][0] = dev::bload<uint32_t>(st.brs, st.sv, cs);
+            }
+        }
+        asm volatile("" ::: "memory");
+    };
+
+    floatx16 acc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nt][i] = 0.0f;
+    const uint32_t M0 = vconst(0x000F000Fu), M1 = vconst(0x00F000F0u), G = vconst(0x64006400u);
+    auto bfrag = [&](const B128 &f, int T, int nt) {
+        const uint4 &q = (T & 1) ? f.qo[nt] : f.qe[nt];
+        const int d = T >> 1;
+        const uint32_t w = d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
+        const uint32_t sw = GS == 32 ? f.sc[nt][(T >> 2) & (GS == 32 ? 1 : 0)] : f.sc[nt][0];
+        const int sel = GS == 32 ? ((T >> 1) & 1) : (T >> 2);
+        const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sw >> (16 * sel)));
+        return dequant8(w, half2v{sh, sh}, M0, M1, G);
+    };
+    // The software pipeline of run_item over eight slices.
+    auto compute = [&](int c, const B128 &f) {
+        if (c >= st.C2) return;
+        const uint8_t *tile = s_a + (c % kSmallStages) * kSmallStageBytes;
+        half8 av = *reinterpret_cast<const half8 *>(tile + lds_unit256(l31, lh)), bc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) bc[nt] = bfrag(f, 0, nt);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            half8 an, bn[2];
+            if (t + 1 < 8) {
+                an = *reinterpret_cast<const half8 *>(tile + lds_unit256(l31, 2 * (t + 1) + lh));
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) bn[nt] = bfrag(f, t + 1, nt);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bc[nt], acc[nt], 0, 0, 0);
+            interleave<0, 2, 14>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < 8) {
+                av = an;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) bc[nt] = bn[nt];
+            }
+        }
+    };
+    auto step = [&](int c, const B128 &cur, B128 &ahead) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(6 + (kSmallAhead - 1) * 8) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(c + kSmallAhead, ahead);
+        compute(c, cur);
+    };
+    B128 b[kSmallStages];
+#pragma unroll
+    for (int i = 0; i < kSmallAhead; ++i) issue(i, b[i]);
+    for (int c = 0; c < st.C2; c += kSmallStages) {
+#pragma unroll
+        for (int i = 0; i < kSmallStages; ++i) step(c + i, b[i], b[(i + kSmallAhead) % kSmallStages]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bool hbad = false;
+    store_tile<GATEUP>(a, st, acc, 0, s_ent, s_w, hbad);
+    if (GATEUP) dev::flag_if(hbad, a.err, kErrHiddenRange);
+}
+
 template <bool GATEUP, int GS, int CR>
 __global__ __launch_bounds__(256, blocks_per_cu<CR>()) void grouped_kernel(FwdArgs a) {
     // Ring of A stages, CR rows x kStepK fp16 each.
-    __shared__ __align__(16) uint8_t s_a[kStages * stage_bytes<CR>()];
+    __shared__ __align__(16) uint8_t s_a[ring_bytes<CR>()];
     // LDS byte address of s_a (for the copies' M0).
     const uint32_t sa_lds = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)(&s_a[0])));
@@ -431,7 +558,7 @@ __global__ __launch_bounds__(256, blocks_per_cu<CR>()) void grouped_kernel(FwdAr
         st.row0 = d.row0;
         st.rows = d.rows;
         st.nb = nb;
-        st.C2 = K / kStepK;
+        st.C2 = CR == kSmallChunkRows ? K / kChunkK : K / kStepK;
         const int C = K / kChunkK;
         // 32-row tiles: 1 to CR / 32 (padding rows are computed and discarded).
         const int mt = (d.rows + 31) / 32;
@@ -485,31 +612,42 @@ __global__ __launch_bounds__(256, blocks_per_cu<CR>()) void grouped_kernel(FwdAr
         // wave cover the first mt*32 rows): lane L fills LDS unit L & 7 of row
         // m = 8 (wave + 4j) + L / 8 with logical unit (L & 7) ^ lds_swz(m).
         const size_t arow = GATEUP ? static_cast<size_t>(H) : static_cast<size_t>(I);
-#pragma unroll
-        for (int j = 0; j < CR / 32; ++j) {
-            const int m = 8 * (wave + 4 * j) + (lane >> 3);
-            const int q = (lane & 7) ^ lds_swz(m);
-            st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
-        }
         if constexpr (CR == kSmallChunkRows) {
-            run_item<GATEUP, 1, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w);
-        } else if (mt >= 2 && d.rows - 32 * (mt - 1) <= 16) {
-            // The last tile would hold 16 rows or fewer: a 16-row tile on
-            // v_mfma_f32_16x16x32_f16 instead of a 32-row one (half the MFMA
-            // work of that tile).
-            switch (mt) {
-                case 5: run_item<GATEUP, 4, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 4: run_item<GATEUP, 3, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 3: run_item<GATEUP, 2, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                default: run_item<GATEUP, 1, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+            // 256-byte rows: copy j of this wave stages rows 4 (wave + 4j) ..
+            // +3; lane L fills unit L & 15 of row 4 (wave + 4j) + L / 16 with
+            // logical unit (L & 15) ^ (m & 15).
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int m = 4 * (wave + 4 * j) + (lane >> 4);
+                const int q = (lane & 15) ^ (m & 15);
+                st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
             }
+            run_item_small<GATEUP, GS>(a, st, s_a, sa_lds, s_ent, s_w);
         } else {
-            switch (mt) {
-                case 5: run_item<GATEUP, 5, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 4: run_item<GATEUP, 4, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 3: run_item<GATEUP, 3, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                case 2: run_item<GATEUP, 2, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
-                default: run_item<GATEUP, 1, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+#pragma unroll
+            for (int j = 0; j < CR / 32; ++j) {
+                const int m = 8 * (wave + 4 * j) + (lane >> 3);
+                const int q = (lane & 7) ^ lds_swz(m);
+                st.src_off[j] = static_cast<uint32_t>(s_tok[m]) * static_cast<uint32_t>(arow) + 8 * q;
+            }
+            if (mt >= 2 && d.rows - 32 * (mt - 1) <= 16) {
+                // The last tile would hold 16 rows or fewer: a 16-row tile on
+                // v_mfma_f32_16x16x32_f16 instead of a 32-row one (half the MFMA
+                // work of that tile).
+                switch (mt) {
+                    case 5: run_item<GATEUP, 4, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    case 4: run_item<GATEUP, 3, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    case 3: run_item<GATEUP, 2, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    default: run_item<GATEUP, 1, GS, CR, true>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                }
+            } else {
+                switch (mt) {
+                    case 5: run_item<GATEUP, 5, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    case 4: run_item<GATEUP, 4, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    case 3: run_item<GATEUP, 3, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    case 2: run_item<GATEUP, 2, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                    default: run_item<GATEUP, 1, GS, CR, false>(a, st, s_a, sa_lds, s_ent, s_w); break;
+                }
             }
         }
     }
