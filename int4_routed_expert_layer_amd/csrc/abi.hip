@@ -322,6 +322,7 @@ struct coli_layer {
     int32_t *queues = nullptr;         // [kQueueInts] grouped work-queue counters, zero at rest
     int32_t *union_blk = nullptr;      // [kUnionMaxBlocks x E + 64]; counter at [kUnionMaxBlocks x E]
     int32_t *union_rank = nullptr;     // [max_tokens x k]
+    UnitDesc *units = nullptr;         // [E + 1] resolved units of the fused small-batch call
     uint8_t *pin_stage = nullptr;    // pinned staging for placement
 
     // tiered forward
@@ -501,7 +502,8 @@ size_t create_bytes(const coli_moe_dims *d) {
            sizeof(_Float16) * (rows + 2) * I + sizeof(_Float16) * (T + 1) * H + sizeof(float) * (rows + 1) * H +
            sizeof(ChunkDesc) * chunks + 2 * sizeof(int32_t) + sizeof(int32_t) * (1 + H / 32) +
            sizeof(int32_t) * kQueueInts + sizeof(int32_t) * (kUnionMaxBlocks * E + 64) + sizeof(int32_t) * T * k +
-           blob_layout(d->hidden, d->inter, d->group, d->weight_bits).total + sizeof(int32_t) * (E + 1);
+           blob_layout(d->hidden, d->inter, d->group, d->weight_bits).total + sizeof(int32_t) * (E + 1) +
+           sizeof(UnitDesc) * (E + 1);
 }
 
 bool all_routed_resident(const coli_layer *L) {
@@ -593,7 +595,7 @@ void free_layer(coli_layer *L) {
     for (auto p : L->dev_tables) dev_free(p);
     if (L->side) (void)hipStreamDestroy(L->side);
     void *ptrs[] = {L->wt, L->bias, L->table_dev, L->logits, L->h, L->xh, L->ys, L->chunks, L->n_chunks, L->err,
-                    L->sync_counters, L->queues, L->union_blk, L->union_rank};
+                    L->sync_counters, L->queues, L->union_blk, L->union_rank, L->units};
     for (void *p : ptrs) dev_free(p);
     host_free(L->pin_stage);
     host_free(L->pin_union);
@@ -642,14 +644,15 @@ coli_status ensure_stream_resources(coli_layer *L, int n_batches) {
 }
 
 // Scratch of one fused small-batch call: logits [n_tok x E], h and ys rows
-// (n_tok * k routed + n_tok shared + the discard row), and the arrival
-// counters [1 + H/32] (zero at rest).
+// (n_tok * k routed + n_tok shared + the discard row), the arrival counters
+// [1 + H/32] (zero at rest) and the unit descriptors [E + 1].
 struct FusedScratch {
     float *logits;
     _Float16 *h;
     float *ys;
     int32_t *counters;
     int discard_row;
+    UnitDesc *units;
 };
 
 // True when coli_moe_layer takes the fused small-batch path for n_tok.
@@ -686,6 +689,9 @@ coli_status run_fused(coli_layer *L, const FusedScratch &w, bool timed, const vo
     f.counter = w.counters;
     f.next_counters = w.counters + 1;
     f.n_next = L->d.hidden / 32;
+    f.units = w.units;
+    f.n_units = std::min(n_tok * L->d.top_k, L->d.n_experts) + (L->d.has_shared ? 1 : 0);
+    a.units = w.units;   // the expert launches read their units resolved
     coli_layer *Lt = timed ? L : nullptr;
     hipError_t e;
     {
@@ -811,6 +817,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->queues), sizeof(int32_t) * kQueueInts, "work-queue counters"},
         {reinterpret_cast<void **>(&L->union_blk), sizeof(int32_t) * (kUnionMaxBlocks * E + 64), "union slab counts"},
         {reinterpret_cast<void **>(&L->union_rank), sizeof(int32_t) * T * dims->top_k, "union ranks"},
+        {reinterpret_cast<void **>(&L->units), sizeof(UnitDesc) * (E + 1), "unit descriptors"},
     };
     for (auto &a : allocs) {
         if ((he = dev_alloc(a.p, a.n)) != hipSuccess) {
@@ -1199,7 +1206,7 @@ coli_status coli_moe_layer(coli_layer *L, const void *x, int32_t n_tok, int32_t 
     }
     DeviceGuard guard(L->device);
     const FusedScratch w{L->logits, L->h, L->ys, L->sync_counters,
-                         static_cast<int>(L->d.max_tokens) * (L->d.top_k + 1)};
+                         static_cast<int>(L->d.max_tokens) * (L->d.top_k + 1), L->units};
     return run_fused(L, w, true, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
                      static_cast<hipStream_t>(stream));
 }
@@ -1214,13 +1221,14 @@ coli_status coli_moe_layer_static(coli_layer *L, const void *x, int32_t n_tok, i
     if (!x || !topk_idx || !topk_w || !n_union || !union_ids || !counts || !offsets || !gather || !y)
         return fail(L, COLI_E_INVALID, "NULL device pointer");
     // Layout of this call in the static scratch: counters first (the same
-    // place for every call, zero at rest), then logits, h, ys.
+    // place for every call, zero at rest), then logits, h, ys, unit descriptors.
     const size_t H = static_cast<size_t>(L->d.hidden), I = static_cast<size_t>(L->d.inter);
     const size_t rows = static_cast<size_t>(n_tok) * (L->d.top_k + 1) + 1;   // + the discard row
     const size_t o_logits = align256(sizeof(int32_t) * (1 + H / 32));
     const size_t o_h = o_logits + align256(sizeof(float) * n_tok * L->d.n_experts);
     const size_t o_ys = o_h + align256(sizeof(_Float16) * rows * I);
-    const size_t need = o_ys + sizeof(float) * rows * H;
+    const size_t o_units = o_ys + align256(sizeof(float) * rows * H);
+    const size_t need = o_units + sizeof(UnitDesc) * (L->d.n_experts + 1);
     if (need > kStaticScratchBytes)
         return fail(L, COLI_E_UNSUPPORTED, "this call needs %zu bytes of static scratch; the maximum is %zu",
                     need, kStaticScratchBytes);
@@ -1234,7 +1242,7 @@ coli_status coli_moe_layer_static(coli_layer *L, const void *x, int32_t n_tok, i
     DeviceGuard guard(L->device);
     const FusedScratch w{reinterpret_cast<float *>(base + o_logits), reinterpret_cast<_Float16 *>(base + o_h),
                          reinterpret_cast<float *>(base + o_ys), reinterpret_cast<int32_t *>(base),
-                         static_cast<int>(rows) - 1};
+                         static_cast<int>(rows) - 1, reinterpret_cast<UnitDesc *>(base + o_units)};
     return run_fused(L, w, false, x, n_tok, topk_idx, topk_w, n_union, union_ids, counts, offsets, gather, y,
                      static_cast<hipStream_t>(stream));
 }

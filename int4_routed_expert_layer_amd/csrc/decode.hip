@@ -76,6 +76,20 @@ __device__ __forceinline__ void wave_router(const FwdArgs &a, const FrontArgs &f
     }
 }
 
+// Unit descriptors past the n_union routed units: the shared expert's (rows
+// n_tok k .. n_tok k + n_tok - 1 of the hidden buffer), then units past the
+// last one (m = -1) up to f.n_units.
+// tsh is the shared expert's blob (loaded early, off the selection's path).
+__device__ __forceinline__ void write_tail_units(const FwdArgs &a, const FrontArgs &f, int n_union,
+                                                 const uint8_t *tsh, int tid) {
+    if (!f.units) return;
+    for (int u = n_union + tid; u < f.n_units; u += kFrontThreads) {
+        const bool shared = u == n_union && a.has_shared;
+        f.units[u] = shared ? UnitDesc{tsh, a.n_tok * a.k, a.n_tok, a.n_experts, 0, 0}
+                            : UnitDesc{nullptr, 0, -1, 0, 0, 0};
+    }
+}
+
 // One token: top-k by ranks within waves and among the finalists, weights in
 // rank order; its union needs no scans, as the k selected experts are
 // distinct: expert e has count 1 if selected, offset = number of selected
@@ -87,6 +101,9 @@ __device__ void select_one_token(const FwdArgs &a, const FrontArgs &f) {
     __shared__ int s_sel[kMaxTopK];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int E = a.n_experts, k = a.k;
+    // Blob pointers for the unit descriptors, in flight with the logits.
+    const uint8_t *tbl = f.units && tid < E ? a.table[tid] : nullptr;
+    const uint8_t *tsh = f.units && a.has_shared ? a.table[E] : nullptr;
     const uint32_t low = 0xFFFFFFFFu - static_cast<uint32_t>(tid);
     uint64_t key = low;
     if (tid < E) key |= static_cast<uint64_t>(dev::float_key(dev::load_coherent(f.logits + tid))) << 32;
@@ -126,12 +143,14 @@ __device__ void select_one_token(const FwdArgs &a, const FrontArgs &f) {
         if (slot >= 0) {
             f.union_ids[below] = tid;
             f.gather[below] = slot;
+            if (f.units) f.units[below] = UnitDesc{tbl, below, 1, tid, 0, 0};
         }
     }
     if (tid == 0) {
         f.offsets[E] = k;
         *f.n_union = k;
     }
+    write_tail_units(a, f, k, tsh, tid);
 }
 
 // Two to kFrontMaxTok tokens: wave t selects token t's experts (lane l holds
@@ -146,6 +165,8 @@ __device__ void select_few_tokens(const FwdArgs &a, const FrontArgs &f) {
     constexpr int kEpl = kFrontMaxExperts / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.n_experts, k = a.k, n_tok = a.n_tok;
+    const uint8_t *tbl = f.units && tid < E ? a.table[tid] : nullptr;
+    const uint8_t *tsh = f.units && a.has_shared ? a.table[E] : nullptr;
     if (wave < n_tok) {
         const int t = wave;
         uint64_t key[kEpl];
@@ -200,12 +221,16 @@ __device__ void select_few_tokens(const FwdArgs &a, const FrontArgs &f) {
         f.counts[tid] = c;
         f.offsets[tid] = excl & 0xFFFF;
         s_off[tid] = excl & 0xFFFF;
-        if (c > 0) f.union_ids[excl >> 16] = tid;
+        if (c > 0) {
+            f.union_ids[excl >> 16] = tid;
+            if (f.units) f.units[excl >> 16] = UnitDesc{tbl, excl & 0xFFFF, c, tid, 0, 0};
+        }
     }
     if (tid == 0) {
         f.offsets[E] = total & 0xFFFF;
         *f.n_union = total >> 16;
     }
+    write_tail_units(a, f, total >> 16, tsh, tid);
     __syncthreads();
     if (tid < n_ent) {
         const int e = s_idx[tid];

@@ -166,11 +166,23 @@ __device__ __forceinline__ T ld_uniform(const T *p) {
 
 // Work unit u of a forward call: routed union entry (u < n_union) or the
 // shared expert (u == n_union), with its blob pointer.  Returns false when u
-// is past the last unit.  The loads come in two rounds, not four: the union
+// is past the last unit.  With a.units (a fused small-batch call) the unit
+// comes resolved; otherwise the loads come in two rounds, not four: the union
 // size and the union entry at u are read together (the entry speculatively,
 // at an in-range index), then the entry's offset, count and blob together.
 // u must be wave-uniform and the routing arrays written by earlier launches.
 __device__ __forceinline__ bool resolve(const FwdArgs &a, int u, int &e, int &r0, int &m, const uint8_t *&blob) {
+    if (a.units) {
+        // Resolved by the decode front: one round of scalar loads.
+        typedef int32_t int8v __attribute__((ext_vector_type(8)));
+        const UnitDesc d = __builtin_bit_cast(UnitDesc, ld_uniform(reinterpret_cast<const int8v *>(a.units + u)));
+        if (d.m < 0) return false;
+        e = d.e;
+        r0 = d.r0;
+        m = d.m;
+        blob = d.blob;
+        return true;
+    }
     const int E = a.n_experts;
     const int nu = ld_uniform(a.n_union);
     const int es = ld_uniform(a.union_ids + (u < E ? u : E - 1));

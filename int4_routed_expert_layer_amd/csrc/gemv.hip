@@ -11,21 +11,28 @@
 namespace coli {
 namespace {
 
-// Kernel arguments an item needs once its unit is known, fetched with the
-// first batch of argument loads: otherwise the compiler reads them after the
-// unit lookups, one more scalar round trip in front of the weight stream.
-__device__ __forceinline__ void fetch_args_early(const FwdArgs &a) {
-    asm volatile("" ::"s"(a.x), "s"(a.act_bf16), "s"(a.h), "s"(a.ys), "s"(a.err), "s"(a.skip_shared), "s"(a.lay.total),
-                 "s"(a.lay.gate_q), "s"(a.lay.up_q), "s"(a.lay.down_q), "s"(a.lay.gate_s), "s"(a.lay.up_s),
-                 "s"(a.lay.down_s));
+// Kernel arguments an item needs, fetched in one batch of argument loads
+// ahead of everything else: otherwise the compiler reads the ones the unit
+// index needs, waits, and reads the rest, one more scalar round trip in
+// front of the unit lookup and the weight stream.  `dim` (a.inter or
+// a.hidden) and `base` (a first unit, a kernel argument of its own) come back
+// through the same statement, so that the unit index computed from them
+// cannot be scheduled in front of the batch.
+__device__ __forceinline__ void fetch_args_early(const FwdArgs &a, int &dim, int &base) {
+    asm volatile("" : "+s"(dim), "+s"(base)
+                 : "s"(a.x), "s"(a.act_bf16), "s"(a.h), "s"(a.ys), "s"(a.err), "s"(a.skip_shared), "s"(a.lay.total),
+                   "s"(a.lay.gate_q), "s"(a.lay.up_q), "s"(a.lay.down_q), "s"(a.lay.gate_s), "s"(a.lay.up_s),
+                   "s"(a.lay.down_s), "s"(a.units), "s"(a.n_union), "s"(a.union_ids), "s"(a.offsets),
+                   "s"(a.counts), "s"(a.n_experts), "s"(a.has_shared));
 }
 
 template <class F, int MAXM>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int P = a.inter / kPanel;
+    int inter = a.inter;
+    fetch_args_early(a, inter, u_begin);
+    const int P = inter / kPanel;
     const int u = u_begin + blockIdx.x / P, p = blockIdx.x % P;
-    fetch_args_early(a);
     int e, r0, M;
     const uint8_t *blob;
     if (!dev::resolve(a, u, e, r0, M, blob)) return;
@@ -37,12 +44,13 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FwdArgs a, int u_begin
 template <class F, int MAXM, bool FUSED_COMBINE>
 __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *counters, int32_t *idle_counter) {
     extern __shared__ __align__(16) uint8_t lds[];
+    int hidden = a.hidden, u0 = 0;
+    fetch_args_early(a, hidden, u0);
+    const int PG = hidden / (2 * kPanel);
     // A counter of an earlier launch of this call (idle now) starts the next
     // call at zero even after calls that overlapped and raced on it.
     if (idle_counter && blockIdx.x == 0 && threadIdx.x == 0) dev::store_coherent(idle_counter, 0);
-    const int PG = a.hidden / (2 * kPanel);
-    const int u = blockIdx.x / PG, pg = blockIdx.x % PG;
-    fetch_args_early(a);
+    const int u = u0 + blockIdx.x / PG, pg = blockIdx.x % PG;
     int e, r0, M;
     const uint8_t *blob;
     if (!dev::resolve(a, u, e, r0, M, blob)) return;

@@ -82,6 +82,16 @@ struct ChunkDesc {
     int32_t pad;
 };
 
+// One work unit of a fused small-batch call, resolved by the decode front's
+// selection so that the expert launches after it read it in one scalar
+// round: the expert's blob, its first hidden-buffer row and row count, and
+// its id (E for the shared expert); m < 0 marks a unit past the last one.
+struct alignas(32) UnitDesc {
+    const uint8_t *blob;
+    int32_t r0, m, e, pad;
+    int64_t pad2;
+};
+
 struct FwdArgs {
     const void *x;                  // [n_tok x H] fp32 or bf16
     int act_bf16;
@@ -105,6 +115,7 @@ struct FwdArgs {
     const int32_t *n_chunks;
     int32_t *queues;                // grouped path: kQueueInts counters, zero at rest
     int skip_shared;                // gate/up: the shared unit was already done
+    const UnitDesc *units;          // resolved units (fused small-batch call), or NULL
     int32_t *err;                   // device error flags (kErr* bits), sticky until read
 };
 
@@ -199,6 +210,10 @@ struct FrontArgs {
     // the counters starts from zero again.
     int32_t *next_counters;
     int n_next;
+    // Resolved units for the expert launches that follow (n_units of them:
+    // the routed slots min(n_tok k, E) plus the shared unit), or NULL.
+    UnitDesc *units;
+    int n_units;
 };
 hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_lds, hipStream_t s);
 // grouped.hip
