@@ -232,14 +232,14 @@ coli_status coli_moe_layer(coli_layer *layer, const void *x, int32_t n_tok,
  * graph capture, tight serving loops, harnesses that forbid allocation):
  * the same arguments, outputs and bits as coli_moe_layer's fused small-batch
  * path, but its scratch (logits, h and per-entry output rows, arrival
- * counters) lives in one static device array of 8 MiB per GPU, set up by the
- * first coli_layer_create on that GPU and held until the process ends; the
- * call allocates nothing and creates no HIP objects (kernel timing is not
- * recorded).  Limits: the fused path only (1..4 tokens, n_experts <= 256,
- * every expert in VRAM, router set, GEMV strategy), else COLI_E_UNSUPPORTED;
- * a call needing more than 8 MiB of scratch, about
- * n_tok*(k+1)*(4*H + 2*I) bytes, is refused with COLI_E_UNSUPPORTED before
- * any device work.  Every layer on a GPU shares that GPU's array, so calls
+ * counters, unit descriptors) lives in one static device array of 8 MiB per
+ * GPU, set up by the first coli_layer_create on that GPU and held until the
+ * process ends; the call allocates nothing and creates no HIP objects
+ * (kernel timing is not recorded).  Limits: the fused path only (1..4
+ * tokens, n_experts <= 256, every expert in VRAM, router set, GEMV
+ * strategy), else COLI_E_UNSUPPORTED; a call needing more than 8 MiB of
+ * scratch, about n_tok*(k+1)*(4*H + 2*I) + 32*(n_experts+1) bytes, is
+ * refused with COLI_E_UNSUPPORTED before any device work.  Every layer on a GPU shares that GPU's array, so calls
  * that overlap in time on one GPU (any layers, any streams) race and give
  * undefined results; issue them in one stream order. */
 coli_status coli_moe_layer_static(coli_layer *layer, const void *x, int32_t n_tok,
