@@ -246,8 +246,8 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
     if (static_cast<int>(blockIdx.x) >= router_blocks) {
         const int p = blockIdx.x - router_blocks;
         // One block per CU here: a deeper load pipeline than the routed kernel.
-        dev::gateup_panel<F, NT, false, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
-                                                            a.n_tok, p, lds, dev::lds_address(lds));
+        dev::gateup_panel<F, NT, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
+                                                     a.n_tok, p, lds, dev::lds_address(lds));
         return;
     }
     if (blockIdx.x == 0 && f.next_counters)

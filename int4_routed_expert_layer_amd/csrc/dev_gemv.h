@@ -301,11 +301,11 @@ __device__ __forceinline__ void gateup_math(const GateUpBuf<NG, F> &b, const uin
 
 // One gate/up work item: rows 16p..16p+15 of expert blob `blob`, for the M
 // tokens of hidden-buffer rows r0..r0+M-1 (rows.token(row) names the token of
-// a row).  Writes h rows (fp16; device-coherent stores when COHERENT, for a
-// consumer in the same launch).  All 256 threads must call it (it
-// synchronises the workgroup).  NG chunks per register buffer (two buffers in
-// flight): more for few workgroups per CU.  F is the weight format (WFmt).
-template <class F, int MAXM, bool COHERENT = false, int NG = kGateUpGroup, class Rows>
+// a row).  Writes h rows (fp16), read by a later launch.  All 256 threads
+// must call it (it synchronises the workgroup).  NG chunks per register
+// buffer (two buffers in flight): more for few workgroups per CU.  F is the
+// weight format (WFmt).
+template <class F, int MAXM, int NG = kGateUpGroup, class Rows>
 __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int p,
                              uint8_t *lds, uint32_t lds_addr) {
     const int H = a.hidden, I = a.inter;
@@ -450,18 +450,11 @@ __device__ void gateup_panel(const FwdArgs &a, const Rows &rows, const uint8_t *
             }
             const _Float16 hh = static_cast<_Float16>(swiglu(g, v));
             hbad = half_nonfinite(hh);
-            _Float16 *dst = a.h + static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r;
-            if (COHERENT) store_coherent(dst, hh);
-            else *dst = hh;
+            a.h[static_cast<size_t>(r0 + mb + m) * I + p * kPanel + r] = hh;
         }
         flag_if(hbad, a.err, kErrHiddenRange);
     }
 }
-
-// Nothing to wait for.
-struct NoWait {
-    __device__ void operator()() const {}
-};
 
 // Rows of a forward call read straight from its routing arrays (kernels that
 // run after the routing kernels have finished).
@@ -557,13 +550,12 @@ __device__ __forceinline__ void down_math_mfma(const DownBuf<F> &b, const uint8_
 // half (w >> 1); the halves are summed through LDS in a fixed order.  Writes
 // ys row rows.entry(row) scaled by rows.weight(row) (the routing weight of a
 // routed row, 1 for a shared row).  With COHERENT, ys is written
-// device-coherently (a consumer in the same launch reads it); before_h()
-// runs, by all threads, after the first weight loads are issued and before h
-// is read (a wait for h's producers).  All 256 threads must call it.  F is
-// the weight format (WFmt).
-template <class F, int MAXM, bool COHERENT = false, class Rows, class BeforeH>
+// device-coherently (the fused combine's last arriver, in the same launch,
+// reads it).  h comes from an earlier launch.  All 256 threads must call it.
+// F is the weight format (WFmt).
+template <class F, int MAXM, bool COHERENT = false, class Rows>
 __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_t *blob, int r0, int M, int pg,
-                                uint8_t *lds, uint32_t lds_addr, const BeforeH &before_h) {
+                                uint8_t *lds, uint32_t lds_addr) {
     const int H = a.hidden, I = a.inter;
     const int C = I / F::kCols;
     const int tid = opaque_tid(), wave = wave_id(), lane = tid & 63;
@@ -602,7 +594,6 @@ __device__ void down_panelgroup(const FwdArgs &a, const Rows &rows, const uint8_
         };
         DownBuf<F> A, B;
         bool b_issued = false;
-        if (mb == 0) before_h();
         __syncthreads();                        // the previous row block is done with hs
         if ((I * 2) % 1024 == 0) {
             // h rows (fp16, from an earlier launch) are copied straight into

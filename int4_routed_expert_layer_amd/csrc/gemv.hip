@@ -55,8 +55,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FwdArgs a, int32_t *coun
     const uint8_t *blob;
     if (!dev::resolve(a, u, e, r0, M, blob)) return;
     if (blob && M > 0)
-        dev::down_panelgroup<F, MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::lds_address(lds),
-                                                  dev::NoWait{});
+        dev::down_panelgroup<F, MAXM, FUSED_COMBINE>(a, dev::PlainRows{a}, blob, r0, M, pg, lds, dev::lds_address(lds));
     if (FUSED_COMBINE) {
         const int units = *a.n_union + (a.has_shared ? 1 : 0);
         // The last workgroup of the panel pair reuses its (now idle) LDS.
