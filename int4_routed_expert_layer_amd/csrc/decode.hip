@@ -23,6 +23,12 @@ namespace {
 constexpr int kFrontThreads = 256;
 constexpr int kFrontMaxExperts = 256;
 constexpr int kFrontGateUpGroup = 4;   // shared gate/up chunks per register buffer
+// Tokens per shared gate/up block: three or four tokens are split over two
+// blocks per panel (two tokens each), which halves the per-block dot-product
+// work on the front's critical path; each token's arithmetic is the same as
+// in a four-token block.
+template <int NT>
+constexpr int front_shared_tokens() { return NT == 4 ? 2 : NT; }
 
 template <int NT, bool BF16>
 __device__ __forceinline__ void wave_router(const FwdArgs &a, const FrontArgs &f, int e) {
@@ -244,10 +250,14 @@ template <class F, int NT, bool BF16>
 __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, FrontArgs f, int router_blocks) {
     extern __shared__ __align__(16) uint8_t lds[];
     if (static_cast<int>(blockIdx.x) >= router_blocks) {
-        const int p = blockIdx.x - router_blocks;
+        constexpr int ST = front_shared_tokens<NT>();
+        const int P = a.inter / kPanel;
+        const int b = blockIdx.x - router_blocks, p = b % P, m0 = ST * (b / P);
+        const int m = min(ST, a.n_tok - m0);
         // One block per CU here: a deeper load pipeline than the routed kernel.
-        dev::gateup_panel<F, NT, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts], a.n_tok * a.k,
-                                                     a.n_tok, p, lds, dev::lds_address(lds));
+        if (m > 0)
+            dev::gateup_panel<F, ST, kFrontGateUpGroup>(a, dev::PlainRows{a}, a.table[a.n_experts],
+                                                         a.n_tok * a.k + m0, m, p, lds, dev::lds_address(lds));
         return;
     }
     if (blockIdx.x == 0 && f.next_counters)
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(kFrontThreads) void decode_front_kernel(FwdArgs a, 
 template <class F, int NT>
 hipError_t launch_t(const FwdArgs &a, const FrontArgs &f, size_t lds, hipStream_t s) {
     const int router_blocks = (a.n_experts + 3) / 4;
-    const int grid = router_blocks + (a.has_shared ? a.inter / kPanel : 0);
+    const int grid = router_blocks + (a.has_shared ? a.inter / kPanel * (NT / front_shared_tokens<NT>()) : 0);
     if (a.act_bf16)
         launch(decode_front_kernel<F, NT, true>, grid, kFrontThreads, lds, s, a, f, router_blocks);
     else
@@ -283,7 +293,7 @@ hipError_t launch_nt(const FwdArgs &a, const FrontArgs &f, int nt, size_t lds, h
 hipError_t launch_decode_front(const FwdArgs &a, const FrontArgs &f, size_t max_lds, hipStream_t s) {
     if (a.n_tok < 1 || a.n_tok > kFrontMaxTok || a.n_experts > kFrontMaxExperts) return hipErrorInvalidValue;
     const int nt = a.n_tok == 1 ? 1 : (a.n_tok == 2 ? 2 : 4);
-    const size_t lds = a.has_shared ? dev::gateup_lds_bytes(nt, a.hidden) : 0;
+    const size_t lds = a.has_shared ? dev::gateup_lds_bytes(nt == 4 ? front_shared_tokens<4>() : nt, a.hidden) : 0;
     if (lds > max_lds) return hipErrorInvalidValue;
     hipError_t e = hipSuccess;
     dev::dispatch_format(a.lay.group, a.lay.bits,
