@@ -75,8 +75,7 @@ int pick_maxm(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1); }
 
 template <class F>
 void launch_gateup_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStream_t s, int u_begin) {
-    if (maxm == 4) launch(gemv_gateup_kernel<F, 4>, grid, 256, lds, s, a, u_begin);
-    else if (maxm == 2) launch(gemv_gateup_kernel<F, 2>, grid, 256, lds, s, a, u_begin);
+    if (maxm == 2) launch(gemv_gateup_kernel<F, 2>, grid, 256, lds, s, a, u_begin);
     else launch(gemv_gateup_kernel<F, 1>, grid, 256, lds, s, a, u_begin);
 }
 
@@ -98,7 +97,13 @@ void launch_down_as(const FwdArgs &a, int maxm, int grid, size_t lds, hipStream_
 }  // namespace
 
 hipError_t launch_gemv_gateup(const FwdArgs &a, size_t max_lds, hipStream_t s, int u_begin, int u_count) {
-    int maxm = pick_maxm(a.n_tok);
+    // At most two tokens per pass: the staged rows of four tokens take 64 KB
+    // of LDS (two workgroups per CU), and with the experts of a small batch
+    // mostly chosen by one token each that costs more than the second pass
+    // over the weights of an expert that all four tokens chose (decode B=4:
+    // 167.5 -> 148 us with random routing; 97 -> 101 us when the four tokens
+    // route alike).  Each token's arithmetic is the same in either form.
+    int maxm = std::min(pick_maxm(a.n_tok), 2);
     while (maxm > 1 && dev::gateup_lds_bytes(maxm, a.hidden) > max_lds) maxm >>= 1;
     const size_t lds = dev::gateup_lds_bytes(maxm, a.hidden);
     if (lds > max_lds) return hipErrorInvalidValue;
