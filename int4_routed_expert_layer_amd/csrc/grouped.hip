@@ -395,9 +395,12 @@ __device__ __forceinline__ void run_item(const FwdArgs &a, const ItemState &st, 
 // dword T / 2 of the even (T even) or odd slot of its lane (the mapping of
 // run_item) and the scale of group T / 2 (size 32) or T / 4 (size 64); a step
 // loads each lane's two 16-byte slots whole, and its scales (four or two per
-// row).  Step c waits for its copies with an explicit count: after them this
-// wave has issued the B loads of step c (6) and the copies (2) and B loads
-// (6) of steps c + 1 .. c + kSmallAhead - 1.
+// row).  Each weight and scale byte is then read once, by the load that
+// fetches it, so those loads are non-temporal (as the GEMV streams): the
+// weight stream does not evict the data other kernels of the call reuse.
+// Step c waits for its copies with an explicit count: after them this wave
+// has issued the B loads of step c (6) and the copies (2) and B loads (6) of
+// steps c + 1 .. c + kSmallAhead - 1.
 template <bool GATEUP, int GS>
 __device__ __forceinline__ void run_item_small(const FwdArgs &a, const ItemState &st, const uint8_t *s_a,
                                                uint32_t sa_lds, const int *s_ent, const float *s_w) {
@@ -418,15 +421,15 @@ __device__ __forceinline__ void run_item_small(const FwdArgs &a, const ItemState
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const uint32_t cq = st.qoff[nt] + static_cast<uint32_t>(cc) * kChunkBytes;
-            f.qe[nt] = dev::bload<uint4>(st.brs, st.qv_even, cq);
-            f.qo[nt] = dev::bload<uint4>(st.brs, st.qv_odd, cq);
+            f.qe[nt] = dev::bload<uint4, dev::kLoadStream>(st.brs, st.qv_even, cq);
+            f.qo[nt] = dev::bload<uint4, dev::kLoadStream>(st.brs, st.qv_odd, cq);
             const uint32_t cs = st.soff[nt] + static_cast<uint32_t>(cc) * scale_chunk_bytes<GS>();
             if constexpr (GS == 32) {
-                const uint2 v = dev::bload<uint2>(st.brs, st.sv, cs);
+                const uint2 v = dev::bload<uint2, dev::kLoadStream>(st.brs, st.sv, cs);
                 f.sc[nt][0] = v.x;
                 f.sc[nt][1] = v.y;
             } else {
-                f.sc[nt][0] = dev::bload<uint32_t>(st.brs, st.sv, cs);
+                f.sc[nt][0] = dev::bload<uint32_t, dev::kLoadStream>(st.brs, st.sv, cs);
             }
         }
         asm volatile("" ::: "memory");
