@@ -168,6 +168,35 @@ def test_fused_layer_odd_shapes(E, k, n_tok):
     L.close()
 
 
+@pytest.mark.parametrize("path", ["auto", "gemv"])
+@pytest.mark.parametrize("n_tok", [3, 4])
+def test_fused_layer_identical_tokens(path, n_tok):
+    """Tokens that route alike: every union expert gets all n_tok tokens, so
+    the gate/up GEMV takes two passes per panel (two tokens per pass) and
+    the front splits the shared gate/up over two blocks per panel.  The fused
+    call is bit-identical to the three separate calls and within tolerance
+    of the oracle."""
+    data = Data(MEDIUM, n_tok=n_tok)
+    data.x[:] = data.x[0]
+    log(f"case fused identical tokens n_tok={n_tok} path={path}")
+    L = make_layer(B, data, path=PATHS.get(path))
+    x = B.activations_to_device(data.x)
+    y, idx, w, u = L.layer(x)
+    torch.cuda.synchronize()
+    assert L.device_errors() == 0
+    nu = int(u["n_union"].cpu()[0])
+    assert nu == MEDIUM.top_k
+    np.testing.assert_array_equal(u["counts"].cpu().numpy()[u["union_ids"].cpu().numpy()[:nu]], n_tok)
+    three = gpu_run(B, L, data, with_logits=False)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), three["y"].view(np.uint32))
+    ref = oracle_route(data)
+    check_routing(three, ref, check_logits=False)
+    y_ref = oracle_y(data, ref, range(n_tok))
+    check_outputs(y.cpu().numpy(), y_ref, f"identical tokens n_tok={n_tok}")
+    assert np.array_equal(y.cpu().numpy()[1:].view(np.uint32), np.repeat(y.cpu().numpy()[:1], n_tok - 1, 0).view(np.uint32))
+    L.close()
+
+
 def test_fused_layer_alternating_sizes():
     """One layer, fused calls of changing batch size back to back: the launch
     counters must be clean after every call."""
