@@ -493,8 +493,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one MoE layer on one GPU; runs on more than one GPU are "
-              "not part of this build (see DESIGN.md for how the layer would shard).",
+        print("bench.py measures one MoE layer on one GPU; the library has no multi-GPU "
+              "(expert-parallel) path, so runs on more than one GPU are not supported.",
               file=sys.stderr)
         sys.exit(2)
 
