@@ -185,14 +185,25 @@ def run_workload(B, torch, wl, x_all, use_graph=True):
     return res
 
 
-def hbm_reference(torch, reps=5):
-    """Streaming rates of plain library kernels on this GPU, as a reference for
-    the expert kernels' bandwidth: torch's sum over 2 GiB of fp32 (reads only)
-    and a 1 GiB device-to-device copy (read + write bytes), best of `reps`.
-    Both sizes are far above the 256 MB last-level cache."""
+def hbm_reference(B, torch, reps=5):
+    """Streaming rates on this GPU, as a reference for the expert kernels'
+    bandwidth: the library's plain read (coli_probe_read, 16-byte loads) over
+    2 GiB, torch's sum over 2 GiB of fp32 (reads only) and a 1 GiB
+    device-to-device copy (read + write bytes), best of `reps`.  All sizes
+    are far above the 256 MB last-level cache."""
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     src = torch.ones(512 << 20, dtype=torch.float32, device="cuda:0")
     out = {}
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    best = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        B.probe_read(src, sink)
+        ev1.record()
+        torch.cuda.synchronize()
+        best = max(best, src.numel() * 4 / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    out["stream_read_GBs"] = best
     best = 0.0
     for _ in range(reps):
         torch.cuda.synchronize()
@@ -216,6 +227,33 @@ def hbm_reference(torch, reps=5):
     out["copy_read_write_GBs"] = best
     del a, bdst
     torch.cuda.empty_cache()
+    return out
+
+
+def mfma_reference(torch, sizes=(8192, 16384), reps=5):
+    """Dense matrix-core rate of the platform's own GEMM (torch.matmul on
+    hipBLASLt) for fp16 and bf16 n x n x n products, the best over `sizes`
+    and `reps`: the achievable figure beside the 2.5 PFLOP/s nominal peak."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        for n in sizes:
+            a = torch.randn(n, n, device="cuda:0").to(dt).contiguous()
+            b = torch.randn(n, n, device="cuda:0").to(dt).contiguous()
+            c = torch.matmul(a, b)
+            best = 0.0
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                ev0.record()
+                torch.matmul(a, b, out=c)
+                ev1.record()
+                torch.cuda.synchronize()
+                best = max(best, 2.0 * n ** 3 / (ev0.elapsed_time(ev1) / 1e3) / 1e12)
+            out[f"{name}_{n}_TFLOPs"] = best
+            out[f"{name}_TFLOPs"] = max(out.get(f"{name}_TFLOPs", 0.0), best)
+            del a, b, c
+            torch.cuda.empty_cache()
+    out["shapes"] = " and ".join(f"{n} x {n} x {n}" for n in sizes) + ", torch.matmul (hipBLASLt)"
     return out
 
 
@@ -625,8 +663,9 @@ def main():
         del layers_i
         torch.cuda.empty_cache()
 
-    log("timing the HBM reference kernels")
-    hbm_ref = hbm_reference(torch)
+    log("timing the HBM and matrix-core reference kernels")
+    hbm_ref = hbm_reference(B, torch)
+    mfma_ref = mfma_reference(torch)
 
     # ---- report
     out_also = {}
@@ -640,6 +679,7 @@ def main():
                      union_mean=r["union_mean"], union_min=r["union_min"], union_max=r["union_max"],
                      step_GBs=nb["total"] / (ms / 1e3) / 1e9,
                      step_frac_hbm=nb["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     step_frac_stream_read=nb["total"] / (ms / 1e3) / 1e9 / hbm_ref["stream_read_GBs"],
                      kernel_us={k: v * 1e3 for k, v in r["kernel_ms"].items()})
         kg, kd = r["kernel_ms"].get("gateup"), r["kernel_ms"].get("down")
         if kg:
@@ -650,10 +690,12 @@ def main():
             fl = expert_flops(spec, spec.n_tok)
             entry["expert_gemm_TFLOPs"] = fl / ((kg + kd) / 1e3) / 1e12
             entry["expert_gemm_frac_mfma"] = entry["expert_gemm_TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+            entry["expert_gemm_frac_library_gemm"] = entry["expert_gemm_TFLOPs"] / mfma_ref["f16_TFLOPs"]
         out_also[name] = entry
     if tiered is not None:
         out_also["tiered_12l"] = tiered
     out_also["hbm_reference"] = hbm_ref
+    out_also["mfma_reference"] = mfma_ref
     if "decode_b1" in out_also and out_also["decode_b1"].get("gateup_GBs"):
         g = out_also["decode_b1"]["gateup_GBs"]
         out_also["decode_b1"]["gateup_vs_sum_read"] = g / hbm_ref["sum_read_GBs"]
@@ -701,7 +743,13 @@ def main():
                      "kernel": kname, "bytes_per_launch": kbytes, "avg_launch_us": kt * 1e3,
                      # the whole layer step: its algorithmic bytes over ms_per_step
                      "step_bytes": step_bytes, "step_achieved": step_bytes / (head["ms_per_step"] / 1e3) / 1e9,
-                     "step_frac": step_bytes / (head["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS},
+                     "step_frac": step_bytes / (head["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     # the plain read's rate on this part (coli_probe_read over 2 GiB), and both
+                     # rates as fractions of it
+                     "stream_read_GBs": hbm_ref["stream_read_GBs"],
+                     "frac_of_stream_read": achieved / hbm_ref["stream_read_GBs"],
+                     "step_frac_of_stream_read": step_bytes / (head["ms_per_step"] / 1e3) / 1e9
+                     / hbm_ref["stream_read_GBs"]},
         "also": out_also,
     }
     if not args.no_cpu_baseline and head_name == "decode_b1":

@@ -1,6 +1,6 @@
 /*
  * coli_moe.h -- C ABI of the int4 routed-expert MoE layer for AMD MI355X
- * (gfx950).  ABI version 4 (COLI_ABI_VERSION).
+ * (gfx950).  ABI version 5 (COLI_ABI_VERSION).
  *
  * One call sequence runs one Mixture-of-Experts layer over a batch of tokens,
  * following the per-token path of the Colibri pages (getting-started page,
@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define COLI_ABI_VERSION 4
+#define COLI_ABI_VERSION 5
 
 typedef enum {
     COLI_OK = 0,
@@ -338,6 +338,20 @@ coli_status coli_set_alloc_limit(int64_t bytes);
 
 /* Bytes of device and pinned host memory the library currently holds. */
 int64_t coli_alloc_bytes(void);
+
+/* Measurement reference, for benchmarks: streams `bytes` of device memory
+ * at `buf` once on `stream` (the current device) with the plainest fast read
+ * -- 16-byte non-temporal loads, four in flight per thread, eight 256-thread
+ * workgroups per CU striding over the buffer -- and XORs every 32-bit word
+ * read into *sink (device memory, one uint32_t, which the caller clears
+ * first to read the XOR).  Timed by the caller over a buffer far larger
+ * than the 256 MB memory-side cache, its rate is the HBM read bandwidth the
+ * part reaches in practice, the ceiling beside the 8 TB/s peak that the
+ * expert kernels' algorithmic rates are compared with.  buf and sink stay
+ * caller-owned.  COLI_E_INVALID for NULL pointers, a size that is not a
+ * multiple of 16 or a buf that is not 16-byte aligned; COLI_E_DEVICE without
+ * a device or if the launch fails.  bytes == 0 launches nothing. */
+coli_status coli_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,7 @@ SIGNATURES = {
     "coli_layer_kernel_times": (C.c_int, [_p, _p, _p]),
     "coli_set_alloc_limit": (C.c_int, [_i64]),
     "coli_alloc_bytes": (_i64, []),
+    "coli_probe_read": (C.c_int, [_p, _sz, _p, _p]),
 }
 KERNEL_KINDS = ["router", "topk", "union", "plan", "gateup", "down", "combine"]
 
@@ -293,6 +294,16 @@ def set_alloc_limit(nbytes: int) -> None:
 
 def alloc_bytes() -> int:
     return int(lib.coli_alloc_bytes())
+
+
+def probe_read(buf, sink, stream=None):
+    """coli_probe_read over the bytes of device tensor `buf` on `stream`
+    (default: torch's current stream); XORs its 32-bit words into the
+    one-element int32 device tensor `sink`."""
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib.coli_probe_read(C.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                               C.c_void_p(sink.data_ptr()), C.c_void_p(st.cuda_stream)))
 
 
 def activations_to_device(x: np.ndarray, device=0):

@@ -717,6 +717,11 @@ coli_status run_fused(coli_layer *L, const FusedScratch &w, bool timed, const vo
 
 }  // namespace
 
+namespace coli {
+// probe.hip: the streaming-read reference kernel behind coli_probe_read.
+hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, int n_cu, hipStream_t s);
+}  // namespace coli
+
 extern "C" {
 
 int32_t coli_abi_version(void) { return COLI_ABI_VERSION; }
@@ -733,6 +738,19 @@ int64_t coli_alloc_bytes(void) {
     MemBook &b = mem_book();
     std::lock_guard<std::mutex> g(b.mu);
     return b.used;
+}
+
+coli_status coli_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink) return fail(nullptr, COLI_E_INVALID, "NULL device pointer");
+    if (bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+        return fail(nullptr, COLI_E_INVALID, "bytes (%zu) must be a multiple of 16 and buf 16-byte aligned", bytes);
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(nullptr, COLI_E_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+    if ((e = launch_probe_read(buf, bytes, sink, n_cu, static_cast<hipStream_t>(stream))) != hipSuccess)
+        return fail(nullptr, COLI_E_DEVICE, "probe launch: %s", hipGetErrorString(e));
+    return COLI_OK;
 }
 
 const char *coli_status_str(coli_status s) {

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lib.coli_abi_version() == 4
+    assert B.lib.coli_abi_version() == 5
     for st, name in enumerate(["COLI_OK", "COLI_E_INVALID", "COLI_E_NOMEM", "COLI_E_DEVICE",
                                "COLI_E_STATE", "COLI_E_UNSUPPORTED"]):
         assert B.status_str(st) == name
@@ -104,6 +104,16 @@ def test_null_layer_calls_are_invalid():
     assert L.coli_layer_stream_stats(None, None, None) == B.E_INVALID
     assert L.coli_layer_device_errors(None, None) == B.E_INVALID
     assert L.coli_layer_destroy(None) == B.OK
+
+
+def test_probe_read_validates_before_the_device():
+    import ctypes as C
+    L = B.lib
+    fake, sink = C.c_void_p(4096), C.c_void_p(8192)     # never dereferenced on the host
+    assert L.coli_probe_read(None, 16, sink, None) == B.E_INVALID
+    assert L.coli_probe_read(fake, 16, None, None) == B.E_INVALID
+    assert L.coli_probe_read(fake, 24, sink, None) == B.E_INVALID          # not a multiple of 16
+    assert L.coli_probe_read(C.c_void_p(4100), 16, sink, None) == B.E_INVALID   # misaligned
 
 
 def documented_layout_i8(blob, H, I, group):
