@@ -341,8 +341,8 @@ int64_t coli_alloc_bytes(void);
 
 /* Measurement reference, for benchmarks: streams `bytes` of device memory
  * at `buf` once on `stream` (the current device) with the plainest fast read
- * -- 16-byte non-temporal loads, four in flight per thread, eight 256-thread
- * workgroups per CU striding over the buffer -- and XORs every 32-bit word
+ * -- 16-byte non-temporal loads, eight in flight per thread, one 256-thread
+ * workgroup per CU striding over the buffer -- and XORs every 32-bit word
  * read into *sink (device memory, one uint32_t, which the caller clears
  * first to read the XOR).  Timed by the caller over a buffer far larger
  * than the 256 MB memory-side cache, its rate is the HBM read bandwidth the

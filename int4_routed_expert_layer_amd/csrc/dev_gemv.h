@@ -124,7 +124,12 @@ __device__ __forceinline__ void stage_slice_seed(float c8, float *cs32, int K, i
     if ((q & 3) == 0) cs32[m * (K / 32) + (q >> 2)] = c;
 }
 
-constexpr int kGateUpGroup = 2;   // gate/up chunks per register buffer
+// Gate/up chunks per register buffer.  One (with two buffers and four
+// workgroups per CU, 64 KB of weights in flight per CU): the HBM streams
+// faster with less in flight per CU -- a plain read of 2 GiB peaks at about
+// 32 KB per CU and slows beyond -- and two per buffer measured slower
+// (decode B=1 gate/up 21.4 against 20.5 us, B=4 74.9 against 69.4 us).
+constexpr int kGateUpGroup = 1;
 constexpr int kPipeGroup = 2;   // down chunks per register buffer
 
 // sum over the 8 columns k0..k0+7 of two int8 dwords (columns k0..k0+3 in
