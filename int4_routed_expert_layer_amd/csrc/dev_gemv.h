@@ -130,7 +130,9 @@ __device__ __forceinline__ void stage_slice_seed(float c8, float *cs32, int K, i
 // 32 KB per CU and slows beyond -- and two per buffer measured slower
 // (decode B=1 gate/up 21.4 against 20.5 us, B=4 74.9 against 69.4 us).
 constexpr int kGateUpGroup = 1;
-constexpr int kPipeGroup = 2;   // down chunks per register buffer
+// Down chunks per register buffer: one, as for gate/up (less in flight per CU;
+// down 15.1 -> 15.0 us at decode B=1, 55.0 -> 54.2 us at B=4).
+constexpr int kPipeGroup = 1;
 
 // sum over the 8 columns k0..k0+7 of two int8 dwords (columns k0..k0+3 in
 // w0, k0+4..k0+7 in w1, each stored as u = q + 128 in byte order k, k+2, k+1,
