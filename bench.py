@@ -190,7 +190,8 @@ def hbm_reference(B, torch, reps=5):
     bandwidth: the library's plain read (coli_probe_read, 16-byte loads) over
     2 GiB, torch's sum over 2 GiB of fp32 (reads only) and a 1 GiB
     device-to-device copy (read + write bytes), best of `reps`.  All sizes
-    are far above the 256 MB last-level cache."""
+    are far above the 256 MB last-level cache.  Run before the layers are
+    placed."""
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     src = torch.ones(512 << 20, dtype=torch.float32, device="cuda:0")
     out = {}
@@ -541,6 +542,10 @@ def main():
     from int4_routed_expert_layer_amd import configs, inputs
 
     torch.cuda.init()
+    # The reference rates first, before the layers' allocations fill the device.
+    log("timing the HBM and matrix-core reference kernels")
+    hbm_ref = hbm_reference(B, torch, reps=10)
+    mfma_ref = mfma_reference(torch)
     wanted = args.workloads.split(",")
     spec1 = configs.DECODE_B1
     log(f"generating experts of {spec1.name}")
@@ -663,9 +668,6 @@ def main():
         del layers_i
         torch.cuda.empty_cache()
 
-    log("timing the HBM and matrix-core reference kernels")
-    hbm_ref = hbm_reference(B, torch)
-    mfma_ref = mfma_reference(torch)
 
     # ---- report
     out_also = {}
