@@ -20,6 +20,18 @@
 #include "internal.h"
 
 namespace coli {
+// probe.hip: the streaming-read reference kernel behind coli_probe_read.
+hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, int n_cu, hipStream_t s);
+// route.hip: router and top-k in one launch for 3 to 128 tokens
+// (hipErrorNotSupported outside), with route_topk_counters() arrival
+// counters, zero at rest.
+int route_topk_counters();
+hipError_t launch_router_topk(const void *x, int act_bf16, const float *wt, const float *bias, int n_tok, int hidden,
+                              int n_experts, int k, float *logits, int32_t *counters, int32_t *idx, float *w,
+                              hipStream_t s);
+}  // namespace coli
+
+namespace coli {
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -318,7 +330,7 @@ struct coli_layer {
     int32_t *n_chunks = nullptr;
     int max_chunks = 0;
     int32_t *err = nullptr;
-    int32_t *sync_counters = nullptr;  // [1 + H/32] arrival counters, zero at rest
+    int32_t *sync_counters = nullptr;  // [1 + H/32 + route_topk_counters()] arrival counters, zero at rest
     int32_t *queues = nullptr;         // [kQueueInts] grouped work-queue counters, zero at rest
     int32_t *union_blk = nullptr;      // [kUnionMaxBlocks x E + 64]; counter at [kUnionMaxBlocks x E]
     int32_t *union_rank = nullptr;     // [max_tokens x k]
@@ -500,7 +512,7 @@ size_t create_bytes(const coli_moe_dims *d) {
     const size_t chunks = static_cast<size_t>(work_list_capacity(d->max_tokens, d->top_k, d->n_experts, d->has_shared));
     return sizeof(float) * E * H + sizeof(float) * E + sizeof(void *) * (E + 1) + sizeof(float) * T * E +
            sizeof(_Float16) * (rows + 2) * I + sizeof(_Float16) * (T + 1) * H + sizeof(float) * (rows + 1) * H +
-           sizeof(ChunkDesc) * chunks + 2 * sizeof(int32_t) + sizeof(int32_t) * (1 + H / 32) +
+           sizeof(ChunkDesc) * chunks + 2 * sizeof(int32_t) + sizeof(int32_t) * (1 + H / 32 + route_topk_counters()) +
            sizeof(int32_t) * kQueueInts + sizeof(int32_t) * (kUnionMaxBlocks * E + 64) + sizeof(int32_t) * T * k +
            blob_layout(d->hidden, d->inter, d->group, d->weight_bits).total + sizeof(int32_t) * (E + 1) +
            sizeof(UnitDesc) * (E + 1);
@@ -717,10 +729,6 @@ coli_status run_fused(coli_layer *L, const FusedScratch &w, bool timed, const vo
 
 }  // namespace
 
-namespace coli {
-// probe.hip: the streaming-read reference kernel behind coli_probe_read.
-hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, int n_cu, hipStream_t s);
-}  // namespace coli
 
 extern "C" {
 
@@ -831,7 +839,8 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         {reinterpret_cast<void **>(&L->chunks), sizeof(ChunkDesc) * L->max_chunks, "work list"},
         {reinterpret_cast<void **>(&L->n_chunks), sizeof(int32_t), "work count"},
         {reinterpret_cast<void **>(&L->err), sizeof(int32_t), "error flags"},
-        {reinterpret_cast<void **>(&L->sync_counters), sizeof(int32_t) * (1 + H / 32), "arrival counters"},
+        {reinterpret_cast<void **>(&L->sync_counters), sizeof(int32_t) * (1 + H / 32 + route_topk_counters()),
+         "arrival counters"},
         {reinterpret_cast<void **>(&L->queues), sizeof(int32_t) * kQueueInts, "work-queue counters"},
         {reinterpret_cast<void **>(&L->union_blk), sizeof(int32_t) * (kUnionMaxBlocks * E + 64), "union slab counts"},
         {reinterpret_cast<void **>(&L->union_rank), sizeof(int32_t) * T * dims->top_k, "union ranks"},
@@ -849,7 +858,7 @@ coli_status coli_layer_create(const coli_moe_dims *dims, int device, coli_layer 
         (he = hipMemset(L->xh + T * H, 0, sizeof(_Float16) * H)) != hipSuccess ||
         (he = hipMemset(L->table_dev, 0, sizeof(void *) * (E + 1))) != hipSuccess ||
         (he = hipMemset(L->err, 0, sizeof(int32_t))) != hipSuccess ||
-        (he = hipMemset(L->sync_counters, 0, sizeof(int32_t) * (1 + H / 32))) != hipSuccess ||
+        (he = hipMemset(L->sync_counters, 0, sizeof(int32_t) * (1 + H / 32 + route_topk_counters()))) != hipSuccess ||
         (he = hipMemset(L->queues, 0, sizeof(int32_t) * kQueueInts)) != hipSuccess ||
         (he = hipMemset(L->union_blk, 0, sizeof(int32_t) * (kUnionMaxBlocks * E + 64))) != hipSuccess ||
         (he = hipMemset(L->bias, 0, sizeof(float) * E)) != hipSuccess ||
@@ -986,7 +995,14 @@ coli_status coli_moe_route(coli_layer *L, const void *x, int32_t n_tok, int32_t 
     DeviceGuard guard(L->device);
     hipStream_t s = static_cast<hipStream_t>(stream);
     {
+        // 3 to 128 tokens: router and top-k in one launch (counted as the router).
         KernelMark m(L, COLI_K_ROUTER, s);
+        const hipError_t e = launch_router_topk(x, L->d.act == COLI_ACT_BF16, L->wt, L->bias, n_tok, L->d.hidden,
+                                                L->d.n_experts, L->d.top_k, L->logits,
+                                                L->sync_counters + 1 + L->d.hidden / 32, topk_idx, topk_w, s);
+        if (e == hipSuccess) return COLI_OK;
+        if (e != hipErrorNotSupported) return hip_fail(L, e, "router and top-k launch");
+        (void)hipGetLastError();
         HIP_TRY(L, launch_router_logits(x, L->d.act == COLI_ACT_BF16, L->wt, L->bias, n_tok, L->d.hidden,
                                         L->d.n_experts, L->logits, s),
                 "router logits launch");
