@@ -175,7 +175,9 @@ coli_status coli_expert_place(coli_layer *layer, int32_t expert,
 /* Route: for n_tok tokens x (device pointer, [n_tok x H], fp32 or bf16 per
  * dims.act), write topk_idx (device, int32 [n_tok x k], rank order) and
  * topk_w (device, fp32 [n_tok x k]).  0 <= n_tok <= max_tokens; n_tok == 0
- * does nothing.  COLI_E_STATE if the router was never set. */
+ * does nothing.  COLI_E_STATE if the router was never set.  3 to 128 tokens
+ * run as one launch (the same bits as the two); calls that overlap on one
+ * layer race on its arrival counters. */
 coli_status coli_moe_route(coli_layer *layer, const void *x, int32_t n_tok,
                            int32_t *topk_idx, float *topk_w, void *stream);
 
@@ -310,7 +312,7 @@ coli_status coli_layer_device_errors(coli_layer *layer, int32_t *flags);
  * COLI_KERNEL_KINDS entries, either may be NULL) and resets them. */
 typedef enum {
     COLI_K_ROUTER = 0,   /* router logits */
-    COLI_K_TOPK = 1,     /* top-k and weights */
+    COLI_K_TOPK = 1,     /* top-k and weights (3 to 128 tokens: in the router's launch) */
     COLI_K_UNION = 2,    /* batch union (2 launches: slab ranks, scatter) */
     COLI_K_PLAN = 3,     /* grouped work list; fp16 activations (2 launches) */
     COLI_K_GATEUP = 4,   /* gate/up + SwiGLU (GEMV or grouped) */
