@@ -3,6 +3,9 @@
 * top-k: E from 1 to 1024 (one to sixteen keys per lane of the selecting
   wave), k from 1 to 32, with exact logit ties planted between experts;
   logits and ids bit for bit, weights to fp32 rounding.
+* top-k at 3 to 128 tokens, where the router and the selection run in one
+  launch (the last router workgroup of each four tokens selects them), with
+  calls on both sides of that range on one layer, the same shapes and ties.
 * union: from a single slab of one chunk to the 64-slab maximum, slabs of
   several chunks, ragged last slabs, E up to 1024 and skewed or uniform
   popularity; every output bit for bit.  Calls of different sizes reuse one
@@ -116,4 +119,31 @@ def test_router_logits_large_batch_matches_oracle(E, act):
     assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_logits.view(np.uint32))
     ref_idx, _ = orc.topk(ref_logits, spec.top_k)
     np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    L.close()
+
+
+ROUTE_SIZES = [128, 3, 77, 129, 2, 4, 5, 64]   # 3..128: router and selection in one launch
+
+
+@pytest.mark.parametrize("E,k,act", [(E, k, "f32") for E, k in TOPK_CASES] + [(256, 8, "bf16"), (1000, 20, "bf16")])
+def test_route_small_batches_match_oracle(E, k, act):
+    n_max = max(ROUTE_SIZES)
+    spec = configs.TINY.with_(hidden=256, inter=128, n_experts=E, top_k=k, n_tok=n_max,
+                              has_shared=False, act=act, routing="gauss")
+    data = Data(spec)
+    for a in range(0, E - 1, 7):
+        data.w[:, a + 1] = data.w[:, a]
+    L = B.MoELayer.from_spec(spec)
+    L.set_router(data.w, data.b)
+    for i, n in enumerate(ROUTE_SIZES):
+        # a different slice of the seeded batch per call, so that counters left
+        # by an earlier call would show in the result
+        x_np = np.ascontiguousarray(np.roll(data.x, 13 * i, axis=0)[:n])
+        log(f"case route-small E={E} k={k} act={act} n_tok={n}")
+        idx, w = L.route(B.activations_to_device(x_np))
+        torch.cuda.synchronize()
+        ref_idx, ref_w = orc.topk(orc.router_logits(x_np, data.w, data.b), k)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx, err_msg=f"n_tok={n}")
+        np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7, err_msg=f"n_tok={n}")
+    assert L.device_errors() == 0
     L.close()
